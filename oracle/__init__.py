@@ -1,0 +1,44 @@
+"""CPU oracle for paged attention -- TEST INFRASTRUCTURE, not product code.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import, call or run anything in this package.  The HIP library never
+imports it and it imports nothing from the HIP library.
+
+Pinned functions (each pin lives in ``tests/test_oracle.py``):
+
+* ``blocks_needed`` / ``slots_allocated`` / ``waste_fraction`` / ``prealloc_waste``
+  -- the worked example of the page "Nano-vLLM-Ascend", section 2.1
+  (``tests/golden/block_count_example.txt``).
+* ``paged_decode`` / ``paged_decode_one`` -- fp64 brute force on tiny inputs,
+  torch's float64 ``scaled_dot_product_attention`` (with ``enable_gqa``) on
+  dense contiguous layouts, closed forms (L = 1, q = 0, constant V, needle),
+  permutation invariance, softmax rows summing to one.
+* ``paged_prefill`` -- float64 causal ``scaled_dot_product_attention`` when
+  nothing is cached, equality with successive decodes, brute force.
+* ``reshape_and_cache`` -- round trip through independently computed slots,
+  padding slots skipped, other slots untouched.
+
+Parity unpinned: the grouping convention of query heads onto KV heads beyond
+what torch's ``enable_gqa`` fixes (the pages never mention grouped-query
+attention; contiguous groups are the reading taken).
+"""
+from .paged_attention import (  # noqa: F401
+    attend,
+    blocks_needed,
+    decode_u16,
+    gather_sequence,
+    kv_head_of,
+    logical_to_physical,
+    paged_decode,
+    paged_decode_one,
+    paged_prefill,
+    pool_utilisation,
+    prealloc_waste,
+    reshape_and_cache,
+    slot_position,
+    slots_allocated,
+    softmax_rows,
+    visible_keys,
+    waste_fraction,
+)
+from . import brute_force  # noqa: F401
