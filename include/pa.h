@@ -1,0 +1,165 @@
+/*
+ * pa.h -- C ABI of libpa.so, paged attention for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  Scaled dot-product attention softmax(q . K^T * scale) . V
+ * (page "Nano-vLLM-Ascend", section 2.2.1, the attention listing) over many
+ * variable-length sequences whose keys and values live in a paged KV cache:
+ * the cache is cut into fixed-size token blocks, a sequence of L tokens holds
+ * ceil(L / block_size) blocks, and a per-sequence block table maps logical
+ * block j to a physical block (same page, section 2.1, the Block / BlockTable
+ * structures and the 16-token worked example).  Block sizes 16, 32 and 256 are
+ * supported (16/32: same page, section 2.1 tip; 256: page "vLLM-Ascend ...",
+ * section 2.2 tuning table).  Softmax statistics are kept in fp32 (page
+ * "vLLM-Ascend ...", section 3.1, problem 2: fp16 accumulation errors fixed by
+ * a float softmax).
+ *
+ * Layouts (all tensors dense, row-major, element type fp16 or bf16 unless
+ * stated):
+ *   key cache, value cache : [num_blocks][block_size][num_kv_heads][head_dim]
+ *                            (the per-block (block_size, num_heads, head_dim)
+ *                            layout of the Block structure, page
+ *                            "Nano-vLLM-Ascend", section 2.1), one array each.
+ *   block_tables           : int32 [num_seqs][max_blocks_per_seq]; entry j of
+ *                            row i is the physical block of logical block j of
+ *                            sequence i.  Entries at or past
+ *                            ceil(context_lens[i] / block_size) are never read.
+ *   context_lens           : int32 [num_seqs]; tokens sequence i attends over,
+ *                            including the tokens written this step.
+ *   slot_mapping           : int64 [num_tokens]; flat slot = block * block_size
+ *                            + offset; a negative slot marks a padding token.
+ *   Query head h reads KV head h / (num_heads / num_kv_heads).
+ *
+ * Ownership and threading.  Every pointer argument except `stream` is a device
+ * pointer owned by the caller; the library allocates no device memory and keeps
+ * no per-call state.  Each call validates its host arguments, enqueues kernels
+ * on `stream` (a hipStream_t; NULL = the default stream) and returns without
+ * synchronising.  Calls are thread-safe.
+ *
+ * Errors.  Every entry point returns a pa_status.  Host arguments are checked
+ * before any HIP call; a failed check returns PA_ERR_INVALID_ARG or
+ * PA_ERR_UNSUPPORTED and enqueues nothing; pa_last_error() then gives a
+ * thread-local message.  A kernel launch failure returns PA_ERR_HIP.  Device
+ * contents are the caller's contract: block ids outside [0, num_blocks) and
+ * slots outside [0, num_blocks * block_size) are skipped by the kernels (never
+ * dereferenced) and leave the affected output undefined.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,  /* null pointer, negative size, inconsistent shape */
+  PA_ERR_UNSUPPORTED = -2,  /* head_dim / block_size / group / dtype not built  */
+  PA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required      */
+  PA_ERR_HIP = -4           /* a HIP launch reported an error                   */
+} pa_status;
+
+typedef enum pa_dtype { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Library version, (major << 16) | minor. */
+int pa_version(void);
+
+/* Static description of a status code. */
+const char* pa_status_string(int status);
+
+/* Detail of the last failed call on the calling thread ("" if none). */
+const char* pa_last_error(void);
+
+/*
+ * reshape_and_cache: write this step's new keys and values into their cache
+ * slots (the fill of fixed-size blocks, page "vLLM-Ascend ...", section 2.2,
+ * preprocessing stage; block layout of page "Nano-vLLM-Ascend", section 2.1).
+ *
+ *   key, value   [num_tokens][num_kv_heads][head_dim]   read
+ *   k_cache, v_cache                                     written at the slots
+ *   slot_mapping [num_tokens] int64                      read; < 0 = skip token
+ *
+ * For every token t with 0 <= slot < num_blocks * block_size, the
+ * num_kv_heads * head_dim row of token t is copied bit for bit to
+ * cache[slot / block_size][slot % block_size].  Duplicate slots in one call
+ * are a caller error (which write lands is unspecified).  num_tokens == 0 is a
+ * no-op.  Supported: head_dim in {64, 128}, block_size in {16, 32, 256}.
+ */
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,
+                         int head_dim, int block_size, int64_t num_blocks, int dtype,
+                         void* stream);
+
+/*
+ * Bytes of device workspace pa_decode needs for these sizes (0 when the
+ * context fits one partition, i.e. partition_size == 0 or
+ * max_context_len <= partition_size).  Pure host arithmetic.
+ */
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int max_context_len,
+                                int partition_size);
+
+/*
+ * pa_decode: one query token per sequence attends over its paged context
+ * (attention of page "Nano-vLLM-Ascend", section 2.2.1; paging of section
+ * 2.1; float softmax of page "vLLM-Ascend ...", section 3.1, problem 2).
+ *
+ *   out  [num_seqs][num_heads][head_dim]   written (same dtype as q)
+ *   q    [num_seqs][num_heads][head_dim]   read
+ *   k_cache, v_cache, block_tables, context_lens as described above.
+ *
+ * out[i][h] = sum_j p_j V_j with p = softmax_j(scale * q[i][h] . K_j) over the
+ * logical tokens j < context_lens[i] of sequence i, K_j/V_j taken from KV head
+ * h / (num_heads / num_kv_heads).  A sequence with context length 0 gets a
+ * zero row.  Context lengths above max_context_len are treated as
+ * max_context_len (which must be <= max_blocks_per_seq * block_size).
+ *
+ * partition_size: 0 = each (sequence, KV head) is processed by one workgroup;
+ * otherwise a positive multiple of block_size: the context is split into
+ * partitions of that many tokens processed in parallel and merged by a second
+ * kernel using each partition's fp32 max and sum, which needs
+ * pa_decode_workspace_size(...) bytes of `workspace` (device memory, caller
+ * owned, no initialisation needed, reused only after the call's kernels finish
+ * on `stream`).
+ *
+ * Supported: num_heads / num_kv_heads in {1, 2, 4, 8}; head_dim in {64, 128};
+ * block_size in {16, 32, 256}; dtype PA_F16 or PA_BF16; finite scale.
+ */
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+              int num_heads, int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+              int max_blocks_per_seq, int max_context_len, float scale, int partition_size,
+              void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * pa_prefill_chunk: chunked prefill over the paged cache (single-device
+ * chunking of long prefills, page "vllm-ascend architecture", section 1.1 and
+ * 3.1).  Sequence i contributes n_i = query_start_loc[i+1] - query_start_loc[i]
+ * new query tokens (rows query_start_loc[i] .. query_start_loc[i+1]-1 of q and
+ * out) that follow c_i = context_lens[i] - n_i cached tokens; the new tokens'
+ * keys and values must already be in the cache (pa_reshape_and_cache).  New
+ * token t attends to logical keys 0 .. c_i + t (its own key included).
+ *
+ *   out, q          [num_tokens][num_heads][head_dim]
+ *   query_start_loc int32 [num_seqs + 1], non-decreasing, query_start_loc[0] = 0,
+ *                   query_start_loc[num_seqs] = num_tokens
+ *   max_query_len   >= every n_i (sizes the grid; longer chunks are truncated)
+ *
+ * QK^T and PV run as bf16/fp16 matrix-core (MFMA) tiles with fp32
+ * accumulation; the softmax is fp32 and the probabilities are rounded to the
+ * input dtype before the PV product.  Supported shapes as for pa_decode;
+ * head_dim must be 128 and the group size 1, 2, 4 or 8.
+ */
+int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens,
+                     const int32_t* query_start_loc, int num_seqs, int64_t num_tokens,
+                     int num_heads, int num_kv_heads, int head_dim, int block_size,
+                     int64_t num_blocks, int max_blocks_per_seq, int max_query_len, float scale,
+                     int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

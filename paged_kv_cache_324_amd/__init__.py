@@ -1,0 +1,17 @@
+"""Paged attention for AMD Instinct MI355X (gfx950).
+
+A thin Python face of ``libpa.so``: the functions here carry the names of the
+library's C entry points and only marshal torch device tensors into them.
+"""
+from ._binding import (  # noqa: F401
+    LIB_PATH,
+    PA_BF16,
+    PA_F16,
+    PAError,
+    load_library,
+    pa_decode,
+    pa_decode_workspace_size,
+    pa_prefill_chunk,
+    pa_reshape_and_cache,
+    pa_version,
+)

@@ -1,0 +1,180 @@
+"""ctypes binding of libpa.so.
+
+Argument marshalling only: each function checks the tensors it is handed
+(device, dtype, contiguity, shape), passes raw device pointers and the current
+HIP stream to the C entry point of the same name, and raises ``PAError`` on a
+non-zero status.  All paged-attention work runs in the library's HIP kernels;
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4
+PA_F16, PA_BF16 = 0, 1
+
+_lib = None
+_lock = threading.Lock()
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def _declare(lib):
+    c_int, c_i64, c_sz, c_vp, c_f = (ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
+                                       ctypes.c_void_p, ctypes.c_float)
+    lib.pa_version.restype = c_int
+    lib.pa_version.argtypes = []
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_status_string.argtypes = [c_int]
+    lib.pa_last_error.restype = ctypes.c_char_p
+    lib.pa_last_error.argtypes = []
+    lib.pa_reshape_and_cache.restype = c_int
+    lib.pa_reshape_and_cache.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_int, c_int, c_int,
+                                         c_i64, c_int, c_vp]
+    lib.pa_decode_workspace_size.restype = c_sz
+    lib.pa_decode_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int]
+    lib.pa_decode.restype = c_int
+    lib.pa_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int,
+                              c_i64, c_int, c_int, c_f, c_int, c_vp, c_sz, c_int, c_vp]
+    lib.pa_prefill_chunk.restype = c_int
+    lib.pa_prefill_chunk.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_int,
+                                     c_int, c_int, c_int, c_i64, c_int, c_int, c_f, c_int, c_vp]
+    return lib
+
+
+def load_library(build_if_missing: bool = True):
+    """Load libpa.so (building it first only if no built library exists)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            if not build_if_missing:
+                raise ImportError(f"{LIB_PATH} is not built")
+            from .build import build_library
+            build_library()
+        _lib = _declare(ctypes.CDLL(LIB_PATH))
+        return _lib
+
+
+def _check(status: int) -> None:
+    if status != PA_OK:
+        lib = load_library()
+        detail = lib.pa_last_error().decode()
+        raise PAError(status, f"{lib.pa_status_string(status).decode()}: {detail}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return PA_F16
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"expected float16 or bfloat16, got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def pa_version() -> int:
+    return load_library().pa_version()
+
+
+def pa_decode_workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
+                             partition_size: int) -> int:
+    return int(load_library().pa_decode_workspace_size(num_seqs, num_heads, head_dim,
+                                                       max_context_len, partition_size))
+
+
+def pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    """Write key/value ``[T][Hkv][D]`` into caches ``[NB][BS][Hkv][D]`` at ``slot_mapping`` (int64)."""
+    lib = load_library()
+    T, Hkv, D = key.shape
+    NB, BS, Hkv2, D2 = k_cache.shape
+    if value.shape != key.shape or v_cache.shape != k_cache.shape or (Hkv2, D2) != (Hkv, D):
+        raise ValueError("reshape_and_cache: inconsistent shapes")
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    dt = _dtype_code(key)
+    for n, x in (("value", value), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(x, n, key.dtype)
+    _check(lib.pa_reshape_and_cache(_dev(key, "key"), value.data_ptr(), k_cache.data_ptr(),
+                                    v_cache.data_ptr(), _dev(slot_mapping, "slot_mapping", torch.int64),
+                                    T, Hkv, D, BS, NB, dt, _stream(key, stream)))
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+              max_context_len: int, partition_size: int = 512, workspace=None,
+              stream=None) -> torch.Tensor:
+    """Paged decode: ``out[i][h] = softmax(scale q K^T) V`` over each sequence's paged context."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    NB, BS, Hkv, D2 = k_cache.shape
+    if out.shape != q.shape or v_cache.shape != k_cache.shape or D2 != D:
+        raise ValueError("decode: inconsistent shapes")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("decode: block_tables must be [B][max_blocks], context_lens [B]")
+    dt = _dtype_code(q)
+    for n, x in (("out", out), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(x, n, q.dtype)
+    need = lib.pa_decode_workspace_size(B, Hq, D, max_context_len, partition_size)
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    _check(lib.pa_decode(_dev(out, "out"), _dev(q, "q"), k_cache.data_ptr(), v_cache.data_ptr(),
+                         _dev(block_tables, "block_tables", torch.int32),
+                         _dev(context_lens, "context_lens", torch.int32),
+                         B, Hq, Hkv, D, BS, NB, block_tables.shape[1], int(max_context_len),
+                         float(scale), int(partition_size), ws_ptr, ws_bytes, dt,
+                         _stream(q, stream)))
+    return out
+
+
+def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                     max_query_len: int, scale: float, stream=None) -> torch.Tensor:
+    """Chunked prefill: query rows of each sequence attend causally over its paged context."""
+    lib = load_library()
+    T, Hq, D = q.shape
+    NB, BS, Hkv, D2 = k_cache.shape
+    B = context_lens.shape[0]
+    if out.shape != q.shape or v_cache.shape != k_cache.shape or D2 != D:
+        raise ValueError("prefill: inconsistent shapes")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or query_start_loc.shape != (B + 1,):
+        raise ValueError("prefill: block_tables must be [B][max_blocks], query_start_loc [B+1]")
+    dt = _dtype_code(q)
+    for n, x in (("out", out), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(x, n, q.dtype)
+    _check(lib.pa_prefill_chunk(_dev(out, "out"), _dev(q, "q"), k_cache.data_ptr(), v_cache.data_ptr(),
+                                _dev(block_tables, "block_tables", torch.int32),
+                                _dev(context_lens, "context_lens", torch.int32),
+                                _dev(query_start_loc, "query_start_loc", torch.int32),
+                                B, T, Hq, Hkv, D, BS, NB, block_tables.shape[1], int(max_query_len),
+                                float(scale), dt, _stream(q, stream)))
+    return out

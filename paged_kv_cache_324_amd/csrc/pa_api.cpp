@@ -1,0 +1,242 @@
+// C ABI of libpa.so: host-side validation, workspace sizing and dispatch.
+//
+// Every entry point checks its host arguments before making any HIP call, so
+// a rejected call enqueues nothing and needs no GPU.  See include/pa.h for
+// the contract of each function.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "pa.h"
+#include "pa_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return PA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+bool supported_block_size(int b) { return b == 16 || b == 32 || b == 256; }
+bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+bool supported_dtype(int t) { return t == PA_F16 || t == PA_BF16; }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t num_partitions(int max_context_len, int partition_size) {
+  if (partition_size <= 0 || max_context_len <= partition_size) return 1;
+  return (max_context_len + (int64_t)partition_size - 1) / partition_size;
+}
+
+// Partial outputs first, then the (max, sum) pairs, each 256-byte aligned.
+size_t workspace_bytes_for(int num_seqs, int num_heads, int head_dim, int64_t parts) {
+  if (parts <= 1) return 0;
+  const size_t rows = (size_t)num_seqs * (size_t)num_heads * (size_t)parts;
+  return align_up(rows * (size_t)head_dim * sizeof(float)) + align_up(rows * 2 * sizeof(float));
+}
+
+// Shared checks of the paged-cache description.
+int check_cache(int num_heads, int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                int max_blocks, int dtype) {
+  if (num_heads < 1 || num_kv_heads < 1)
+    return fail(PA_ERR_INVALID_ARG, "num_heads (%d) and num_kv_heads (%d) must be >= 1", num_heads,
+                num_kv_heads);
+  if (num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_heads (%d) is not a multiple of num_kv_heads (%d)",
+                num_heads, num_kv_heads);
+  if (!supported_group(num_heads / num_kv_heads))
+    return fail(PA_ERR_UNSUPPORTED, "query heads per KV head %d not in {1,2,4,8}",
+                num_heads / num_kv_heads);
+  if (!supported_head_dim(head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not in {64,128}", head_dim);
+  if (!supported_block_size(block_size))
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not in {16,32,256}", block_size);
+  if (!supported_dtype(dtype)) return fail(PA_ERR_UNSUPPORTED, "dtype %d not PA_F16/PA_BF16", dtype);
+  if (num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  if (max_blocks < 1) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
+  if ((int64_t)max_blocks * block_size > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size exceeds 2^31-1");
+  if ((int64_t)num_kv_heads * head_dim * 2 * block_size > (int64_t)1 << 30)
+    return fail(PA_ERR_INVALID_ARG, "one cache block exceeds 1 GiB");
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_version(void) { return (1 << 16) | 0; }
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG: invalid argument";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: configuration not built";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: HIP runtime error";
+    default: return "unknown pa_status";
+  }
+}
+
+const char* pa_last_error(void) { return g_last_error; }
+
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,
+                         int head_dim, int block_size, int64_t num_blocks, int dtype,
+                         void* stream) {
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens must be >= 0");
+  if (num_kv_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
+  if (!supported_head_dim(head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not in {64,128}", head_dim);
+  if (!supported_block_size(block_size))
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not in {16,32,256}", block_size);
+  if (!supported_dtype(dtype)) return fail(PA_ERR_UNSUPPORTED, "dtype %d not PA_F16/PA_BF16", dtype);
+  if (num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if ((int64_t)num_kv_heads * head_dim * 2 > INT32_MAX / 2)
+    return fail(PA_ERR_INVALID_ARG, "token row too large");
+  pa::ReshapeArgs a;
+  a.key = key;
+  a.value = value;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_slots = num_blocks * (int64_t)block_size;
+  a.row_chunks = num_kv_heads * head_dim * 2 / 16;
+  return hip_status(pa::launch_reshape_and_cache(a, static_cast<hipStream_t>(stream)),
+                    "reshape_and_cache launch");
+}
+
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int max_context_len,
+                                int partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  return workspace_bytes_for(num_seqs, num_heads, head_dim,
+                             num_partitions(max_context_len, partition_size));
+}
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+              int num_heads, int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+              int max_blocks_per_seq, int max_context_len, float scale, int partition_size,
+              void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0");
+  int st = check_cache(num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, dtype);
+  if (st != PA_OK) return st;
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PA_ERR_INVALID_ARG, "max_context_len %d outside [0, max_blocks_per_seq*block_size]",
+                max_context_len);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0))
+    return fail(PA_ERR_INVALID_ARG, "partition_size %d must be 0 or a positive multiple of %d",
+                partition_size, block_size);
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  const int64_t parts = num_partitions(max_context_len, partition_size);
+  const int64_t grid = (int64_t)num_seqs * num_kv_heads * parts;
+  if (grid > INT32_MAX || (int64_t)num_seqs * num_heads > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "launch grid too large");
+  const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, parts);
+  if (need > 0) {
+    if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if (workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+      return fail(PA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  }
+
+  pa::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  const size_t rows = (size_t)num_seqs * num_heads * (size_t)parts;
+  a.part_out = need ? static_cast<float*>(workspace) : nullptr;
+  a.part_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             align_up(rows * head_dim * sizeof(float)))
+                   : nullptr;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.num_parts = (int)parts;
+  a.part_tokens = parts > 1 ? partition_size : (max_context_len > 0 ? max_context_len : 1);
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+  const int group = num_heads / num_kv_heads;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dtype == PA_BF16 ? pa::launch_decode_bf16(a, head_dim, block_size, group, s)
+                                  : pa::launch_decode_f16(a, head_dim, block_size, group, s);
+  return hip_status(e, "decode launch");
+}
+
+int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens,
+                     const int32_t* query_start_loc, int num_seqs, int64_t num_tokens,
+                     int num_heads, int num_kv_heads, int head_dim, int block_size,
+                     int64_t num_blocks, int max_blocks_per_seq, int max_query_len, float scale,
+                     int dtype, void* stream) {
+  if (num_seqs < 0 || num_tokens < 0)
+    return fail(PA_ERR_INVALID_ARG, "num_seqs and num_tokens must be >= 0");
+  int st = check_cache(num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, dtype);
+  if (st != PA_OK) return st;
+  if (head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "prefill supports head_dim 128 only");
+  if (max_query_len < 0) return fail(PA_ERR_INVALID_ARG, "max_query_len must be >= 0");
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (num_tokens > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "num_tokens exceeds 2^31-1");
+
+  pa::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.num_blocks = num_blocks;
+  a.num_tokens = num_tokens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_query_len = max_query_len;
+  a.q_tiles = 0;  // chosen by the launcher
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return hip_status(pa::launch_prefill(a, dtype, head_dim, block_size, num_heads / num_kv_heads,
+                                       static_cast<hipStream_t>(stream)),
+                    "prefill launch");
+}
+
+}  // extern "C"

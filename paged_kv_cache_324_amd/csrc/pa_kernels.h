@@ -1,0 +1,70 @@
+// Internal launch interface between the C ABI (pa_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct ReshapeArgs {
+  const void* key;
+  const void* value;
+  void* k_cache;
+  void* v_cache;
+  const int64_t* slot_mapping;
+  int64_t num_tokens;
+  int64_t num_slots;   // num_blocks * block_size
+  int row_chunks;      // 16-byte chunks in one token's num_kv_heads * head_dim row
+};
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* part_out;     // [num_seqs][num_heads][num_parts][head_dim], partition-normalised
+  float* part_ml;      // [num_seqs][num_heads][num_parts][2]: log2-domain max, sum
+  int64_t num_blocks;
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int max_blocks;
+  int max_context_len;
+  int num_parts;       // partitions per sequence in the grid
+  int part_tokens;     // tokens per partition (>= every context when unsplit)
+  float scale_log2;    // scale * log2(e)
+};
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start_loc;
+  int64_t num_blocks;
+  int64_t num_tokens;
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int max_blocks;
+  int max_query_len;
+  int q_tiles;         // query tiles per sequence in the grid
+  float scale_log2;
+};
+
+hipError_t launch_reshape_and_cache(const ReshapeArgs& a, hipStream_t s);
+
+// dtype DT_F16 / DT_BF16; head_dim 64/128; block_size 16/32/256; group 1/2/4/8.
+hipError_t launch_decode_f16(const DecodeArgs& a, int head_dim, int block_size, int group,
+                             hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, int head_dim, int block_size, int group,
+                              hipStream_t s);
+
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int block_size,
+                          int group, hipStream_t s);
+
+}  // namespace pa

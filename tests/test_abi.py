@@ -1,0 +1,129 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, and rejects bad host arguments before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_324_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+INVALID, UNSUPPORTED, WORKSPACE = pa.PAError, pa.PAError, pa.PAError
+P = ctypes.c_void_p(0x1000)   # a non-null host-side stand-in; never dereferenced by a rejected call
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_0-9]+\*?\s+\*?(pa_[a-z_0-9]+)\s*\(",
+                                 text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pa.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("pa_reshape_and_cache", "pa_decode", "pa_decode_workspace_size",
+              "pa_prefill_chunk", "pa_status_string", "pa_last_error", "pa_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert lib.pa_status_string(code)
+    assert lib.pa_version() >> 16 == 1
+
+
+def _decode(lib, **kw):
+    a = dict(out=P, q=P, k=P, v=P, bt=P, lens=P, B=2, Hq=16, Hkv=8, D=128, BS=16, NB=100,
+             maxb=10, maxL=160, scale=0.1, part=0, ws=None, wsb=0, dt=pa.PA_BF16)
+    a.update(kw)
+    return lib.pa_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["lens"], a["B"], a["Hq"],
+                         a["Hkv"], a["D"], a["BS"], a["NB"], a["maxb"], a["maxL"], a["scale"],
+                         a["part"], a["ws"], a["wsb"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(out=None), -1, "null pointer"),
+    (dict(bt=None), -1, "null pointer"),
+    (dict(B=-1), -1, "num_seqs"),
+    (dict(Hkv=5), -1, "multiple"),
+    (dict(Hq=48, Hkv=3), -2, "query heads per KV head"),
+    (dict(D=96), -2, "head_dim"),
+    (dict(BS=8), -2, "block_size"),
+    (dict(dt=7), -2, "dtype"),
+    (dict(NB=0), -1, "num_blocks"),
+    (dict(maxL=161), -1, "max_context_len"),
+    (dict(scale=float("inf")), -1, "scale"),
+    (dict(scale=float("nan")), -1, "scale"),
+    (dict(part=24), -1, "partition_size"),
+    (dict(part=-16), -1, "partition_size"),
+    (dict(part=32), -3, "workspace"),
+    (dict(part=32, ws=P, wsb=100), -3, "workspace"),
+])
+def test_decode_rejects_bad_arguments(lib, kw, code, msg):
+    assert _decode(lib, **kw) == code
+    assert msg in lib.pa_last_error().decode()
+
+
+def test_decode_zero_sequences_is_a_noop(lib):
+    assert _decode(lib, B=0, out=None, q=None) == 0
+
+
+def test_workspace_size(lib):
+    assert lib.pa_decode_workspace_size(128, 16, 128, 2048, 0) == 0
+    assert lib.pa_decode_workspace_size(128, 16, 128, 512, 512) == 0
+    n = lib.pa_decode_workspace_size(128, 16, 128, 2048, 512)
+    rows = 128 * 16 * 4
+    assert n >= rows * 128 * 4 + rows * 2 * 4 and n % 256 == 0
+
+
+def test_reshape_rejects_bad_arguments(lib):
+    f = lib.pa_reshape_and_cache
+    assert f(None, P, P, P, P, 4, 8, 128, 16, 100, pa.PA_BF16, None) == -1
+    assert f(P, P, P, P, P, -1, 8, 128, 16, 100, pa.PA_BF16, None) == -1
+    assert f(P, P, P, P, P, 4, 8, 80, 16, 100, pa.PA_BF16, None) == -2
+    assert f(P, P, P, P, P, 4, 8, 128, 48, 100, pa.PA_BF16, None) == -2
+    assert f(P, P, P, P, P, 4, 8, 128, 16, 0, pa.PA_BF16, None) == -1
+    assert f(None, None, None, None, None, 0, 8, 128, 16, 100, pa.PA_F16, None) == 0
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    f = lib.pa_prefill_chunk
+    args = [P, P, P, P, P, P, P, 2, 64, 32, 8, 128, 16, 100, 10, 32, 0.1, pa.PA_BF16, None]
+    bad = list(args)
+    bad[6] = None
+    assert f(*bad) == -1
+    bad = list(args)
+    bad[9] = 6      # 32 heads over 6 KV heads
+    assert f(*bad) == -1
+    bad = list(args)
+    bad[16] = float("nan")
+    assert f(*bad) == -1
+    bad = list(args)
+    bad[15] = -1
+    assert f(*bad) == -1
+
+
+def test_python_binding_names_match_c_entry_points():
+    for name in ("pa_reshape_and_cache", "pa_decode", "pa_decode_workspace_size",
+                 "pa_prefill_chunk"):
+        assert callable(getattr(pa, name))
+
+
+def test_bench_refuses_several_gpus():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0 and "one GPU" in r.stderr

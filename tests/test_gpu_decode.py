@@ -1,0 +1,233 @@
+"""GPU parity of reshape_and_cache and paged decode against the CPU oracle.
+
+All calls go through libpa.so's C ABI (via the ctypes binding).  Device pools
+are filled with NaN (0xFFFF) except the referenced blocks, and the unused tail
+of every sequence's last block is NaN too, so any read of a wrong slot shows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_324_amd import pa_decode, pa_reshape_and_cache
+from workloads import CONFIGS, make_batch, make_config, to_u16
+
+from _gpu import (check_close, host_caches_after_write, log, to_bits, to_f64, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+def _step(b, d, partition):
+    """One decode step on the GPU: write the new token, then attend."""
+    pa_reshape_and_cache(d.key_new, d.value_new, d.k_cache, d.v_cache, d.slot_mapping)
+    out = torch.empty_like(d.q)
+    pa_decode(out, d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, b.scale,
+              b.max_context_len, partition)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle_rows(b, rows=None):
+    kc, vc = host_caches_after_write(b)
+    sel = np.arange(b.B) if rows is None else np.asarray(rows)
+    return oracle.paged_decode(b.q[sel], kc, vc, b.block_tables_compact[sel],
+                               b.context_lens[sel], b.scale, b.dtype), sel
+
+
+# ------------------------------------------------------------------ reshape_and_cache
+@pytest.mark.parametrize("name", ["tiny_decode", "chunked_prefill"])
+def test_reshape_and_cache_bit_exact(name):
+    b = make_config(name)
+    log(f"reshape {name}: T={b.num_tokens} NB={b.NB}")
+    d = upload(b)
+    pa_reshape_and_cache(d.key_new, d.value_new, d.k_cache, d.v_cache, d.slot_mapping)
+    torch.cuda.synchronize()
+    kc_ref, vc_ref = host_caches_after_write(b)
+    assert np.array_equal(to_bits(d.k_cache[d.idx]), kc_ref)
+    assert np.array_equal(to_bits(d.v_cache[d.idx]), vc_ref)
+    untouched = torch.ones(b.NB, dtype=torch.bool, device="cuda")
+    untouched[d.idx] = False
+    assert bool((d.k_cache.view(torch.int16)[untouched] == -1).all())
+    assert bool((d.v_cache.view(torch.int16)[untouched] == -1).all())
+
+
+def test_reshape_skips_padding_and_out_of_pool_slots():
+    b = make_batch(B=6, Hq=4, Hkv=4, D=128, BS=16, dtype="bf16", scale=0.1, seed=31,
+                   n_new=5, ctx_range=(0, 40), NB=64)
+    d = upload(b)
+    slots = d.slot_mapping.clone()
+    slots[3] = -1
+    slots[7] = b.NB * b.BS          # one past the pool: skipped, never written
+    slots[8] = -(1 << 40)
+    pa_reshape_and_cache(d.key_new, d.value_new, d.k_cache, d.v_cache, slots)
+    torch.cuda.synchronize()
+    sl = b.slot_mapping_compact.copy()
+    sl[[3, 7, 8]] = -1
+    kc, vc = b.k_blocks.copy(), b.v_blocks.copy()
+    oracle.reshape_and_cache(b.key_new, b.value_new, kc, vc, sl)
+    assert np.array_equal(to_bits(d.k_cache[d.idx]), kc)
+    assert np.array_equal(to_bits(d.v_cache[d.idx]), vc)
+
+
+def test_reshape_empty_is_noop():
+    b = make_config("tiny_decode")
+    d = upload(b)
+    before = to_bits(d.k_cache)
+    pa_reshape_and_cache(d.key_new[:0], d.value_new[:0], d.k_cache, d.v_cache, d.slot_mapping[:0])
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(d.k_cache), before)
+
+
+# ------------------------------------------------------------------ decode parity
+@pytest.mark.parametrize("partition", [0, 16, 64])
+def test_decode_tiny_config(partition):
+    b = make_config("tiny_decode")
+    log(f"decode tiny partition={partition} lens={b.context_lens.tolist()}")
+    got = to_f64(_step(b, upload(b), partition))
+    ref, _ = _oracle_rows(b)
+    check_close(got, ref, f"tiny p={partition}")
+
+
+@pytest.mark.parametrize("partition", [512, 0, 256])
+def test_decode_qwen3_shaped_full_size(partition):
+    b = make_config("qwen3_0p6b_decode")
+    log(f"decode qwen3-shaped B={b.B} NB={b.NB} partition={partition}")
+    got = to_f64(_step(b, upload(b), partition))
+    ref, _ = _oracle_rows(b)
+    mx, rel = check_close(got, ref, f"qwen3 p={partition}")
+    log(f"  max_abs={mx:.3e} rel_l2={rel:.3e}")
+
+
+@pytest.mark.parametrize("partition", [512, 0])
+def test_decode_long_context_split_k(partition):
+    b = make_config("long_splitk_decode")
+    log(f"decode long split-K B={b.B} BS={b.BS} maxL={b.max_context_len} partition={partition}")
+    got = to_f64(_step(b, upload(b), partition))
+    ref, _ = _oracle_rows(b)
+    mx, rel = check_close(got, ref, f"long p={partition}")
+    log(f"  max_abs={mx:.3e} rel_l2={rel:.3e}")
+
+
+@pytest.mark.parametrize("name", ["llama2_70b_decode_bs16", "llama2_70b_decode_bs32"])
+def test_decode_llama2_shaped_prefix_sharing_sampled(name):
+    b = make_config(name)
+    log(f"decode {name} B={b.B} G={b.G} shared blocks={b.shared_pairs}")
+    got = to_f64(_step(b, upload(b), CONFIGS[name]["partition"]))
+    rows = [0, 1, 2, 3, 30, 31, 62, 63]      # pairs (2k, 2k+1) share prefix blocks
+    ref, sel = _oracle_rows(b, rows)
+    mx, rel = check_close(got[sel], ref, name)
+    log(f"  max_abs={mx:.3e} rel_l2={rel:.3e}")
+    assert np.all(np.isfinite(got))
+
+
+LENS = [1, 15, 16, 17, 255, 256, 257, 511, 512, 513, 1000, 0]
+
+
+@pytest.mark.parametrize("partition", [0, 512, 256, 32])
+def test_decode_length_edges(partition):
+    b = make_batch(B=len(LENS), Hq=16, Hkv=8, D=128, BS=16, dtype="bf16", scale=0.088, seed=41,
+                   lens=LENS, NB=4096)
+    got = to_f64(_step(b, upload(b), partition))
+    ref, _ = _oracle_rows(b)
+    assert np.all(got[-1] == 0)              # context length 0 gives a zero row
+    check_close(got, ref, f"edges p={partition}")
+
+
+SWEEP = [(dt, D, BS, G) for dt in ("f16", "bf16") for D in (64, 128) for BS in (16, 32, 256)
+         for G in (1, 2, 4, 8)]
+
+
+@pytest.mark.parametrize("dt,D,BS,G", SWEEP)
+def test_decode_shape_sweep(dt, D, BS, G):
+    Hkv = 2
+    b = make_batch(B=3, Hq=Hkv * G, Hkv=Hkv, D=D, BS=BS, dtype=dt, scale=D ** -0.5,
+                   seed=1000 + SWEEP.index((dt, D, BS, G)), lens_range=(1, 700))
+    d = upload(b)
+    ref, _ = _oracle_rows(b)
+    got0 = to_f64(_step(b, d, 0))
+    check_close(got0, ref, f"sweep {dt} D{D} BS{BS} G{G} unsplit")
+    out = torch.empty_like(d.q)
+    pa_decode(out, d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, b.scale,
+              b.max_context_len, 2 * BS if BS < 256 else 256)
+    torch.cuda.synchronize()
+    check_close(to_f64(out), ref, f"sweep {dt} D{D} BS{BS} G{G} split")
+
+
+# ------------------------------------------------------------------ exact properties
+def _set_logical(b, which, i, pos, kvh, row_bits):
+    """Set the K (which='k') or V row of logical token pos of sequence i (pre-write state + new token)."""
+    L, n = int(b.context_lens[i]), int(b.n_new[i])
+    if pos >= L - n:
+        arr = b.key_new if which == "k" else b.value_new
+        arr[int(b.query_start_loc[i]) + pos - (L - n), kvh] = row_bits
+    else:
+        arr = b.k_blocks if which == "k" else b.v_blocks
+        arr[b.block_tables_compact[i, pos // b.BS], pos % b.BS, kvh] = row_bits
+
+
+@pytest.mark.parametrize("partition", [0, 512, 64])
+def test_needle_probe_is_bit_exact(partition):
+    """q = e0, scale 1, K_j[0] = -100 except one target token (+100): out = V_target exactly."""
+    lens = [1000, 513, 40, 2048]
+    b = make_batch(B=4, Hq=8, Hkv=2, D=128, BS=16, dtype="bf16", scale=1.0, seed=43, lens=lens,
+                   NB=1024)
+    one = to_u16(np.ones(1, np.float32), "bf16")[0]
+    b.q[:] = 0
+    b.q[:, :, 0] = one
+    rng = np.random.default_rng(0)
+    targets = {}
+    for i, L in enumerate(lens):
+        for kvh in range(2):
+            t = int(rng.integers(0, L))
+            targets[(i, kvh)] = t
+            for j in range(L):
+                row = np.zeros(128, np.uint16)
+                row[0] = to_u16(np.array([100.0 if j == t else -100.0], np.float32), "bf16")[0]
+                _set_logical(b, "k", i, j, kvh, row)
+    got = to_bits(_step(b, upload(b), partition))
+    kc, vc = host_caches_after_write(b)
+    for (i, kvh), t in targets.items():
+        want = vc[b.block_tables_compact[i, t // 16], t % 16, kvh]
+        for g in range(4):
+            assert np.array_equal(got[i, kvh * 4 + g], want), (i, kvh, t)
+
+
+def test_block_permutation_invariance_is_bit_exact():
+    b = make_batch(B=16, Hq=16, Hkv=8, D=128, BS=16, dtype="bf16", scale=0.088, seed=44,
+                   lens_range=(1, 1500), NB=4096)
+    out1 = to_bits(_step(b, upload(b), 512))
+    perm = np.random.default_rng(1).permutation(b.NB)
+    b2 = make_batch(B=16, Hq=16, Hkv=8, D=128, BS=16, dtype="bf16", scale=0.088, seed=44,
+                    lens_range=(1, 1500), NB=4096)
+    b2.block_tables = np.where(b2.block_tables >= 0, perm[np.maximum(b2.block_tables, 0)], -1
+                               ).astype(np.int32)
+    b2.phys_ids = perm[b2.phys_ids]
+    b2.slot_mapping = perm[b2.slot_mapping // 16] * 16 + b2.slot_mapping % 16
+    out2 = to_bits(_step(b2, upload(b2), 512))
+    assert np.array_equal(out1, out2)
+
+
+@pytest.mark.parametrize("partition", [0, 128])
+def test_constant_values_give_exact_constant(partition):
+    b = make_batch(B=5, Hq=8, Hkv=4, D=64, BS=32, dtype="f16", scale=0.125, seed=45,
+                   lens_range=(1, 900), NB=512)
+    one = to_u16(np.ones(1, np.float32), "f16")[0]
+    poison = b.v_blocks == 0xFFFF
+    b.v_blocks[:] = one
+    b.v_blocks[poison] = 0xFFFF
+    b.value_new[:] = one
+    got = to_f64(_step(b, upload(b), partition))
+    assert np.all(got == 1.0)
+
+
+def test_zero_query_gives_mean_of_values():
+    b = make_batch(B=6, Hq=4, Hkv=2, D=128, BS=16, dtype="bf16", scale=0.088, seed=46,
+                   lens_range=(1, 3000), NB=2048)
+    b.q[:] = 0
+    got = to_f64(_step(b, upload(b), 512))
+    kc, vc = host_caches_after_write(b)
+    for i in range(b.B):
+        L = int(b.context_lens[i])
+        V = oracle.gather_sequence(vc, b.block_tables_compact[i], L, "bf16")
+        for h in range(4):
+            check_close(got[i, h], V[:, h // 2].mean(axis=0), f"mean seq {i}")

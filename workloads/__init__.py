@@ -78,7 +78,7 @@ class PagedBatch:
     phys_ids: np.ndarray       # int64 [n_used], physical id of each compact block (sorted)
     k_blocks: np.ndarray       # uint16 [n_used][BS][Hkv][D]
     v_blocks: np.ndarray       # uint16 [n_used][BS][Hkv][D]
-    q: np.ndarray              # uint16 [T][Hq][D]
+    q: np.ndarray              # uint16 [B][Hq][D] (decode) or [T][Hq][D] (prefill)
     key_new: np.ndarray        # uint16 [T][Hkv][D]
     value_new: np.ndarray      # uint16 [T][Hkv][D]
     slot_mapping: np.ndarray   # int64 [T], physical slot = block*BS + offset
@@ -130,8 +130,13 @@ def to_u16(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f16":
         return x.astype(np.float16).view(np.uint16)
     if dtype == "bf16":
-        u = x.view(np.uint32).astype(np.uint64)
-        r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+        u = x.view(np.uint32)
+        if not np.all(np.isfinite(x)):
+            raise ValueError("bf16 rounding here is for finite values only")
+        r = (u >> 16) & 1
+        r += u
+        r += 0x7FFF          # cannot wrap: finite floats stay below 0xFF800000
+        r >>= 16
         return r.astype(np.uint16)
     raise ValueError(dtype)
 
@@ -210,8 +215,8 @@ def make_batch(*, B: int, Hq: int, Hkv: int, D: int, BS: int, dtype: str, scale:
     qsl[1:] = np.cumsum(nn)
     T = int(qsl[-1])
 
-    # 3. queries
-    q = _normal_u16(rng, (T, Hq, D), dtype)
+    # 3. queries: one per sequence for decode (even an empty one), one per new token for prefill
+    q = _normal_u16(rng, (T if ctx_range is not None else B, Hq, D), dtype)
     # 4. cached K/V of earlier tokens (whole blocks drawn, then unwritten slots poisoned)
     n_used = len(phys_ids)
     k_blocks = _normal_u16(rng, (n_used, BS, Hkv, D), dtype)
