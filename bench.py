@@ -146,27 +146,36 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
 
-    def step(ev=None):
+    def step():
         pa.pa_reshape_and_cache(key_new, value_new, k_cache, v_cache, slot, stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
         pa.pa_decode(out, q, k_cache, v_cache, tables, lens, b.scale, b.max_context_len, partition,
                      workspace=workspace, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+
+    def decode_only():
+        pa.pa_decode(out, q, k_cache, v_cache, tables, lens, b.scale, b.max_context_len, partition,
+                     workspace=workspace, stream=stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    # Timed region: exactly `steps` steps back to back, nothing else on the stream.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # Kernel timing for the roofline: each pa_decode call (partition kernel +
+    # merge kernel) bracketed by HIP events recorded on the stream it runs on.
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    for i in range(args.steps):
+        events[i][0].record(stream)
+        decode_only()
+        events[i][1].record(stream)
+    torch.cuda.synchronize()
     decode_ms = np.array([s.elapsed_time(e) for s, e in events])
 
     ms_per_step = wall / args.steps * 1e3

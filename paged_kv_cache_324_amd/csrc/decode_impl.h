@@ -37,7 +37,18 @@
 
 namespace pa {
 
+#ifndef PA_DECODE_PF
+#define PA_DECODE_PF 8    // steps of K and V in flight per lane (group size)
+#endif
+#ifndef PA_DECODE_WPE
+#define PA_DECODE_WPE 2   // minimum resident waves per SIMD the register budget must allow
+#endif
+#ifndef PA_DECODE_AUX
+#define PA_DECODE_AUX kCachePolicyNT
+#endif
+
 constexpr int kDecodeWaves = 4;
+constexpr int kTableCap = 256;  // block ids staged in LDS per chunk of a partition
 constexpr float kEmptyMax = -1.0e30f;  // finite "no token yet" max: keeps 2^(m - m') finite
 
 __device__ __forceinline__ int clamp_context(const DecodeArgs& a, int seq) {
@@ -45,8 +56,9 @@ __device__ __forceinline__ int clamp_context(const DecodeArgs& a, int seq) {
   return L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
 }
 
-template <int DT, int D, int BS, int G, int PF>
-__global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs a) {
+template <int DT, int D, int BS, int G, int PF, int WAVES_PER_EU, int LOAD_AUX>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_EU, 8)))
+void decode_partition_kernel(const DecodeArgs a) {
   constexpr int LPR = D / 8;           // lanes per token row
   constexpr int RPW = 64 / LPR;        // token rows per wavefront load
   constexpr int NW = kDecodeWaves;
@@ -55,21 +67,45 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
 
   __shared__ float s_acc[NW][G][D];
   __shared__ float s_ml[NW][G][2];
+  __shared__ int32_t s_tbl[kTableCap];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane / LPR;
   const int c = lane % LPR;
 
-  int wg = blockIdx.x;
-  const int part = wg % a.num_parts;
-  wg /= a.num_parts;
-  const int kvh = wg % a.num_kv_heads;
-  const int seq = wg / a.num_kv_heads;
+  // Partition-major order: every sequence's first partition is dispatched
+  // before any second partition, so long contexts start early and the
+  // workgroups of partitions past a short context (which exit at once) come
+  // last.
+  const int per_part = a.num_seqs * a.num_kv_heads;
+  const int part = blockIdx.x / per_part;
+  const int rest = blockIdx.x - part * per_part;
+  const int seq = rest / a.num_kv_heads;
+  const int kvh = rest - seq * a.num_kv_heads;
   const int h0 = kvh * G;
 
-  const int L = clamp_context(a, seq);
+  // Issue the independent loads of the prologue together: the context
+  // length (scalar), this workgroup's queries, and the block ids of the first
+  // chunk (speculatively, before the length is known; every id read lies in
+  // the sequence's table row).
   const int t0 = part * a.part_tokens;
+  const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks;
+  const int lb_first = t0 / BS;
+  const int32_t tbl_first =
+      lb_first + (int)threadIdx.x < a.max_blocks ? bt[lb_first + threadIdx.x] : -1;
+  uint32_t qv[G][4];
+  {
+    const int c = (threadIdx.x & 63) % LPR;
+    const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) +
+                                                     ((int64_t)seq * a.num_heads + h0) * D) + c;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const u32x4 t = qp[g * (D / 8)];
+      qv[g][0] = t.x; qv[g][1] = t.y; qv[g][2] = t.z; qv[g][3] = t.w;
+    }
+  }
+  const int L = clamp_context(a, seq);
   if (L == 0) {
     if (part == 0) {
       uint16_t* o = static_cast<uint16_t*>(a.out) + ((int64_t)seq * a.num_heads + h0) * D;
@@ -80,25 +116,12 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
   if (t0 >= L) return;
   const int t1 = min(L, t0 + a.part_tokens);
   const int nparts_seq = 1 + (L - 1) / a.part_tokens;
-  const int nblk = (L + BS - 1) / BS;
 
   const uint32_t row_stride = (uint32_t)a.num_kv_heads * D * 2;
   const uint64_t block_bytes = (uint64_t)BS * row_stride;
   const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)kvh * D * 2;
   const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)kvh * D * 2;
-  const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks;
-  const uint32_t lane_off = (uint32_t)r * row_stride + (uint32_t)c * 16;
-
-  uint32_t qv[G][4];
-  {
-    const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) +
-                                                     ((int64_t)seq * a.num_heads + h0) * D) + c;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const u32x4 t = qp[g * (D / 8)];
-      qv[g][0] = t.x; qv[g][1] = t.y; qv[g][2] = t.z; qv[g][3] = t.w;
-    }
-  }
+  const uint32_t lane_off = (uint32_t)r * row_stride + (uint32_t)c * 16;  // within a step
 
   float m[G], l[G], acc[G][8];
 #pragma unroll
@@ -109,78 +132,114 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
   }
 
-  // Scalar addressing of the block holding this wavefront's rows at step s.
-  struct Where { uint64_t boff; uint32_t nrec; uint32_t voff; };
-  auto where = [&](int s) -> Where {
-    const int tb = t0 + s * TPS + wave * RPW;
-    const int lb = tb / BS;
-    const int nv = min(BS, t1 - lb * BS);
-    int blk = bt[min(lb, nblk - 1)];
-    const bool ok = nv > 0 && blk >= 0 && (int64_t)blk < a.num_blocks;
-    Where w;
-    w.nrec = ok ? (uint32_t)(nv - 1) * row_stride + D * 2 : 0u;
-    w.boff = ok ? (uint64_t)blk * block_bytes : 0ull;
-    w.voff = (uint32_t)(tb - lb * BS) * row_stride + lane_off;
-    return w;
-  };
+  // The partition is walked in chunks of at most kTableCap blocks whose ids are
+  // first staged in LDS; each step then reads its block id with one uniform
+  // LDS read instead of a dependent scalar load.
+  const int32_t nb32 = a.num_blocks > INT32_MAX ? INT32_MAX : (int32_t)a.num_blocks;
+  constexpr int kChunkTokens = kTableCap * BS;
+  for (int c0 = t0; c0 < t1; c0 += kChunkTokens) {
+    const int c1 = min(t1, c0 + kChunkTokens);
+    const int lb0 = c0 / BS;
+    const int nchunk_blk = (c1 - c0 + BS - 1) / BS;
+    static_assert(kTableCap == 256, "one table entry per thread");
+    __syncthreads();  // previous chunk's table reads are done
+    if ((int)threadIdx.x < nchunk_blk) {
+      const int32_t blk = c0 == t0 ? tbl_first : bt[lb0 + threadIdx.x];
+      s_tbl[threadIdx.x] = (blk >= 0 && blk < nb32) ? blk : -1;
+    }
+    __syncthreads();
 
-  const int nsteps = (t1 - t0 + TPS - 1) / TPS;
-  u32x4 kb[PF], vb[PF];
-  Where wh[PF];
-#pragma unroll
-  for (int u = 0; u < PF; ++u) {
-    wh[u] = where(u);
-    kb[u] = buffer_load16(make_rsrc(kbase + wh[u].boff, wh[u].nrec), wh[u].voff);
-    vb[u] = buffer_load16(make_rsrc(vbase + wh[u].boff, wh[u].nrec), wh[u].voff);
-  }
+    // Addressing of a group of PF steps: lane u (mod PF) works out step
+    // sbase + u -- the block holding the wavefront's rows, the byte offset of
+    // its first row, and how many bytes from there are valid -- with one LDS
+    // read for the whole group.  Each step then takes its values with
+    // v_readlane into scalar registers (all operands non-negative; BS and TPS
+    // are powers of two).
+    const uint32_t wave_t0 = (uint32_t)c0 + (uint32_t)wave * RPW;
+    struct Group { uint32_t lo, hi, nrec; };
+    auto group_where = [&](int sbase) -> Group {
+      const uint32_t tb = wave_t0 + (uint32_t)(sbase + (lane & (PF - 1))) * TPS;
+      const uint32_t lb = tb / BS;
+      const uint32_t o = tb % BS;                        // first row inside the block
+      const int nvr = min(BS, c1 - (int)(lb * BS)) - (int)o;  // valid rows from there
+      const int32_t blk = s_tbl[min((int)lb - lb0, nchunk_blk - 1)];
+      const bool ok = nvr > 0 && blk >= 0;
+      const uint64_t off = ok ? (uint64_t)(uint32_t)blk * block_bytes + o * row_stride : 0ull;
+      Group g;
+      g.lo = (uint32_t)off;
+      g.hi = (uint32_t)(off >> 32);
+      g.nrec = ok ? (uint32_t)(nvr - 1) * row_stride + D * 2 : 0u;
+      return g;
+    };
+    auto load = [&](const char* base, const Group& g, int u) -> u32x4 {
+      const uint64_t off = ((uint64_t)__builtin_amdgcn_readlane(g.hi, u) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane(g.lo, u);
+      const uint32_t nrec = __builtin_amdgcn_readlane(g.nrec, u);
+      return buffer_load16<LOAD_AUX>(make_rsrc(base + off, nrec), lane_off);
+    };
 
-  for (int s0 = 0; s0 < nsteps; s0 += PF) {
-    float sc[PF][G];
+    // Loads are issued K first, then V, in every group, so that the wait for
+    // a group's K leaves its V loads in flight, and the wait for each V leaves
+    // the next group's K loads in flight.
+    const int nsteps = (c1 - c0 + TPS - 1) / TPS;
+    u32x4 kb[PF], vb[PF];
+    Group gcur = group_where(0);
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const bool valid = t0 + (s0 + u) * TPS + wave * RPW + r < t1;
+    for (int u = 0; u < PF; ++u) kb[u] = load(kbase, gcur, u);
+#pragma unroll
+    for (int u = 0; u < PF; ++u) vb[u] = load(vbase, gcur, u);
+    Group gnext = group_where(PF);
+
+    for (int s0 = 0; s0 < nsteps; s0 += PF) {
+      float sc[PF][G];
+      const bool full = c0 + (s0 + PF) * TPS <= c1;  // no masked row in this group
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        const bool valid = full || (c0 + (s0 + u) * TPS + wave * RPW + r < c1);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float d = dot2<DT>(qv[g][0], kb[u].x, 0.f);
+          d = dot2<DT>(qv[g][1], kb[u].y, d);
+          d = dot2<DT>(qv[g][2], kb[u].z, d);
+          d = dot2<DT>(qv[g][3], kb[u].w, d);
+          d = group_sum<LPR>(d);
+          sc[u][g] = valid ? d * a.scale_log2 : -__builtin_inff();
+        }
+      }
+      // K registers are free: start the next group's K loads here, before the
+      // softmax and PV work (the scheduler may not sink them past it).
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < PF; ++u) kb[u] = load(kbase, gnext, u);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float d = dot2<DT>(qv[g][0], kb[u].x, 0.f);
-        d = dot2<DT>(qv[g][1], kb[u].y, d);
-        d = dot2<DT>(qv[g][2], kb[u].z, d);
-        d = dot2<DT>(qv[g][3], kb[u].w, d);
-        d = group_sum<LPR>(d);
-        sc[u][g] = valid ? d * a.scale_log2 : -__builtin_inff();
+        float mx = m[g];
+#pragma unroll
+        for (int u = 0; u < PF; ++u) mx = fmaxf(mx, sc[u][g]);
+        const float alpha = fast_exp2(m[g] - mx);
+        m[g] = mx;
+        l[g] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] *= alpha;
       }
-    }
-    // K registers are free: start the next group's K loads.
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      wh[u] = where(s0 + PF + u);
-      kb[u] = buffer_load16(make_rsrc(kbase + wh[u].boff, wh[u].nrec), wh[u].voff);
-    }
+      for (int u = 0; u < PF; ++u) {
+        float vf[8];
+        vf[0] = lo_f32<DT>(vb[u].x); vf[1] = hi_f32<DT>(vb[u].x);
+        vf[2] = lo_f32<DT>(vb[u].y); vf[3] = hi_f32<DT>(vb[u].y);
+        vf[4] = lo_f32<DT>(vb[u].z); vf[5] = hi_f32<DT>(vb[u].z);
+        vf[6] = lo_f32<DT>(vb[u].w); vf[7] = hi_f32<DT>(vb[u].w);
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mx = m[g];
+        for (int g = 0; g < G; ++g) {
+          const float p = fast_exp2(sc[u][g] - m[g]);
+          l[g] += p;
 #pragma unroll
-      for (int u = 0; u < PF; ++u) mx = fmaxf(mx, sc[u][g]);
-      const float alpha = fast_exp2(m[g] - mx);
-      m[g] = mx;
-      l[g] *= alpha;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[g][e] *= alpha;
-    }
-#pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      float vf[8];
-      vf[0] = lo_f32<DT>(vb[u].x); vf[1] = hi_f32<DT>(vb[u].x);
-      vf[2] = lo_f32<DT>(vb[u].y); vf[3] = hi_f32<DT>(vb[u].y);
-      vf[4] = lo_f32<DT>(vb[u].z); vf[5] = hi_f32<DT>(vb[u].z);
-      vf[6] = lo_f32<DT>(vb[u].w); vf[7] = hi_f32<DT>(vb[u].w);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float p = fast_exp2(sc[u][g] - m[g]);
-        l[g] += p;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
+          for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
+        }
+        vb[u] = load(vbase, gnext, u);
       }
-      vb[u] = buffer_load16(make_rsrc(vbase + wh[u].boff, wh[u].nrec), wh[u].voff);
+      gnext = group_where(s0 + 2 * PF);  // its LDS read overlaps the next group's scores
     }
   }
 
@@ -246,39 +305,83 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(const DecodeArgs 
 }
 
 // One wavefront per (sequence, query head): merge that row's partitions.
+// Lane p folds the (m, l) of partitions p, p+64, ...; the partial outputs are
+// fetched in batches of 8 partitions, each lane owning D/64 consecutive
+// dimensions.  The first batch and all (m, l) are loaded before the context
+// length is known; entries of partitions past the context are never used.
 template <int DT, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
   constexpr int E = D / 64;
+  constexpr int PB = 8;
+  typedef float floatE __attribute__((ext_vector_type(E)));
   const int lane = threadIdx.x;
   const int h = blockIdx.x % a.num_heads;
   const int seq = blockIdx.x / a.num_heads;
+  const int P = a.num_parts;
+  const int64_t base = ((int64_t)seq * a.num_heads + h) * P;
+  const float* po = a.part_out + base * D + lane * E;
+  floatE pv[PB];
+#pragma unroll
+  for (int j = 0; j < PB; ++j)
+    pv[j] = j < P ? *reinterpret_cast<const floatE*>(po + (int64_t)j * D) : floatE{};
+  const float m_own = lane < P ? a.part_ml[(base + lane) * 2] : 0.f;
+  const float l_own = lane < P ? a.part_ml[(base + lane) * 2 + 1] : 0.f;
+
   const int L = clamp_context(a, seq);
   const int n = L > 0 ? 1 + (L - 1) / a.part_tokens : 0;
   if (n <= 1) return;  // single-partition rows were written by the partition kernel
-  const int64_t base = ((int64_t)seq * a.num_heads + h) * a.num_parts;
-  const float* ml = a.part_ml + base * 2;
-  float M = -__builtin_inff();
-  for (int p = 0; p < n; ++p) M = fmaxf(M, ml[2 * p]);
-  float den = 0.f, o[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.f;
-  for (int p = 0; p < n; ++p) {
-    const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
-    den += w;
-    const float* po = a.part_out + (base + p) * D;
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = fmaf(w, po[lane + 64 * e], o[e]);
+
+  float mp = -__builtin_inff(), lp = 0.f;
+  if (lane < n) { mp = m_own; lp = l_own; }
+  for (int p = lane + 64; p < n; p += 64) {  // only with more than 64 partitions
+    const float m2 = a.part_ml[(base + p) * 2], l2 = a.part_ml[(base + p) * 2 + 1];
+    const float mn = fmaxf(mp, m2);           // finite: partition p holds a token
+    lp = lp * fast_exp2(mp - mn) + l2 * fast_exp2(m2 - mn);
+    mp = mn;
   }
-  uint16_t* out = static_cast<uint16_t*>(a.out) + ((int64_t)seq * a.num_heads + h) * D;
+  float M = mp;
 #pragma unroll
-  for (int e = 0; e < E; ++e) out[lane + 64 * e] = to_u16<DT>(o[e] / den);
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const float w_own = lane < n ? lp * fast_exp2(mp - M) : 0.f;  // lane p's weight if n <= 64
+  float den = w_own;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
+
+  floatE acc = {};
+  for (int p0 = 0; p0 < n; p0 += PB) {
+    if (p0 > 0) {
+#pragma unroll
+      for (int j = 0; j < PB; ++j)
+        pv[j] = p0 + j < n ? *reinterpret_cast<const floatE*>(po + (int64_t)(p0 + j) * D)
+                           : floatE{};
+    }
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      const int p = p0 + j;
+      if (p < n) {
+        float w;
+        if (n <= 64) {
+          w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_own), p));
+        } else {
+          w = a.part_ml[(base + p) * 2 + 1] * fast_exp2(a.part_ml[(base + p) * 2] - M);
+        }
+        acc += w * pv[j];
+      }
+    }
+  }
+  uint16_t* out = static_cast<uint16_t*>(a.out) + ((int64_t)seq * a.num_heads + h) * D + lane * E;
+  const float inv = 1.0f / den;
+#pragma unroll
+  for (int e = 0; e < E; ++e) out[e] = to_u16<DT>(acc[e] * inv);
 }
 
 template <int DT, int D, int BS, int G>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
-  constexpr int PF = (G <= 2) ? 8 : 4;
+  constexpr int PF = (G <= 2) ? PA_DECODE_PF : 4;
+  constexpr int WPE = (G <= 4) ? PA_DECODE_WPE : 2;
   const unsigned grid = (unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_parts);
-  hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, PF>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, PF, WPE, PA_DECODE_AUX>), dim3(grid),
+                     dim3(256), 0, s, a);
   if (a.num_parts > 1) {
     hipLaunchKernelGGL((decode_merge_kernel<DT, D>), dim3((unsigned)(a.num_seqs * a.num_heads)),
                        dim3(64), 0, s, a);

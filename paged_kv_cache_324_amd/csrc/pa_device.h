@@ -22,8 +22,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            kBufferWord3);
 }
 
+// Cache-policy bits of a buffer instruction on gfx94x/gfx950: nt marks data
+// that is read once (streamed), so it does not displace reused lines.
+constexpr int kCachePolicyNT = 2;
+
+template <int AUX = 0>
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voffset, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voffset, 0, AUX);
 }
 
 // ---- 16-bit float pairs packed in a dword ------------------------------------
