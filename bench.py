@@ -3,8 +3,8 @@
 
 A step is one pass of the decode hot path over one synthetic batch already
 resident in HBM: ``pa_reshape_and_cache`` writes each sequence's new K/V token
-into its cache slot, then ``pa_decode`` (partition kernel + partition merge)
-attends every query head over its paged context.  The default workload is the
+into its cache slot, then ``pa_decode`` (partition kernel + partition merge
+kernel) attends every query head over its paged context.  The default workload is the
 Qwen3-0.6B-shaped decode batch (128 sequences, 16 query / 8 KV heads, head_dim
 128, 16-token blocks shuffled over a 300k-block pool, context lengths uniform
 in [200, 2048], bf16).
@@ -95,8 +95,14 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qwen3_0p6b_decode")
     ap.add_argument("--partition", type=int, default=None, help="tokens per context partition")
+    ap.add_argument("--unfused", action="store_true",
+                    help="step = pa_reshape_and_cache + pa_decode (two launches) instead of the "
+                         "fused pa_decode_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--copy-kernel-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes (--steps "
+                         "times): the reference kernel for scaling HBM byte counters")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -112,6 +118,19 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+    if args.copy_kernel_bytes:
+        src = torch.ones(args.copy_kernel_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt_s = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"copy_bytes": args.copy_kernel_bytes, "steps": args.steps,
+                          "us_per_copy": round(dt_s * 1e6, 2),
+                          "read_plus_write_GBps": round(2 * args.copy_kernel_bytes / dt_s / 1e9, 1)}))
+        return 0
     pa.load_library()
     cfg = CONFIGS[args.workload]
     if cfg["kind"] != "decode":
@@ -141,19 +160,28 @@ def main(argv=None) -> int:
     tables = torch.from_numpy(b.block_tables).to(dev)
     lens = torch.from_numpy(b.context_lens).to(dev)
     out = torch.empty_like(q)
-    ws_bytes = pa.pa_decode_workspace_size(b.B, b.Hq, b.D, b.max_context_len, partition)
-    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    workspace = pa.decode_workspace(b.B, b.Hq, b.D, b.max_context_len, partition, dev)
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
 
+    # Longest-first visiting order of the sequences, computed on the host from
+    # the lengths the caller knows (the library's pa_decode_order).
+    order = torch.from_numpy(pa.pa_decode_order(b.context_lens)).to(dev)
+
     def step():
-        pa.pa_reshape_and_cache(key_new, value_new, k_cache, v_cache, slot, stream=stream)
-        pa.pa_decode(out, q, k_cache, v_cache, tables, lens, b.scale, b.max_context_len, partition,
-                     workspace=workspace, stream=stream)
+        if args.unfused:
+            pa.pa_reshape_and_cache(key_new, value_new, k_cache, v_cache, slot, stream=stream)
+            pa.pa_decode(out, q, k_cache, v_cache, tables, lens, b.scale, b.max_context_len,
+                         partition, workspace=workspace, seq_order=order, stream=stream)
+        else:
+            pa.pa_decode_step(out, q, key_new, value_new, slot, k_cache, v_cache, tables, lens,
+                              b.scale, b.max_context_len, partition, workspace=workspace,
+                              seq_order=order, stream=stream)
 
     def decode_only():
-        pa.pa_decode(out, q, k_cache, v_cache, tables, lens, b.scale, b.max_context_len, partition,
-                     workspace=workspace, stream=stream)
+        step() if not args.unfused else pa.pa_decode(
+            out, q, k_cache, v_cache, tables, lens, b.scale, b.max_context_len, partition,
+            workspace=workspace, seq_order=order, stream=stream)
 
     for _ in range(args.warmup):
         step()

@@ -115,22 +115,58 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int m
  * zero row.  Context lengths above max_context_len are treated as
  * max_context_len (which must be <= max_blocks_per_seq * block_size).
  *
+ * seq_order: NULL, or an int32 [num_seqs] device array holding a permutation
+ * of 0..num_seqs-1: the order in which the kernel's workgroups take up the
+ * sequences.  It changes no result, only the schedule: longest context first
+ * (pa_decode_order) lets the hardware dispatcher balance the compute units.
+ * Entries outside [0, num_seqs) are skipped (those outputs are not written).
+ *
  * partition_size: 0 = each (sequence, KV head) is processed by one workgroup;
  * otherwise a positive multiple of block_size: the context is split into
  * partitions of that many tokens processed in parallel and merged by a second
  * kernel using each partition's fp32 max and sum, which needs
  * pa_decode_workspace_size(...) bytes of `workspace` (device memory, caller
- * owned, no initialisation needed, reused only after the call's kernels finish
- * on `stream`).
+ * owned, 16-byte aligned, no initialisation needed, reused only after the
+ * call's kernels finish on `stream`).
  *
  * Supported: num_heads / num_kv_heads in {1, 2, 4, 8}; head_dim in {64, 128};
  * block_size in {16, 32, 256}; dtype PA_F16 or PA_BF16; finite scale.
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-              const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
-              int num_heads, int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
-              int max_blocks_per_seq, int max_context_len, float scale, int partition_size,
-              void* workspace, size_t workspace_bytes, int dtype, void* stream);
+              const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
+              int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+              int64_t num_blocks, int max_blocks_per_seq, int max_context_len, float scale,
+              int partition_size, void* workspace, size_t workspace_bytes, int dtype,
+              void* stream);
+
+/*
+ * pa_decode_step: one decode step, i.e. pa_reshape_and_cache of one new token
+ * per sequence followed by pa_decode, in a single kernel launch.  The new
+ * token of sequence i is logical position context_lens[i] - 1; its rows
+ * key[i], value[i] ([num_seqs][num_kv_heads][head_dim]) are attended to as
+ * that position's K/V and stored bit for bit at cache slot slot_mapping[i]
+ * (skipped when the slot is negative or outside the pool).  Cache positions
+ * below context_lens[i] - 1 are read from the caches.  Results equal
+ * pa_reshape_and_cache followed by pa_decode whenever slot_mapping[i] is the
+ * slot of position context_lens[i] - 1 in sequence i's block table; the
+ * summation order differs, so bits may differ within rounding.  Other
+ * arguments, workspace rules and supported shapes as for pa_decode.
+ */
+int pa_decode_step(void* out, const void* q, const void* key, const void* value,
+                   const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                   const int32_t* block_tables, const int32_t* context_lens,
+                   const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads,
+                   int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                   int max_context_len, float scale, int partition_size, void* workspace,
+                   size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * pa_decode_order: host-side helper (HOST pointers, no GPU work).  Writes to
+ * order[0..num_seqs) the sequence indices sorted by decreasing
+ * context_lens[i], equal lengths in index order -- the longest-first visiting
+ * order to pass (after a copy to the device) as seq_order.
+ */
+int pa_decode_order(const int32_t* context_lens, int num_seqs, int32_t* order);
 
 /*
  * pa_prefill_chunk: chunked prefill over the paged cache (single-device

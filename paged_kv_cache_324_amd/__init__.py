@@ -8,8 +8,11 @@ from ._binding import (  # noqa: F401
     PA_BF16,
     PA_F16,
     PAError,
+    decode_workspace,
     load_library,
     pa_decode,
+    pa_decode_order,
+    pa_decode_step,
     pa_decode_workspace_size,
     pa_prefill_chunk,
     pa_reshape_and_cache,

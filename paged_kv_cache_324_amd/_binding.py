@@ -45,8 +45,14 @@ def _declare(lib):
     lib.pa_decode_workspace_size.restype = c_sz
     lib.pa_decode_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int]
     lib.pa_decode.restype = c_int
-    lib.pa_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int,
-                              c_i64, c_int, c_int, c_f, c_int, c_vp, c_sz, c_int, c_vp]
+    lib.pa_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
+                              c_int, c_i64, c_int, c_int, c_f, c_int, c_vp, c_sz, c_int, c_vp]
+    lib.pa_decode_step.restype = c_int
+    lib.pa_decode_step.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                   c_int, c_int, c_int, c_int, c_int, c_i64, c_int, c_int, c_f,
+                                   c_int, c_vp, c_sz, c_int, c_vp]
+    lib.pa_decode_order.restype = c_int
+    lib.pa_decode_order.argtypes = [c_vp, c_int, c_vp]
     lib.pa_prefill_chunk.restype = c_int
     lib.pa_prefill_chunk.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_int,
                                      c_int, c_int, c_int, c_i64, c_int, c_int, c_f, c_int, c_vp]
@@ -111,6 +117,13 @@ def pa_decode_workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_c
                                                        max_context_len, partition_size))
 
 
+def decode_workspace(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
+                     partition_size: int, device) -> torch.Tensor:
+    """A workspace of the size pa_decode needs (one byte if none)."""
+    n = pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len, partition_size)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
 def pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:
     """Write key/value ``[T][Hkv][D]`` into caches ``[NB][BS][Hkv][D]`` at ``slot_mapping`` (int64)."""
     lib = load_library()
@@ -128,10 +141,8 @@ def pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None
                                     T, Hkv, D, BS, NB, dt, _stream(key, stream)))
 
 
-def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
-              max_context_len: int, partition_size: int = 512, workspace=None,
-              stream=None) -> torch.Tensor:
-    """Paged decode: ``out[i][h] = softmax(scale q K^T) V`` over each sequence's paged context."""
+def _decode_common(q, k_cache, v_cache, block_tables, context_lens, seq_order, out,
+                   max_context_len, partition_size, workspace):
     lib = load_library()
     B, Hq, D = q.shape
     NB, BS, Hkv, D2 = k_cache.shape
@@ -139,6 +150,8 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
         raise ValueError("decode: inconsistent shapes")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("decode: block_tables must be [B][max_blocks], context_lens [B]")
+    if seq_order is not None and seq_order.shape != (B,):
+        raise ValueError("decode: seq_order must be [B]")
     dt = _dtype_code(q)
     for n, x in (("out", out), ("k_cache", k_cache), ("v_cache", v_cache)):
         _dev(x, n, q.dtype)
@@ -148,13 +161,55 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
         if workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    order_ptr = None if seq_order is None else _dev(seq_order, "seq_order", torch.int32)
+    return (lib, B, Hq, Hkv, D, BS, NB, dt, ws_ptr, ws_bytes, order_ptr)
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+              max_context_len: int, partition_size: int = 512, workspace=None, seq_order=None,
+              stream=None) -> torch.Tensor:
+    """Paged decode: ``out[i][h] = softmax(scale q K^T) V`` over each sequence's paged context."""
+    lib, B, Hq, Hkv, D, BS, NB, dt, ws_ptr, ws_bytes, order_ptr = _decode_common(
+        q, k_cache, v_cache, block_tables, context_lens, seq_order, out, max_context_len,
+        partition_size, workspace)
     _check(lib.pa_decode(_dev(out, "out"), _dev(q, "q"), k_cache.data_ptr(), v_cache.data_ptr(),
                          _dev(block_tables, "block_tables", torch.int32),
-                         _dev(context_lens, "context_lens", torch.int32),
+                         _dev(context_lens, "context_lens", torch.int32), order_ptr,
                          B, Hq, Hkv, D, BS, NB, block_tables.shape[1], int(max_context_len),
                          float(scale), int(partition_size), ws_ptr, ws_bytes, dt,
                          _stream(q, stream)))
     return out
+
+
+def pa_decode_step(out, q, key, value, slot_mapping, k_cache, v_cache, block_tables,
+                   context_lens, scale: float, max_context_len: int, partition_size: int = 512,
+                   workspace=None, seq_order=None, stream=None) -> torch.Tensor:
+    """One decode step: store each sequence's new K/V token at its slot and attend, in one launch."""
+    lib, B, Hq, Hkv, D, BS, NB, dt, ws_ptr, ws_bytes, order_ptr = _decode_common(
+        q, k_cache, v_cache, block_tables, context_lens, seq_order, out, max_context_len,
+        partition_size, workspace)
+    if key.shape != (B, Hkv, D) or value.shape != key.shape or slot_mapping.shape != (B,):
+        raise ValueError("decode step: key/value must be [B][Hkv][D], slot_mapping [B]")
+    _dev(key, "key", q.dtype)
+    _dev(value, "value", q.dtype)
+    _check(lib.pa_decode_step(_dev(out, "out"), _dev(q, "q"), key.data_ptr(), value.data_ptr(),
+                              _dev(slot_mapping, "slot_mapping", torch.int64),
+                              k_cache.data_ptr(), v_cache.data_ptr(),
+                              _dev(block_tables, "block_tables", torch.int32),
+                              _dev(context_lens, "context_lens", torch.int32), order_ptr,
+                              B, Hq, Hkv, D, BS, NB, block_tables.shape[1], int(max_context_len),
+                              float(scale), int(partition_size), ws_ptr, ws_bytes, dt,
+                              _stream(q, stream)))
+    return out
+
+
+def pa_decode_order(context_lens) -> "numpy.ndarray":
+    """Longest-first visiting order of the sequences (host computation) as int32."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    order = np.empty(lens.shape[0], dtype=np.int32)
+    _check(load_library().pa_decode_order(lens.ctypes.data, lens.shape[0], order.ctypes.data))
+    return order
 
 
 def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,

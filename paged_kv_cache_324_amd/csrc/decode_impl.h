@@ -78,11 +78,16 @@ void decode_partition_kernel(const DecodeArgs a) {
   // before any second partition, so long contexts start early and the
   // workgroups of partitions past a short context (which exit at once) come
   // last.
+  // Within a partition index, sequences are visited in `seq_order` when one
+  // is given (longest first lets the dispatcher balance the CUs like
+  // longest-processing-time list scheduling).
   const int per_part = a.num_seqs * a.num_kv_heads;
   const int part = blockIdx.x / per_part;
   const int rest = blockIdx.x - part * per_part;
-  const int seq = rest / a.num_kv_heads;
-  const int kvh = rest - seq * a.num_kv_heads;
+  const int rank = rest / a.num_kv_heads;
+  const int kvh = rest - rank * a.num_kv_heads;
+  const int seq = a.seq_order ? a.seq_order[rank] : rank;
+  if (seq < 0 || seq >= a.num_seqs) return;  // not a permutation entry: nothing to do
   const int h0 = kvh * G;
 
   // Issue the independent loads of the prologue together: the context
@@ -116,6 +121,17 @@ void decode_partition_kernel(const DecodeArgs a) {
   if (t0 >= L) return;
   const int t1 = min(L, t0 + a.part_tokens);
   const int nparts_seq = 1 + (L - 1) / a.part_tokens;
+  // Fused step: the partition holding position L-1 reads only the cached
+  // tokens before it and takes the new token's rows from key_new/value_new
+  // (fetched now, used after the cached tokens).
+  const bool new_here = a.key_new != nullptr && t1 == L;
+  const int t1c = new_here ? L - 1 : t1;
+  u32x4 k_new = {0u, 0u, 0u, 0u}, v_new = {0u, 0u, 0u, 0u};
+  if (new_here && wave == 0 && r == 0) {
+    const int64_t row = ((int64_t)seq * a.num_kv_heads + kvh) * D;
+    k_new = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.key_new) + row)[c];
+    v_new = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.value_new) + row)[c];
+  }
 
   const uint32_t row_stride = (uint32_t)a.num_kv_heads * D * 2;
   const uint64_t block_bytes = (uint64_t)BS * row_stride;
@@ -137,8 +153,8 @@ void decode_partition_kernel(const DecodeArgs a) {
   // LDS read instead of a dependent scalar load.
   const int32_t nb32 = a.num_blocks > INT32_MAX ? INT32_MAX : (int32_t)a.num_blocks;
   constexpr int kChunkTokens = kTableCap * BS;
-  for (int c0 = t0; c0 < t1; c0 += kChunkTokens) {
-    const int c1 = min(t1, c0 + kChunkTokens);
+  for (int c0 = t0; c0 < t1c; c0 += kChunkTokens) {
+    const int c1 = min(t1c, c0 + kChunkTokens);
     const int lb0 = c0 / BS;
     const int nchunk_blk = (c1 - c0 + BS - 1) / BS;
     static_assert(kTableCap == 256, "one table entry per thread");
@@ -240,6 +256,38 @@ void decode_partition_kernel(const DecodeArgs a) {
         vb[u] = load(vbase, gnext, u);
       }
       gnext = group_where(s0 + 2 * PF);  // its LDS read overlaps the next group's scores
+    }
+  }
+
+  if (new_here && wave == 0) {
+    // Row slot 0 of wavefront 0 takes the new token; in the other row slots
+    // the score is -inf, which leaves their state unchanged.
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float d = dot2<DT>(qv[g][0], k_new.x, 0.f);
+      d = dot2<DT>(qv[g][1], k_new.y, d);
+      d = dot2<DT>(qv[g][2], k_new.z, d);
+      d = dot2<DT>(qv[g][3], k_new.w, d);
+      d = group_sum<LPR>(d);
+      const float sc = r == 0 ? d * a.scale_log2 : -__builtin_inff();
+      const float mx = fmaxf(m[g], sc);
+      const float alpha = fast_exp2(m[g] - mx), p = fast_exp2(sc - mx);
+      m[g] = mx;
+      l[g] = fmaf(l[g], alpha, p);
+      acc[g][0] = fmaf(acc[g][0], alpha, p * lo_f32<DT>(v_new.x));
+      acc[g][1] = fmaf(acc[g][1], alpha, p * hi_f32<DT>(v_new.x));
+      acc[g][2] = fmaf(acc[g][2], alpha, p * lo_f32<DT>(v_new.y));
+      acc[g][3] = fmaf(acc[g][3], alpha, p * hi_f32<DT>(v_new.y));
+      acc[g][4] = fmaf(acc[g][4], alpha, p * lo_f32<DT>(v_new.z));
+      acc[g][5] = fmaf(acc[g][5], alpha, p * hi_f32<DT>(v_new.z));
+      acc[g][6] = fmaf(acc[g][6], alpha, p * lo_f32<DT>(v_new.w));
+      acc[g][7] = fmaf(acc[g][7], alpha, p * hi_f32<DT>(v_new.w));
+    }
+    const int64_t slot = a.slot_mapping[seq];
+    if (r == 0 && slot >= 0 && slot < a.num_slots) {
+      const int64_t dst = (slot * a.num_kv_heads + kvh) * D;
+      reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.k_cache_w) + dst)[c] = k_new;
+      reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.v_cache_w) + dst)[c] = v_new;
     }
   }
 

@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 
 #include "pa.h"
 #include "pa_kernels.h"
@@ -138,11 +139,24 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int m
                              num_partitions(max_context_len, partition_size));
 }
 
-int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-              const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
-              int num_heads, int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
-              int max_blocks_per_seq, int max_context_len, float scale, int partition_size,
-              void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+struct NewTokens {
+  const void* key;
+  const void* value;
+  const int64_t* slot_mapping;
+  void* k_cache;
+  void* v_cache;
+};
+
+int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens,
+                const int32_t* seq_order, const NewTokens* nt, int num_seqs, int num_heads,
+                int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                int max_blocks_per_seq, int max_context_len, float scale, int partition_size,
+                void* workspace, size_t workspace_bytes, int dtype, void* stream) {
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0");
   int st = check_cache(num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                        max_blocks_per_seq, dtype);
@@ -156,6 +170,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
                 partition_size, block_size);
   if (num_seqs == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (nt && (!nt->key || !nt->value || !nt->slot_mapping || !nt->k_cache || !nt->v_cache))
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   const int64_t parts = num_partitions(max_context_len, partition_size);
   const int64_t grid = (int64_t)num_seqs * num_kv_heads * parts;
@@ -182,6 +198,13 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   a.part_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                              align_up(rows * head_dim * sizeof(float)))
                    : nullptr;
+  a.seq_order = seq_order;
+  a.key_new = nt ? nt->key : nullptr;
+  a.value_new = nt ? nt->value : nullptr;
+  a.slot_mapping = nt ? nt->slot_mapping : nullptr;
+  a.k_cache_w = nt ? nt->k_cache : nullptr;
+  a.v_cache_w = nt ? nt->v_cache : nullptr;
+  a.num_slots = num_blocks * (int64_t)block_size;
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
@@ -196,6 +219,48 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   hipError_t e = dtype == PA_BF16 ? pa::launch_decode_bf16(a, head_dim, block_size, group, s)
                                   : pa::launch_decode_f16(a, head_dim, block_size, group, s);
   return hip_status(e, "decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
+              int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+              int64_t num_blocks, int max_blocks_per_seq, int max_context_len, float scale,
+              int partition_size, void* workspace, size_t workspace_bytes, int dtype,
+              void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, seq_order, nullptr,
+                     num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
+                     workspace_bytes, dtype, stream);
+}
+
+int pa_decode_step(void* out, const void* q, const void* key, const void* value,
+                   const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                   const int32_t* block_tables, const int32_t* context_lens,
+                   const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads,
+                   int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                   int max_context_len, float scale, int partition_size, void* workspace,
+                   size_t workspace_bytes, int dtype, void* stream) {
+  NewTokens nt{key, value, slot_mapping, k_cache, v_cache};
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, seq_order, &nt,
+                     num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
+                     workspace_bytes, dtype, stream);
+}
+
+int pa_decode_order(const int32_t* context_lens, int num_seqs, int32_t* order) {
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0");
+  if (num_seqs == 0) return ok();
+  if (!context_lens || !order) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  for (int i = 0; i < num_seqs; ++i) order[i] = i;
+  // Longest context first; equal lengths keep their index order.
+  std::stable_sort(order, order + num_seqs, [context_lens](int32_t x, int32_t y) {
+    return context_lens[x] > context_lens[y];
+  });
+  return ok();
 }
 
 int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,

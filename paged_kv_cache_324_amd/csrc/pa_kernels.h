@@ -26,6 +26,16 @@ struct DecodeArgs {
   const int32_t* context_lens;
   float* part_out;     // [num_seqs][num_heads][num_parts][head_dim], partition-normalised
   float* part_ml;      // [num_seqs][num_heads][num_parts][2]: log2-domain max, sum
+  const int32_t* seq_order;  // optional [num_seqs]: order in which sequences are visited
+  // Fused decode step (all null otherwise): this step's token of sequence i is
+  // at position context_lens[i] - 1; its K/V rows come from key_new/value_new
+  // [num_seqs][num_kv_heads][head_dim] and are also stored at slot_mapping[i].
+  const void* key_new;
+  const void* value_new;
+  const int64_t* slot_mapping;
+  void* k_cache_w;
+  void* v_cache_w;
+  int64_t num_slots;   // num_blocks * block_size
   int64_t num_blocks;
   int num_seqs;
   int num_heads;

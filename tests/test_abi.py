@@ -48,7 +48,7 @@ def _decode(lib, **kw):
     a = dict(out=P, q=P, k=P, v=P, bt=P, lens=P, B=2, Hq=16, Hkv=8, D=128, BS=16, NB=100,
              maxb=10, maxL=160, scale=0.1, part=0, ws=None, wsb=0, dt=pa.PA_BF16)
     a.update(kw)
-    return lib.pa_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["lens"], a["B"], a["Hq"],
+    return lib.pa_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["lens"], None, a["B"], a["Hq"],
                          a["Hkv"], a["D"], a["BS"], a["NB"], a["maxb"], a["maxL"], a["scale"],
                          a["part"], a["ws"], a["wsb"], a["dt"], None)
 
@@ -116,9 +116,37 @@ def test_prefill_rejects_bad_arguments(lib):
 
 
 def test_python_binding_names_match_c_entry_points():
-    for name in ("pa_reshape_and_cache", "pa_decode", "pa_decode_workspace_size",
-                 "pa_prefill_chunk"):
+    for name in ("pa_reshape_and_cache", "pa_decode", "pa_decode_step", "pa_decode_order",
+                 "pa_decode_workspace_size", "pa_prefill_chunk"):
         assert callable(getattr(pa, name))
+
+
+def test_decode_step_rejects_bad_arguments(lib):
+    f = lib.pa_decode_step
+    base = [P, P, P, P, P, P, P, P, P, None, 2, 16, 8, 128, 16, 100, 10, 160, 0.1, 0, None, 0,
+            pa.PA_BF16, None]
+    bad = list(base)
+    bad[4] = None                          # slot_mapping
+    assert f(*bad) == -1 and "null" in lib.pa_last_error().decode()
+    bad = list(base)
+    bad[13] = 80                           # head_dim
+    assert f(*bad) == -2
+    bad = list(base)
+    bad[19] = 32                           # needs a workspace
+    assert f(*bad) == -3
+
+
+def test_decode_order_is_longest_first_and_stable():
+    import numpy as np
+    lens = np.array([5, 9, 5, 0, 12, 9, 1], dtype=np.int32)
+    order = pa.pa_decode_order(lens)
+    assert order.tolist() == [4, 1, 5, 0, 2, 6, 3]
+    rng = np.random.default_rng(3)
+    lens = rng.integers(0, 3000, size=1000).astype(np.int32)
+    order = pa.pa_decode_order(lens)
+    assert sorted(order.tolist()) == list(range(1000))
+    assert np.all(np.diff(lens[order]) <= 0)
+    assert pa.pa_decode_order(np.zeros(0, np.int32)).shape == (0,)
 
 
 def test_bench_refuses_several_gpus():

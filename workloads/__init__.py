@@ -36,7 +36,7 @@ CONFIGS = {
         dtype="f16", scale=1.0 / 8.0, share=0.0, partition=0, seed=324_001),
     "qwen3_0p6b_decode": dict(
         kind="decode", B=128, Hq=16, Hkv=8, D=128, BS=16, NB=300_000, lens=(200, 2048),
-        dtype="bf16", scale=1.0 / math.sqrt(128), share=0.0, partition=512, seed=324_002),
+        dtype="bf16", scale=1.0 / math.sqrt(128), share=0.0, partition=0, seed=324_002),
     "llama2_70b_decode_bs16": dict(
         kind="decode", B=64, Hq=64, Hkv=8, D=128, BS=16, NB=None, lens=(4096, 8192),
         dtype="bf16", scale=1.0 / math.sqrt(128), share=0.10, partition=512, seed=324_003),
