@@ -170,29 +170,33 @@ int pa_decode_order(const int32_t* context_lens, int num_seqs, int32_t* order);
 
 /*
  * pa_prefill_chunk: chunked prefill over the paged cache (single-device
- * chunking of long prefills, page "vllm-ascend architecture", section 1.1 and
- * 3.1).  Sequence i contributes n_i = query_start_loc[i+1] - query_start_loc[i]
- * new query tokens (rows query_start_loc[i] .. query_start_loc[i+1]-1 of q and
- * out) that follow c_i = context_lens[i] - n_i cached tokens; the new tokens'
- * keys and values must already be in the cache (pa_reshape_and_cache).  New
- * token t attends to logical keys 0 .. c_i + t (its own key included).
+ * chunking of long prefills, page "vllm-ascend architecture", sections 1.1
+ * and 3.1).  Sequence i contributes n_i = query_start_loc[i+1] -
+ * query_start_loc[i] new query tokens (rows query_start_loc[i] ..
+ * query_start_loc[i+1]-1 of q and out) that follow c_i = context_lens[i] - n_i
+ * cached tokens; the new tokens' keys and values must already be in the cache
+ * (pa_reshape_and_cache).  New token t attends to logical keys 0 .. c_i + t
+ * (its own key included); a row that sees no key (c_i + t < 0, a caller
+ * error) is written as zeros.
  *
  *   out, q          [num_tokens][num_heads][head_dim]
  *   query_start_loc int32 [num_seqs + 1], non-decreasing, query_start_loc[0] = 0,
  *                   query_start_loc[num_seqs] = num_tokens
+ *   seq_order       NULL or a permutation of 0..num_seqs-1 (visiting order, as
+ *                   for pa_decode; longest context first balances best)
  *   max_query_len   >= every n_i (sizes the grid; longer chunks are truncated)
  *
- * QK^T and PV run as bf16/fp16 matrix-core (MFMA) tiles with fp32
- * accumulation; the softmax is fp32 and the probabilities are rounded to the
- * input dtype before the PV product.  Supported shapes as for pa_decode;
- * head_dim must be 128 and the group size 1, 2, 4 or 8.
+ * QK^T and PV run as 32x32x16 matrix-core (MFMA) tiles with fp32 accumulation;
+ * the softmax is fp32 and the probabilities are rounded to the input dtype
+ * before the PV product.  Supported: head_dim 128; block_size 16, 32, 256;
+ * num_heads / num_kv_heads in {1, 2, 4, 8}; dtype PA_F16 or PA_BF16.
  */
 int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_tables, const int32_t* context_lens,
-                     const int32_t* query_start_loc, int num_seqs, int64_t num_tokens,
-                     int num_heads, int num_kv_heads, int head_dim, int block_size,
-                     int64_t num_blocks, int max_blocks_per_seq, int max_query_len, float scale,
-                     int dtype, void* stream);
+                     const int32_t* query_start_loc, const int32_t* seq_order, int num_seqs,
+                     int64_t num_tokens, int num_heads, int num_kv_heads, int head_dim,
+                     int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                     int max_query_len, float scale, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

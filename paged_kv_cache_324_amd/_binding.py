@@ -54,8 +54,9 @@ def _declare(lib):
     lib.pa_decode_order.restype = c_int
     lib.pa_decode_order.argtypes = [c_vp, c_int, c_vp]
     lib.pa_prefill_chunk.restype = c_int
-    lib.pa_prefill_chunk.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_int,
-                                     c_int, c_int, c_int, c_i64, c_int, c_int, c_f, c_int, c_vp]
+    lib.pa_prefill_chunk.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64,
+                                     c_int, c_int, c_int, c_int, c_i64, c_int, c_int, c_f, c_int,
+                                     c_vp]
     return lib
 
 
@@ -213,7 +214,7 @@ def pa_decode_order(context_lens) -> "numpy.ndarray":
 
 
 def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
-                     max_query_len: int, scale: float, stream=None) -> torch.Tensor:
+                     max_query_len: int, scale: float, seq_order=None, stream=None) -> torch.Tensor:
     """Chunked prefill: query rows of each sequence attend causally over its paged context."""
     lib = load_library()
     T, Hq, D = q.shape
@@ -223,13 +224,16 @@ def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, context_lens, query
         raise ValueError("prefill: inconsistent shapes")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or query_start_loc.shape != (B + 1,):
         raise ValueError("prefill: block_tables must be [B][max_blocks], query_start_loc [B+1]")
+    if seq_order is not None and seq_order.shape != (B,):
+        raise ValueError("prefill: seq_order must be [B]")
     dt = _dtype_code(q)
     for n, x in (("out", out), ("k_cache", k_cache), ("v_cache", v_cache)):
         _dev(x, n, q.dtype)
+    order_ptr = None if seq_order is None else _dev(seq_order, "seq_order", torch.int32)
     _check(lib.pa_prefill_chunk(_dev(out, "out"), _dev(q, "q"), k_cache.data_ptr(), v_cache.data_ptr(),
                                 _dev(block_tables, "block_tables", torch.int32),
                                 _dev(context_lens, "context_lens", torch.int32),
-                                _dev(query_start_loc, "query_start_loc", torch.int32),
+                                _dev(query_start_loc, "query_start_loc", torch.int32), order_ptr,
                                 B, T, Hq, Hkv, D, BS, NB, block_tables.shape[1], int(max_query_len),
                                 float(scale), dt, _stream(q, stream)))
     return out

@@ -265,7 +265,8 @@ int pa_decode_order(const int32_t* context_lens, int num_seqs, int32_t* order) {
 
 int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_tables, const int32_t* context_lens,
-                     const int32_t* query_start_loc, int num_seqs, int64_t num_tokens,
+                     const int32_t* query_start_loc, const int32_t* seq_order, int num_seqs,
+                     int64_t num_tokens,
                      int num_heads, int num_kv_heads, int head_dim, int block_size,
                      int64_t num_blocks, int max_blocks_per_seq, int max_query_len, float scale,
                      int dtype, void* stream) {
@@ -290,6 +291,7 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.query_start_loc = query_start_loc;
+  a.seq_order = seq_order;
   a.num_blocks = num_blocks;
   a.num_tokens = num_tokens;
   a.num_seqs = num_seqs;

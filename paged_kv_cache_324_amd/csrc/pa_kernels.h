@@ -55,6 +55,7 @@ struct PrefillArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   const int32_t* query_start_loc;
+  const int32_t* seq_order;  // optional [num_seqs]: order in which sequences are visited
   int64_t num_blocks;
   int64_t num_tokens;
   int num_seqs;

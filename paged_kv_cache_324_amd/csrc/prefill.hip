@@ -1,9 +1,11 @@
-// Chunked prefill over the paged cache (MFMA kernel lands here).
-#include "pa_device.h"
-#include "pa_kernels.h"
+// Instantiations of the MFMA chunked-prefill kernel (head_dim 128).
+#include "prefill_impl.h"
 
 namespace pa {
-hipError_t launch_prefill(const PrefillArgs&, int, int, int, int, hipStream_t) {
-  return hipErrorNotSupported;
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int block_size, int group,
+                          hipStream_t s) {
+  if (head_dim != kPrefillD) return hipErrorInvalidValue;
+  return dtype == DT_BF16 ? launch_prefill_dt<DT_BF16>(a, block_size, group, s)
+                          : launch_prefill_dt<DT_F16>(a, block_size, group, s);
 }
 }  // namespace pa

@@ -100,19 +100,22 @@ def test_reshape_rejects_bad_arguments(lib):
 
 def test_prefill_rejects_bad_arguments(lib):
     f = lib.pa_prefill_chunk
-    args = [P, P, P, P, P, P, P, 2, 64, 32, 8, 128, 16, 100, 10, 32, 0.1, pa.PA_BF16, None]
+    args = [P, P, P, P, P, P, P, None, 2, 64, 32, 8, 128, 16, 100, 10, 32, 0.1, pa.PA_BF16, None]
     bad = list(args)
     bad[6] = None
     assert f(*bad) == -1
     bad = list(args)
-    bad[9] = 6      # 32 heads over 6 KV heads
+    bad[10] = 6     # 32 heads over 6 KV heads
     assert f(*bad) == -1
     bad = list(args)
-    bad[16] = float("nan")
+    bad[17] = float("nan")
     assert f(*bad) == -1
     bad = list(args)
-    bad[15] = -1
+    bad[16] = -1
     assert f(*bad) == -1
+    bad = list(args)
+    bad[12] = 64    # head_dim 64 has no prefill kernel
+    assert f(*bad) == -2
 
 
 def test_python_binding_names_match_c_entry_points():
