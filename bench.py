@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged-attn decode effective KV GB/s (% of HBM peak) + sequences/s, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16/fp16 matrix-core peak
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["paged_kv_cache_324_amd/csrc/decode_impl.h",
                   "paged_kv_cache_324_amd/csrc/pa_device.h"]
@@ -88,6 +89,120 @@ def cpu_baseline(b, budget_s: float = 10.0):
             "host_cpus_visible": len(os.sched_getaffinity(0))}
 
 
+def _stats_us(ms):
+    return {"mean": round(float(np.mean(ms)) * 1e3, 2), "p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
+            "p50": round(float(np.median(ms)) * 1e3, 2), "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)}
+
+
+def prefill_flops(b) -> float:
+    """Algorithmic FLOPs of a chunk: 2 D per visible key for QK^T and 2 D for PV, every query head."""
+    n = b.n_new.astype(np.int64)
+    c = b.context_lens.astype(np.int64) - n
+    visible = (n * c + n * (n + 1) // 2).sum()
+    return float(4 * b.D * b.Hq * visible)
+
+
+def upload(torch, b, dev):
+    """Device pool of b.NB blocks, NaN everywhere except the referenced blocks."""
+    import types
+    dt = torch.bfloat16 if b.dtype == "bf16" else torch.float16
+    shape = (b.NB, b.BS, b.Hkv, b.D)
+    k_cache = torch.full(shape, -1, dtype=torch.int16, device=dev)
+    v_cache = torch.full(shape, -1, dtype=torch.int16, device=dev)
+    idx = torch.from_numpy(b.phys_ids).to(dev)
+    k_cache[idx] = torch.from_numpy(b.k_blocks.view(np.int16)).to(dev)
+    v_cache[idx] = torch.from_numpy(b.v_blocks.view(np.int16)).to(dev)
+
+    def dev16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(dt)
+
+    return types.SimpleNamespace(
+        k_cache=k_cache.view(dt), v_cache=v_cache.view(dt), q=dev16(b.q), key_new=dev16(b.key_new),
+        value_new=dev16(b.value_new), slot=torch.from_numpy(b.slot_mapping).to(dev),
+        tables=torch.from_numpy(b.block_tables).to(dev),
+        lens=torch.from_numpy(b.context_lens).to(dev),
+        qsl=torch.from_numpy(b.query_start_loc).to(dev))
+
+
+def _timed(torch, fn, steps):
+    """Wall time of `steps` back-to-back calls, nothing else on the stream."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
+
+
+def _events(torch, fn, steps, stream):
+    """Per-call durations (ms) of fn, each bracketed by HIP events on `stream`."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for s, e in ev:
+        s.record(stream)
+        fn()
+        e.record(stream)
+    torch.cuda.synchronize()
+    return np.array([s.elapsed_time(e) for s, e in ev])
+
+
+def run_decode(pa, torch, b, partition, steps, warmup, unfused, dev):
+    d = upload(torch, b, dev)
+    out = torch.empty_like(d.q)
+    workspace = pa.decode_workspace(b.B, b.Hq, b.D, b.max_context_len, partition, dev)
+    stream = torch.cuda.current_stream(dev)
+    # Longest-first visiting order of the sequences, computed on the host from
+    # the lengths the caller knows (the library's pa_decode_order).
+    order = torch.from_numpy(pa.pa_decode_order(b.context_lens)).to(dev)
+
+    def decode():
+        pa.pa_decode(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, b.scale, b.max_context_len,
+                     partition, workspace=workspace, seq_order=order, stream=stream)
+
+    def step():
+        if unfused:
+            pa.pa_reshape_and_cache(d.key_new, d.value_new, d.k_cache, d.v_cache, d.slot,
+                                    stream=stream)
+            decode()
+        else:
+            pa.pa_decode_step(out, d.q, d.key_new, d.value_new, d.slot, d.k_cache, d.v_cache,
+                              d.tables, d.lens, b.scale, b.max_context_len, partition,
+                              workspace=workspace, seq_order=order, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    ms = _timed(torch, step, steps)                       # the timed region
+    kernel_ms = _events(torch, decode if unfused else step, steps, stream)
+    name = ("pa_decode" if unfused else "pa_decode_step") + (
+        " (partition + merge kernels)" if partition and b.max_context_len > partition else
+        " (one decode_partition_kernel launch)")
+    return {"ms_per_step": ms, "kernel_ms": kernel_ms, "kernel_name": name}
+
+
+def run_prefill(pa, torch, b, steps, warmup, dev):
+    d = upload(torch, b, dev)
+    out = torch.empty_like(d.q)
+    stream = torch.cuda.current_stream(dev)
+    order = torch.from_numpy(pa.pa_decode_order(b.context_lens)).to(dev)
+
+    def reshape():
+        pa.pa_reshape_and_cache(d.key_new, d.value_new, d.k_cache, d.v_cache, d.slot, stream=stream)
+
+    def prefill():
+        pa.pa_prefill_chunk(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.qsl,
+                            b.max_query_len, b.scale, seq_order=order, stream=stream)
+
+    def step():
+        reshape()
+        prefill()
+
+    for _ in range(warmup):
+        step()
+    ms = _timed(torch, step, steps)
+    return {"ms_per_step": ms, "kernel_ms": _events(torch, prefill, steps, stream),
+            "reshape_ms": _events(torch, reshape, steps, stream)}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,6 +213,8 @@ def main(argv=None) -> int:
     ap.add_argument("--unfused", action="store_true",
                     help="step = pa_reshape_and_cache + pa_decode (two launches) instead of the "
                          "fused pa_decode_step")
+    ap.add_argument("--secondary", default="chunked_prefill",
+                    help="comma-separated extra workloads reported beside the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-kernel-bytes", type=int, default=0,
@@ -137,82 +254,16 @@ def main(argv=None) -> int:
         print("bench.py: the headline workload is a decode batch", file=sys.stderr)
         return 2
     partition = cfg["partition"] if args.partition is None else args.partition
+    dev = torch.device("cuda:0")
 
     t_gen = time.perf_counter()
     b = make_config(args.workload)
     print(f"[bench] generated {args.workload} in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
           flush=True)
-    dt = torch.bfloat16 if b.dtype == "bf16" else torch.float16
-    dev = torch.device("cuda:0")
-    shape = (b.NB, b.BS, b.Hkv, b.D)
-    k_cache = torch.full(shape, -1, dtype=torch.int16, device=dev)
-    v_cache = torch.full(shape, -1, dtype=torch.int16, device=dev)
-    idx = torch.from_numpy(b.phys_ids).to(dev)
-    k_cache[idx] = torch.from_numpy(b.k_blocks.view(np.int16)).to(dev)
-    v_cache[idx] = torch.from_numpy(b.v_blocks.view(np.int16)).to(dev)
-    k_cache, v_cache = k_cache.view(dt), v_cache.view(dt)
-
-    def dev16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(dt)
-
-    q, key_new, value_new = dev16(b.q), dev16(b.key_new), dev16(b.value_new)
-    slot = torch.from_numpy(b.slot_mapping).to(dev)
-    tables = torch.from_numpy(b.block_tables).to(dev)
-    lens = torch.from_numpy(b.context_lens).to(dev)
-    out = torch.empty_like(q)
-    workspace = pa.decode_workspace(b.B, b.Hq, b.D, b.max_context_len, partition, dev)
-    stream = torch.cuda.current_stream(dev)
-    torch.cuda.synchronize()
-
-    # Longest-first visiting order of the sequences, computed on the host from
-    # the lengths the caller knows (the library's pa_decode_order).
-    order = torch.from_numpy(pa.pa_decode_order(b.context_lens)).to(dev)
-
-    def step():
-        if args.unfused:
-            pa.pa_reshape_and_cache(key_new, value_new, k_cache, v_cache, slot, stream=stream)
-            pa.pa_decode(out, q, k_cache, v_cache, tables, lens, b.scale, b.max_context_len,
-                         partition, workspace=workspace, seq_order=order, stream=stream)
-        else:
-            pa.pa_decode_step(out, q, key_new, value_new, slot, k_cache, v_cache, tables, lens,
-                              b.scale, b.max_context_len, partition, workspace=workspace,
-                              seq_order=order, stream=stream)
-
-    def decode_only():
-        step() if not args.unfused else pa.pa_decode(
-            out, q, k_cache, v_cache, tables, lens, b.scale, b.max_context_len, partition,
-            workspace=workspace, seq_order=order, stream=stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # Timed region: exactly `steps` steps back to back, nothing else on the stream.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # Kernel timing for the roofline: each pa_decode call (partition kernel +
-    # merge kernel) bracketed by HIP events recorded on the stream it runs on.
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    for i in range(args.steps):
-        events[i][0].record(stream)
-        decode_only()
-        events[i][1].record(stream)
-    torch.cuda.synchronize()
-    decode_ms = np.array([s.elapsed_time(e) for s, e in events])
-
-    ms_per_step = wall / args.steps * 1e3
+    r = run_decode(pa, torch, b, partition, args.steps, args.warmup, args.unfused, dev)
     kv = b.kv_bytes()
-    value = kv / (ms_per_step * 1e-3) / 1e9
-    dec_avg_s = float(decode_ms.mean()) * 1e-3
-    achieved = kv / dec_avg_s / 1e9
-    traffic = recorded_traffic(args.workload, partition)
-
+    value = kv / (r["ms_per_step"] * 1e-3) / 1e9
+    achieved = kv / (float(r["kernel_ms"].mean()) * 1e-3) / 1e9
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -220,7 +271,7 @@ def main(argv=None) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(r["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -230,18 +281,56 @@ def main(argv=None) -> int:
                    "num_kv_heads": b.Hkv, "head_dim": b.D, "block_size": b.BS,
                    "pool_blocks": b.NB, "context_lens": "uniform[%d,%d]" % tuple(cfg["lens"]),
                    "seed": cfg["seed"], "partition_size": partition,
+                   "step": "pa_reshape_and_cache + pa_decode" if args.unfused else
+                           "pa_decode_step (new-token store + decode, one launch)",
+                   "seq_order": "longest context first (pa_decode_order on the host)",
                    "kv_bytes_per_step": kv},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "seqs_per_s": round(b.B / (ms_per_step * 1e-3), 1),
-        "decode_us": {"mean": round(float(decode_ms.mean()) * 1e3, 2),
-                      "p10": round(float(np.percentile(decode_ms, 10)) * 1e3, 2),
-                      "p50": round(float(np.median(decode_ms)) * 1e3, 2),
-                      "p90": round(float(np.percentile(decode_ms, 90)) * 1e3, 2)},
-        "roofline": {"bound": "hbm", "kernel": "pa_decode (partition + merge kernels)",
+        "seqs_per_s": round(b.B / (r["ms_per_step"] * 1e-3), 1),
+        "decode_us": _stats_us(r["kernel_ms"]),
+        "roofline": {"bound": "hbm", "kernel": r["kernel_name"],
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic},
+                     "traffic": recorded_traffic(args.workload, partition)},
     }
+    secondary = {}
+    for name in [x for x in args.secondary.split(",") if x]:
+        c2 = CONFIGS[name]
+        t_gen = time.perf_counter()
+        b2 = make_config(name)
+        print(f"[bench] generated {name} in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
+              flush=True)
+        steps2 = max(5, args.steps // 10)
+        if c2["kind"] == "prefill":
+            r2 = run_prefill(pa, torch, b2, steps2, max(2, args.warmup // 4), dev)
+            flops = prefill_flops(b2)
+            tfl = flops / (float(r2["kernel_ms"].mean()) * 1e-3) / 1e12
+            secondary[name] = {
+                "step": "pa_reshape_and_cache (all new tokens) + pa_prefill_chunk",
+                "steps": steps2, "ms_per_step": round(r2["ms_per_step"], 5),
+                "prefill_us": _stats_us(r2["kernel_ms"]),
+                "reshape_and_cache_us": _stats_us(r2["reshape_ms"]),
+                "algorithmic_gflop": round(flops / 1e9, 2),
+                "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tfl, 2),
+                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}}
+        else:
+            p2 = c2["partition"]
+            r2 = run_decode(pa, torch, b2, p2, steps2, max(2, args.warmup // 4), False, dev)
+            kv2 = b2.kv_bytes()
+            ach2 = kv2 / (float(r2["kernel_ms"].mean()) * 1e-3) / 1e9
+            secondary[name] = {
+                "step": "pa_decode_step", "partition_size": p2, "steps": steps2,
+                "ms_per_step": round(r2["ms_per_step"], 5),
+                "effective_GBps": round(kv2 / (r2["ms_per_step"] * 1e-3) / 1e9, 2),
+                "unique_kv_bytes": b2.unique_kv_bytes(), "kv_bytes": kv2,
+                "decode_us": _stats_us(r2["kernel_ms"]),
+                "roofline": {"bound": "hbm", "kernel": r2["kernel_name"],
+                             "achieved": round(ach2, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": round(ach2 / HBM_PEAK_GBPS, 4), "traffic": None}}
+        del b2
+    if secondary:
+        result["secondary"] = secondary
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(b, args.cpu_budget)
