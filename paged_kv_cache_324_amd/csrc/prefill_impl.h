@@ -55,32 +55,57 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 constexpr int kPrefillD = 128;
-constexpr int kPrefillKeys = 64;                   // keys per KV tile
-constexpr int kPrefillKStride = kPrefillD * 2 + 16;  // LDS bytes per key row of the K tile
-constexpr int kPrefillVStride = kPrefillKeys * 2 + 8;  // LDS bytes per dim row of the V^T tile
+constexpr int kPrefillKeys = 64;        // keys per KV tile
+constexpr int kPrefillRow = kPrefillD * 2;  // bytes per key row in LDS (16 chunks of 16 B)
+constexpr int kPrefillTile = kPrefillKeys * kPrefillRow;
 constexpr float kPrefillEmptyMax = -1.0e30f;
+constexpr int kXcds = 8;  // workgroups are dispatched round-robin over the 8 XCDs of an MI355X
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Byte offset of 16-byte chunk `chunk` of row `row` in a tile: chunks are
+// XOR-swizzled by the row so that 16 consecutive rows read at one column hit
+// 16 different bank groups.
+__device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
+  return (uint32_t)row * kPrefillRow + (uint32_t)((chunk ^ (row & 15)) * 16);
+}
+
+// Four 16-bit elements, transposed across each group of 16 lanes (ds_read_b64_tr_b16):
+// lane i of a group receives element i % 4 of what group lane 4 j + i / 4 addressed, j = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* p) {
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
 
 template <int DT, int BS, int G>
 __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   constexpr int D = kPrefillD;
   constexpr int NK = kPrefillKeys;
   constexpr int QT = 128 / G;
-  constexpr int KSTR = kPrefillKStride;
-  constexpr int VSTR = kPrefillVStride;
-  __shared__ __attribute__((aligned(16))) unsigned char s_k[NK * KSTR];
-  __shared__ __attribute__((aligned(16))) unsigned char s_v[D * VSTR];
+  static_assert(BS % 16 == 0, "a wavefront stages 16 keys of one block");
+  // [buffer][K or V][64 key rows x 256 B]: double-buffered tiles filled straight
+  // from the cache by buffer loads into LDS.
+  __shared__ __attribute__((aligned(16))) unsigned char s_kv[2][2][kPrefillTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
 
-  // Heaviest tiles first: the last query tiles of a chunk see the most keys.
-  const int per_tile = a.num_seqs * a.num_kv_heads;
-  const int qt = a.q_tiles - 1 - (int)(blockIdx.x / per_tile);
-  const int rest = blockIdx.x % per_tile;
-  const int rank = rest / a.num_kv_heads;
-  const int kvh = rest - rank * a.num_kv_heads;
+  // XCD-aware order.  Workgroup b runs on XCD b % 8; each XCD takes every 8th
+  // (sequence, KV head) group and runs that group's query tiles back to back,
+  // so the group's K/V is fetched from HBM once and then served by that
+  // XCD's L2.  Groups go heaviest sequence first (seq_order), and within a
+  // group the last query tiles (which see the most keys) go first.
+  const int xcd = blockIdx.x % kXcds;
+  const int kx = blockIdx.x / kXcds;
+  const int gi = kx / a.q_tiles;
+  const int qt = a.q_tiles - 1 - (kx - gi * a.q_tiles);
+  const int group = gi * kXcds + xcd;
+  if (group >= a.num_seqs * a.num_kv_heads) return;
+  const int rank = group / a.num_kv_heads;
+  const int kvh = group - rank * a.num_kv_heads;
   const int seq = a.seq_order ? a.seq_order[rank] : rank;
   if (seq < 0 || seq >= a.num_seqs) return;
 
@@ -110,7 +135,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   u32x4 qf[D / 16];
   {
     const u32x4* qp = reinterpret_cast<const u32x4*>(
-        static_cast<const uint16_t*>(a.q) + ((int64_t)(s0 + (row_valid ? t : 0)) * a.num_heads + h) * D);
+        static_cast<const uint16_t*>(a.q) +
+        ((int64_t)(s0 + (row_valid ? t : 0)) * a.num_heads + h) * D);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const u32x4 v = qp[ks * 2 + half];
@@ -123,60 +149,68 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
   float m = kPrefillEmptyMax, lsum = 0.f;
 
+  // ---- staging: wavefront w moves keys kv0 + 16 w .. + 15 (one block) of K
+  // and of V with four 1 KB buffer loads each; lane l of load i brings key row
+  // 4 i + l / 16, chunk (l % 16) ^ row, so the tile lands already swizzled.
   const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks;
   const int32_t nb32 = a.num_blocks > INT32_MAX ? INT32_MAX : (int32_t)a.num_blocks;
-  const size_t row_bytes = (size_t)a.num_kv_heads * D * 2;
-  const unsigned char* kbase = static_cast<const unsigned char*>(a.k_cache) + (size_t)kvh * D * 2;
-  const unsigned char* vbase = static_cast<const unsigned char*>(a.v_cache) + (size_t)kvh * D * 2;
-  const int ld_key = tid >> 4;    // staging: key row tid/16 (+16 per round), 16-byte chunk tid%16
-  const int ld_chunk = tid & 15;
-
-  for (int kv0 = 0; kv0 < kv_end; kv0 += NK) {
-    // ---- stage the K tile (row-major) and the V tile (transposed) in LDS
-    u32x4 kr[4], vr[4];
+  const uint32_t row_bytes = (uint32_t)a.num_kv_heads * D * 2;
+  const uint64_t block_bytes = (uint64_t)BS * row_bytes;
+  const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)kvh * D * 2;
+  const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)kvh * D * 2;
+  const int nblk = (L + BS - 1) / BS;
+  const int srow = lane >> 4;  // row within a 1 KB load (4 rows of 256 B)
+  auto stage = [&](int kv0, int buf) {
+    const int key0 = kv0 + 16 * wave;
+    const int lb = key0 / BS;
+    const int32_t blk = bt[min(lb, nblk - 1)];
+    const int nvalid = min(16, L - key0);
+    const bool ok = nvalid > 0 && blk >= 0 && blk < nb32;
+    const uint64_t boff = ok ? (uint64_t)(uint32_t)blk * block_bytes +
+                                   (uint64_t)(key0 - lb * BS) * row_bytes
+                             : 0ull;
+    const uint32_t nrec = ok ? (uint32_t)(nvalid - 1) * row_bytes + D * 2 : 0u;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + boff, nrec);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + boff, nrec);
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int j = kv0 + it * 16 + ld_key;
-      kr[it] = u32x4{0u, 0u, 0u, 0u};
-      vr[it] = u32x4{0u, 0u, 0u, 0u};
-      if (j < L) {
-        const int32_t blk = bt[j / BS];
-        if (blk >= 0 && blk < nb32) {
-          const size_t off = ((size_t)(uint32_t)blk * BS + (j % BS)) * row_bytes + ld_chunk * 16;
-          kr[it] = *reinterpret_cast<const u32x4*>(kbase + off);
-          vr[it] = *reinterpret_cast<const u32x4*>(vbase + off);
-        }
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * i + srow;  // 0..15, also the tile row modulo 16
+      const uint32_t voff = (uint32_t)r * row_bytes + (uint32_t)(((lane & 15) ^ r) * 16);
+      unsigned char* kd = s_kv[buf][0] + (16 * wave + 4 * i) * kPrefillRow;
+      unsigned char* vd = s_kv[buf][1] + (16 * wave + 4 * i) * kPrefillRow;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)kd,
+                                               16, (int)voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)vd,
+                                               16, (int)voff, 0, 0, 0);
     }
-    __syncthreads();  // the previous tile's LDS reads are done
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int key = it * 16 + ld_key;
-      *reinterpret_cast<u32x4*>(s_k + key * KSTR + ld_chunk * 16) = kr[it];
-      const uint32_t w[4] = {vr[it].x, vr[it].y, vr[it].z, vr[it].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint16_t x = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
-        *reinterpret_cast<uint16_t*>(s_v + (ld_chunk * 8 + e) * VSTR + key * 2) = x;
-      }
-    }
-    __syncthreads();
-    if (kv0 >= wave_end) continue;  // nothing in this tile is visible to this wavefront
+  };
 
-    // ---- S^T = K Q^T for the tile's two 32-key halves
+  // Operand addressing inside a tile.
+  //   S^T = K Q^T, A operand: key row 32 sub + l % 32, dims 16 ks + 8 half .. + 7.
+  //   O^T = V^T P^T, A operand by transposed reads: 16-lane group q = l / 16
+  //   (half = q / 2, dim half dh = q % 2), position p = l % 16 addresses key row
+  //   16 kk + 4 half (+ 8 for the second read) + p / 4 at dims
+  //   32 dt + 16 dh + 4 (p % 4) .. + 3, so lane l receives those four keys of
+  //   dim 32 dt + l % 32.
+  const int p16 = lane & 15;
+  const int dh = (lane >> 4) & 1;
+
+  auto compute = [&](int kv0, int buf) {
+    const unsigned char* sk = s_kv[buf][0];
+    const unsigned char* sv = s_kv[buf][1];
+    // ---- S^T for the tile's two 32-key halves
     f32x16 s[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       s[sub] = f32x16{};
-      const unsigned char* kp = s_k + (sub * 32 + (lane & 31)) * KSTR + half * 16;
+      const int kr = sub * 32 + (lane & 31);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(kp + ks * 32);
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(sk + tile_off(kr, 2 * ks + half));
         s[sub] = mfma32x32x16<DT>(kf, qf[ks], s[sub]);
       }
     }
-
-    // ---- scale, mask, online softmax (this lane's query; partner lane l^32)
+    // ---- scale, mask, online softmax (this lane's query; partner lane l ^ 32)
     float mx = kPrefillEmptyMax;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -206,7 +240,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     lsum = fmaf(lsum, alpha, psum);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-
     // ---- O^T += V^T P^T over the tile's four 16-key steps
 #pragma unroll
     for (int kk = 0; kk < NK / 16; ++kk) {
@@ -214,14 +247,30 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
       const int jb = 8 * (kk & 1);
       const u32x4 pf = {pack2<DT>(ps[jb + 0], ps[jb + 1]), pack2<DT>(ps[jb + 2], ps[jb + 3]),
                         pack2<DT>(ps[jb + 4], ps[jb + 5]), pack2<DT>(ps[jb + 6], ps[jb + 7])};
+      const int r1 = 16 * kk + 4 * half + (p16 >> 2);
+      const int r2 = r1 + 8;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const unsigned char* vp = s_v + (dt * 32 + (lane & 31)) * VSTR + (16 * kk + 4 * half) * 2;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 16);
+        const int chunk = 4 * dt + 2 * dh + ((p16 & 3) >> 1);
+        const int sub8 = 8 * (p16 & 1);
+        const u32x2 lo = lds_read_tr16(sv + tile_off(r1, chunk) + sub8);
+        const u32x2 hi = lds_read_tr16(sv + tile_off(r2, chunk) + sub8);
         o[dt] = mfma32x32x16<DT>(u32x4{lo.x, lo.y, hi.x, hi.y}, pf, o[dt]);
       }
     }
+  };
+
+  // ---- pipeline: tile i+1 streams into the other buffer while tile i computes
+  const int ntiles = (kv_end + NK - 1) / NK;
+  if (ntiles > 0) stage(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int kv0 = it * NK;
+    if (it + 1 < ntiles) stage(kv0 + NK, (it + 1) & 1);
+    if (kv0 < wave_end) compute(kv0, it & 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
 
   // ---- normalise and store: lane holds dims 32 dt + 8 (j/4) + 4 half + (j%4)
@@ -245,7 +294,8 @@ hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t s) {
   PrefillArgs a = a0;
   constexpr int QT = 128 / G;
   a.q_tiles = (a.max_query_len + QT - 1) / QT;
-  const int64_t grid = (int64_t)a.q_tiles * a.num_seqs * a.num_kv_heads;
+  const int64_t groups = (int64_t)a.num_seqs * a.num_kv_heads;
+  const int64_t grid = (groups + kXcds - 1) / kXcds * kXcds * a.q_tiles;
   if (grid == 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL((prefill_kernel<DT, BS, G>), dim3((unsigned)grid), dim3(256), 0, s, a);
