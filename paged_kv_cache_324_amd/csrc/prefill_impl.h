@@ -59,15 +59,21 @@ constexpr int kPrefillKeys = 64;        // keys per KV tile
 constexpr int kPrefillRow = kPrefillD * 2;  // bytes per key row in LDS (16 chunks of 16 B)
 constexpr int kPrefillTile = kPrefillKeys * kPrefillRow;
 constexpr float kPrefillEmptyMax = -1.0e30f;
+constexpr float kLazyRescale = 8.0f;
 constexpr int kXcds = 8;  // workgroups are dispatched round-robin over the 8 XCDs of an MI355X
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-// Byte offset of 16-byte chunk `chunk` of row `row` in a tile: chunks are
-// XOR-swizzled by the row so that 16 consecutive rows read at one column hit
-// 16 different bank groups.
+// Swizzle of the 16-byte chunks of a tile row: chunk c of row r is stored at
+// position c ^ swz(r), with swz(r) the two 2-bit fields of r & 15 swapped.
+// Both read patterns then hit 16 distinct 16-byte bank groups: 16 consecutive
+// rows at one chunk (the K operand), and 4 consecutive rows (4 r0 .. 4 r0 + 3)
+// at 4 adjacent chunks (4 a .. 4 a + 3, the transposed V operand), since
+// (4 a + i) ^ ((j << 2) | k) = 4 (a ^ j) + (i ^ k).
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
 __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
-  return (uint32_t)row * kPrefillRow + (uint32_t)((chunk ^ (row & 15)) * 16);
+  return (uint32_t)row * kPrefillRow + (uint32_t)((chunk ^ swz(row)) * 16);
 }
 
 // Four 16-bit elements, transposed across each group of 16 lanes (ds_read_b64_tr_b16):
@@ -79,7 +85,8 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* p) {
 }
 
 template <int DT, int BS, int G>
-__global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_kernel(const PrefillArgs a) {
   constexpr int D = kPrefillD;
   constexpr int NK = kPrefillKeys;
   constexpr int QT = 128 / G;
@@ -151,7 +158,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
 
   // ---- staging: wavefront w moves keys kv0 + 16 w .. + 15 (one block) of K
   // and of V with four 1 KB buffer loads each; lane l of load i brings key row
-  // 4 i + l / 16, chunk (l % 16) ^ row, so the tile lands already swizzled.
+  // 4 i + l / 16, chunk (l % 16) ^ swz(row), so the tile lands already swizzled.
   const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks;
   const int32_t nb32 = a.num_blocks > INT32_MAX ? INT32_MAX : (int32_t)a.num_blocks;
   const uint32_t row_bytes = (uint32_t)a.num_kv_heads * D * 2;
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * i + srow;  // 0..15, also the tile row modulo 16
-      const uint32_t voff = (uint32_t)r * row_bytes + (uint32_t)(((lane & 15) ^ r) * 16);
+      const uint32_t voff = (uint32_t)r * row_bytes + (uint32_t)(((lane & 15) ^ swz(r)) * 16);
       unsigned char* kd = s_kv[buf][0] + (16 * wave + 4 * i) * kPrefillRow;
       unsigned char* vd = s_kv[buf][1] + (16 * wave + 4 * i) * kPrefillRow;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)kd,
@@ -195,6 +202,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   const int p16 = lane & 15;
   const int dh = (lane >> 4) & 1;
 
+  // Smallest causal limit over the wavefront's rows: tiles below it need no mask.
+  int wave_min_vis = vis;
+#pragma unroll
+  for (int o2 = 32; o2 >= 1; o2 >>= 1) wave_min_vis = min(wave_min_vis, __shfl_xor(wave_min_vis, o2));
+  wave_min_vis = __builtin_amdgcn_readfirstlane(wave_min_vis);
+
   auto compute = [&](int kv0, int buf) {
     const unsigned char* sk = s_kv[buf][0];
     const unsigned char* sv = s_kv[buf][1];
@@ -210,36 +223,49 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
         s[sub] = mfma32x32x16<DT>(kf, qf[ks], s[sub]);
       }
     }
-    // ---- scale, mask, online softmax (this lane's query; partner lane l ^ 32)
-    float mx = kPrefillEmptyMax;
+    // ---- mask, online softmax (this lane's query; partner lane l ^ 32).  Only
+    // tiles that cross some row's causal limit need the mask.  The scale is
+    // positive, so the maximum is taken over raw scores and folded into the
+    // exponent.  O and l are rescaled only when some row's maximum grows by
+    // more than kLazyRescale (log2 units); until then p <= 2^kLazyRescale,
+    // harmless in fp32 and in the 16-bit P.
+    if (kv0 + NK > wave_min_vis) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = kv0 + sub * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+          s[sub][j] = key < vis ? s[sub][j] : -__builtin_inff();
+        }
+      }
+    }
+    float mx = -__builtin_inff();
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = kv0 + sub * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-        const float v = key < vis ? s[sub][j] * a.scale_log2 : -__builtin_inff();
-        s[sub][j] = v;
-        mx = fmaxf(mx, v);
-      }
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[sub][j]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - m_new);
-    m = m_new;
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    if (__builtin_amdgcn_read_exec() & __builtin_amdgcn_ballot_w64(mx > m + kLazyRescale)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+    }
     float psum = 0.f;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float p = fast_exp2(s[sub][j] - m_new);
+        const float p = fast_exp2(fmaf(s[sub][j], a.scale_log2, -m));
         s[sub][j] = p;
         psum += p;
       }
     }
     psum += __shfl_xor(psum, 32);
-    lsum = fmaf(lsum, alpha, psum);
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+    lsum += psum;
     // ---- O^T += V^T P^T over the tile's four 16-key steps
 #pragma unroll
     for (int kk = 0; kk < NK / 16; ++kk) {
