@@ -1,5 +1,5 @@
 // bf16 instantiations of the paged-attention decode kernels.
-#include "decode_impl.h"
+#include "decode_mfma_impl.h"
 
 namespace pa {
 hipError_t launch_decode_bf16(const DecodeArgs& a, int head_dim, int block_size, int group,

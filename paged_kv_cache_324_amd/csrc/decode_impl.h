@@ -423,13 +423,27 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
   for (int e = 0; e < E; ++e) out[e] = to_u16<DT>(acc[e] * inv);
 }
 
+template <int DT, int BS, int G>
+__global__ void decode_mfma_kernel(const DecodeArgs a);
+
+// Matrix cores take the score/value products once a KV head serves 4 or more
+// query heads (head_dim 128); below that the fp32 vector path is faster.
+template <int D, int G>
+constexpr bool decode_uses_mfma() {
+  return D == 128 && G >= 4;
+}
+
 template <int DT, int D, int BS, int G>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   constexpr int PF = (G <= 2) ? PA_DECODE_PF : 4;
   constexpr int WPE = (G <= 4) ? PA_DECODE_WPE : 2;
   const unsigned grid = (unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_parts);
-  hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, PF, WPE, PA_DECODE_AUX>), dim3(grid),
-                     dim3(256), 0, s, a);
+  if constexpr (decode_uses_mfma<D, G>()) {
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, G>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, PF, WPE, PA_DECODE_AUX>), dim3(grid),
+                       dim3(256), 0, s, a);
+  }
   if (a.num_parts > 1) {
     hipLaunchKernelGGL((decode_merge_kernel<DT, D>), dim3((unsigned)(a.num_seqs * a.num_heads)),
                        dim3(64), 0, s, a);

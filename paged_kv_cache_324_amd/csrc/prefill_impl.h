@@ -33,26 +33,11 @@
 // 2); the probabilities are rounded to the input dtype for the PV product.
 #pragma once
 
+#include "mfma.h"
 #include "pa_device.h"
 #include "pa_kernels.h"
 
 namespace pa {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-template <int DT>
-__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
-  if constexpr (DT == DT_BF16) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  } else {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-}
 
 constexpr int kPrefillD = 128;
 constexpr int kPrefillKeys = 64;        // keys per KV tile
@@ -61,8 +46,6 @@ constexpr int kPrefillTile = kPrefillKeys * kPrefillRow;
 constexpr float kPrefillEmptyMax = -1.0e30f;
 constexpr float kLazyRescale = 8.0f;
 constexpr int kXcds = 8;  // workgroups are dispatched round-robin over the 8 XCDs of an MI355X
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 // Swizzle of the 16-byte chunks of a tile row: chunk c of row r is stored at
 // position c ^ swz(r), with swz(r) the two 2-bit fields of r & 15 swapped.
@@ -74,14 +57,6 @@ __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >>
 
 __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
   return (uint32_t)row * kPrefillRow + (uint32_t)((chunk ^ swz(row)) * 16);
-}
-
-// Four 16-bit elements, transposed across each group of 16 lanes (ds_read_b64_tr_b16):
-// lane i of a group receives element i % 4 of what group lane 4 j + i / 4 addressed, j = 0..3.
-__device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* p) {
-  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)(p));
-  return __builtin_bit_cast(u32x2, v);
 }
 
 template <int DT, int BS, int G>
@@ -185,10 +160,8 @@ void prefill_kernel(const PrefillArgs a) {
       const uint32_t voff = (uint32_t)r * row_bytes + (uint32_t)(((lane & 15) ^ swz(r)) * 16);
       unsigned char* kd = s_kv[buf][0] + (16 * wave + 4 * i) * kPrefillRow;
       unsigned char* vd = s_kv[buf][1] + (16 * wave + 4 * i) * kPrefillRow;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)kd,
-                                               16, (int)voff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)vd,
-                                               16, (int)voff, 0, 0, 0);
+      buffer_load16_lds(rk, kd, voff);
+      buffer_load16_lds(rv, vd, voff);
     }
   };
 
