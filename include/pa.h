@@ -101,6 +101,22 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int m
                                 int partition_size);
 
 /*
+ * A partition_size for pa_decode / pa_decode_step suited to the current
+ * device: 0 (no split) when the num_seqs * num_kv_heads (sequence, KV head)
+ * pairs already give every compute unit two workgroups; otherwise a multiple
+ * of block_size (at least 256) that cuts max_context_len into enough
+ * partitions for about eight workgroups per compute unit.  Every split gives
+ * the same attention up to rounding; this one trades the partitions'
+ * parallelism against the partial results they write (page "vLLM-Ascend ...",
+ * section 3.1: split the long context across cores, then reduce).  Host
+ * arithmetic plus a device-attribute query; returns PA_ERR_INVALID_ARG for
+ * non-positive counts or a negative length, PA_ERR_UNSUPPORTED for another
+ * block size.
+ */
+int pa_decode_partition_hint(int num_seqs, int num_kv_heads, int max_context_len,
+                             int block_size);
+
+/*
  * pa_decode: one query token per sequence attends over its paged context
  * (attention of page "Nano-vLLM-Ascend", section 2.2.1; paging of section
  * 2.1; float softmax of page "vLLM-Ascend ...", section 3.1, problem 2).
@@ -124,7 +140,8 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int m
  * partition_size: 0 = each (sequence, KV head) is processed by one workgroup;
  * otherwise a positive multiple of block_size: the context is split into
  * partitions of that many tokens processed in parallel and merged by a second
- * kernel using each partition's fp32 max and sum, which needs
+ * kernel using each partition's fp32 max and sum and its normalised output
+ * (rounded to the cache dtype, as the final output is), which needs
  * pa_decode_workspace_size(...) bytes of `workspace` (device memory, caller
  * owned, 16-byte aligned, no initialisation needed, reused only after the
  * call's kernels finish on `stream`).

@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     load_library,
     pa_decode,
     pa_decode_order,
+    pa_decode_partition_hint,
     pa_decode_step,
     pa_decode_workspace_size,
     pa_prefill_chunk,

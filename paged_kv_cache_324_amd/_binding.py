@@ -42,6 +42,8 @@ def _declare(lib):
     lib.pa_reshape_and_cache.restype = c_int
     lib.pa_reshape_and_cache.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_int, c_int, c_int,
                                          c_i64, c_int, c_vp]
+    lib.pa_decode_partition_hint.restype = c_int
+    lib.pa_decode_partition_hint.argtypes = [c_int, c_int, c_int, c_int]
     lib.pa_decode_workspace_size.restype = c_sz
     lib.pa_decode_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int]
     lib.pa_decode.restype = c_int
@@ -116,6 +118,16 @@ def pa_decode_workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_c
                              partition_size: int) -> int:
     return int(load_library().pa_decode_workspace_size(num_seqs, num_heads, head_dim,
                                                        max_context_len, partition_size))
+
+
+def pa_decode_partition_hint(num_seqs: int, num_kv_heads: int, max_context_len: int,
+                             block_size: int) -> int:
+    """A partition_size suited to the current device (0 = no split)."""
+    lib = load_library()
+    r = int(lib.pa_decode_partition_hint(num_seqs, num_kv_heads, max_context_len, block_size))
+    if r < 0:
+        raise PAError(r, lib.pa_last_error().decode())
+    return r
 
 
 def decode_workspace(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,

@@ -32,6 +32,8 @@
 // Sequences that fit one partition write `out` directly.
 #pragma once
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -323,7 +325,9 @@ void decode_partition_kernel(const DecodeArgs a) {
   }
   __syncthreads();
 
-  // Merge the wavefronts and write the partition (or final) result.
+  // Merge the wavefronts and write the partition (or final) result.  A
+  // partition's rows of the G heads are contiguous in part_out.
+  const int64_t prow = ((int64_t)seq * a.num_parts + part) * a.num_heads + h0;
   for (int idx = threadIdx.x; idx < G * D; idx += 256) {
     const int g = idx / D;
     const int d = idx - g * D;
@@ -338,17 +342,21 @@ void decode_partition_kernel(const DecodeArgs a) {
       o = fmaf(s_acc[w][g][d], f, o);
     }
     const float val = o / den;
-    const int h = h0 + g;
     if (nparts_seq == 1) {
-      static_cast<uint16_t*>(a.out)[((int64_t)seq * a.num_heads + h) * D + d] = to_u16<DT>(val);
+      static_cast<uint16_t*>(a.out)[((int64_t)seq * a.num_heads + h0 + g) * D + d] = to_u16<DT>(val);
     } else {
-      const int64_t pidx = ((int64_t)seq * a.num_heads + h) * a.num_parts + part;
-      a.part_out[pidx * D + d] = val;
-      if (d == 0) {
-        a.part_ml[pidx * 2] = M;
-        a.part_ml[pidx * 2 + 1] = den;
-      }
+      a.part_out[prow * D + idx] = to_u16<DT>(val);
     }
+  }
+  if (nparts_seq > 1 && (int)threadIdx.x < G) {
+    const int g = threadIdx.x;
+    float M = s_ml[0][g][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[w][g][0]);
+    float den = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) den = fmaf(s_ml[w][g][1], fast_exp2(s_ml[w][g][0] - M), den);
+    reinterpret_cast<float2*>(a.part_ml)[prow + g] = make_float2(M, den);
   }
 }
 
@@ -362,18 +370,30 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
   constexpr int E = D / 64;
   constexpr int PB = 8;
   typedef float floatE __attribute__((ext_vector_type(E)));
+  // A lane's E partial-output elements (cache dtype) as one raw word.
+  typedef typename std::conditional<E == 2, uint32_t, uint16_t>::type RawE;
+  auto widen = [](RawE r) -> floatE {
+    floatE f;
+    f[0] = lo_f32<DT>((uint32_t)r);
+    if constexpr (E == 2) f[1] = hi_f32<DT>((uint32_t)r);
+    return f;
+  };
   const int lane = threadIdx.x;
   const int h = blockIdx.x % a.num_heads;
   const int seq = blockIdx.x / a.num_heads;
   const int P = a.num_parts;
-  const int64_t base = ((int64_t)seq * a.num_heads + h) * P;
-  const float* po = a.part_out + base * D + lane * E;
-  floatE pv[PB];
+  // Partition p of this row is entry (seq * P + p) * num_heads + h.
+  const int64_t base = (int64_t)seq * P * a.num_heads + h;
+  const int64_t pstride = a.num_heads;
+  const RawE* po = reinterpret_cast<const RawE*>(a.part_out + base * D + lane * E);
+  const int64_t rstride = pstride * (D / E);  // RawE words between partitions
+  const float2* pml = reinterpret_cast<const float2*>(a.part_ml) + base;
+  RawE pv[PB];
 #pragma unroll
   for (int j = 0; j < PB; ++j)
-    pv[j] = j < P ? *reinterpret_cast<const floatE*>(po + (int64_t)j * D) : floatE{};
-  const float m_own = lane < P ? a.part_ml[(base + lane) * 2] : 0.f;
-  const float l_own = lane < P ? a.part_ml[(base + lane) * 2 + 1] : 0.f;
+    pv[j] = j < P ? po[j * rstride] : RawE(0);
+  const float2 ml_own = lane < P ? pml[lane * pstride] : make_float2(0.f, 0.f);
+  const float m_own = ml_own.x, l_own = ml_own.y;
 
   const int L = clamp_context(a, seq);
   const int n = L > 0 ? 1 + (L - 1) / a.part_tokens : 0;
@@ -382,7 +402,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
   float mp = -__builtin_inff(), lp = 0.f;
   if (lane < n) { mp = m_own; lp = l_own; }
   for (int p = lane + 64; p < n; p += 64) {  // only with more than 64 partitions
-    const float m2 = a.part_ml[(base + p) * 2], l2 = a.part_ml[(base + p) * 2 + 1];
+    const float2 ml2 = pml[p * pstride];
+    const float m2 = ml2.x, l2 = ml2.y;
     const float mn = fmaxf(mp, m2);           // finite: partition p holds a token
     lp = lp * fast_exp2(mp - mn) + l2 * fast_exp2(m2 - mn);
     mp = mn;
@@ -400,8 +421,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
     if (p0 > 0) {
 #pragma unroll
       for (int j = 0; j < PB; ++j)
-        pv[j] = p0 + j < n ? *reinterpret_cast<const floatE*>(po + (int64_t)(p0 + j) * D)
-                           : floatE{};
+        pv[j] = p0 + j < n ? po[(p0 + j) * rstride] : RawE(0);
     }
 #pragma unroll
     for (int j = 0; j < PB; ++j) {
@@ -411,9 +431,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
         if (n <= 64) {
           w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_own), p));
         } else {
-          w = a.part_ml[(base + p) * 2 + 1] * fast_exp2(a.part_ml[(base + p) * 2] - M);
+          const float2 mlp = pml[p * pstride];
+          w = mlp.y * fast_exp2(mlp.x - M);
         }
-        acc += w * pv[j];
+        acc += w * widen(pv[j]);
       }
     }
   }

@@ -1,6 +1,6 @@
 // Paged-attention decode on matrix cores, for 4..16 query heads per KV head.
 //
-// Same computation, inputs, grid order and partition scheme as
+// Same computation, inputs, outputs and partition scheme as
 // decode_partition_kernel (decode_impl.h): out[i][h] = softmax(scale q K^T) V
 // over the paged context (page "Nano-vLLM-Ascend", sections 2.1 and 2.2.1),
 // with fp32 softmax statistics (page "vLLM-Ascend ...", section 3.1, problem
@@ -11,7 +11,7 @@
 //
 // One workgroup (4 wavefronts) per (sequence, KV head, context partition).
 // The partition is cut into 32-key steps taken round-robin by the four
-// wavefronts; each wavefront streams its own steps with no barrier:
+// wavefronts:
 //   S^T = K Q^T   16x16x32 MFMA, two 16-key groups per step.  A = K rows
 //                 (16 keys x 32 dims), loaded straight from the cache into
 //                 registers: lane l takes key l % 16, dims 32 ks + 8 (l/16) ..,
@@ -23,13 +23,15 @@
 //                 O is lazy (only when a maximum grows by more than 2^8).
 //   O^T += V^T P^T  16x16x16 MFMA over each group's 16 keys.  V rows are
 //                 loaded into registers with K, stored to this wavefront's LDS
-//                 buffer just before use and read back transposed
-//                 (ds_read_b64_tr_b16); P^T is the softmax registers.
-// K and V of the wavefront's next step are in flight while a step computes;
-// block ids come from an LDS copy of the table, so no wait on the table ever
-// drains the prefetch.
-// At the end the four wavefronts' (m, l, O) are merged through LDS; a
-// partition either writes `out` or its normalised partial for the merge kernel.
+//                 buffer and read back transposed (ds_read_b64_tr_b16); P^T is
+//                 the softmax registers.
+// As soon as a step's K and V have left their registers (scores issued, V in
+// LDS) the same registers take the loads of the wavefront's next step, whose
+// block ids were loaded a step earlier still; so one step per wavefront is
+// always in flight.
+// At the end the four wavefronts' (m, l, O) are merged through LDS and the
+// partition writes `out` (unsplit context) or its normalised partial for the
+// merge kernel.
 #pragma once
 
 #include "decode_impl.h"
@@ -53,13 +55,18 @@ void decode_mfma_kernel(const DecodeArgs a) {
   constexpr int D = 128;
   static_assert(G >= 1 && G <= 16, "heads of a group fill the 16 MFMA columns");
   static_assert(BS % 16 == 0, "a 16-key group lies in one block");
-  __shared__ __attribute__((aligned(16))) unsigned char s_v[4][kMdStep];  // 32 KB, one per wave
-  __shared__ int32_t s_tbl[kTableCap];
+  // One V buffer per wavefront; at the end the same bytes hold that
+  // wavefront's fp32 O^T (16 heads x 128 dims) for the merge.
+  __shared__ __attribute__((aligned(16))) unsigned char s_v[4][kMdStep];  // 32 KB
+  __shared__ float s_ml[4 * 16 * 2];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;   // head (score / output column)
   const int quad = lane >> 4;  // which 4 keys / dims of a group this lane holds
 
+  // Partition-major order (every sequence's first partition before any
+  // second one); within a partition index, sequences in `seq_order` when one
+  // is given.
   const int per_part = a.num_seqs * a.num_kv_heads;
   const int part = blockIdx.x / per_part;
   const int rest = blockIdx.x - part * per_part;
@@ -68,9 +75,33 @@ void decode_mfma_kernel(const DecodeArgs a) {
   const int seq = a.seq_order ? a.seq_order[rank] : rank;
   if (seq < 0 || seq >= a.num_seqs) return;
   const int h0 = kvh * G;
+  const int t0 = part * a.part_tokens;  // a block boundary
+
+  // Prologue loads are issued together: the block ids of this wavefront's
+  // first two steps (speculatively, before the context length is known;
+  // reads are clamped to the sequence's table row), the queries and the
+  // length.
+  const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks;
+  const int lbA = t0 / BS;
+  // Lane l holds the block id of 16-key group (l & 1) of step s.
+  auto load_ids = [&](int s) -> int32_t {
+    return bt[min(lbA + (kMdStepKeys * s + 16 * (lane & 1)) / BS, a.max_blocks - 1)];
+  };
+  const int32_t ids_first = load_ids(wave);
+  int32_t ids_next = load_ids(wave + 4);
+
+  // Q^T fragments: column = head col, dims 32 ks + 8 quad .. + 7.  Columns
+  // past G repeat head h0 (finite scores in columns of their own, never
+  // written out), so no select has to wait for the loads.
+  u32x4 qf[4];
+  {
+    const u32x4* qp = reinterpret_cast<const u32x4*>(
+        static_cast<const uint16_t*>(a.q) + ((int64_t)seq * a.num_heads + h0 + (col < G ? col : 0)) * D);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = qp[4 * ks + quad];
+  }
 
   const int L = clamp_context(a, seq);
-  const int t0 = part * a.part_tokens;
   if (L == 0) {
     if (part == 0) {
       uint16_t* o = static_cast<uint16_t*>(a.out) + ((int64_t)seq * a.num_heads + h0) * D;
@@ -79,25 +110,14 @@ void decode_mfma_kernel(const DecodeArgs a) {
     return;
   }
   if (t0 >= L) return;
-  const int t1 = min(L, t0 + a.part_tokens);
+  const int t1 = (int)min((int64_t)L, (int64_t)t0 + a.part_tokens);
   const int nparts_seq = 1 + (L - 1) / a.part_tokens;
 
-  // Q^T fragments: column = head col (zero past G), dims 32 ks + 8 quad .. + 7.
-  u32x4 qf[4];
-  {
-    const u32x4* qp = reinterpret_cast<const u32x4*>(
-        static_cast<const uint16_t*>(a.q) + ((int64_t)seq * a.num_heads + h0 + (col < G ? col : 0)) * D);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const u32x4 v = qp[4 * ks + quad];
-      qf[ks] = col < G ? v : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-
-  // Fused step: the partition holding position L-1 takes that position's
-  // K/V from key_new/value_new (patched into the registers of the one step
-  // that holds it) and stores them bit for bit at the sequence's slot.
+  // Fused step: the partition holding position L-1 streams the cached tokens
+  // before it, takes that position's K/V from key_new/value_new in a one-key
+  // step of its own, and stores them bit for bit at the slot.
   const bool new_here = a.key_new != nullptr && t1 == L;
+  const int t1c = new_here ? L - 1 : t1;  // end of the cached range
   const int64_t new_row = ((int64_t)seq * a.num_kv_heads + kvh) * D;
   if (new_here && wave == 0 && lane < 32) {
     const int64_t slot = a.slot_mapping[seq];
@@ -109,7 +129,6 @@ void decode_mfma_kernel(const DecodeArgs a) {
     }
   }
 
-  const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks;
   const int32_t nb32 = a.num_blocks > INT32_MAX ? INT32_MAX : (int32_t)a.num_blocks;
   const uint32_t row_bytes = (uint32_t)a.num_kv_heads * D * 2;
   const uint64_t block_bytes = (uint64_t)BS * row_bytes;
@@ -121,16 +140,60 @@ void decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{};
   unsigned char* const sv = s_v[wave];
+  u32x4 kf[2][4], vr[2][4];
 
-  auto compute = [&](int kb, const u32x4 (&kf)[2][4], int kend) {
-    f32x4 sc[2];
+  // K fragments to registers (lane: key col, dims 32 ks + 8 quad ..) and the
+  // V rows this lane will store (row 4 i + quad of each group, chunk col ^
+  // swizzle), for step s; `ids` holds the step's block ids.  Past
+  // the cached range the resources have size 0: loads return zeros without
+  // touching memory.
+  auto issue = [&](int s, int32_t ids) {
+#pragma unroll
+    for (int gr = 0; gr < 2; ++gr) {
+      const int g0 = t0 + kMdStepKeys * s + 16 * gr;
+      const int lb = g0 / BS;
+      const int32_t blk = __builtin_amdgcn_readlane(ids, gr);
+      const int nv = min(16, t1c - g0);
+      const bool ok = nv > 0 && blk >= 0 && blk < nb32;
+      const uint64_t off = ok ? (uint64_t)(uint32_t)blk * block_bytes +
+                                    (uint64_t)(g0 - lb * BS) * row_bytes
+                              : 0ull;
+      const uint32_t nrec = ok ? (uint32_t)(nv - 1) * row_bytes + D * 2 : 0u;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + off, nrec);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + off, nrec);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kf[gr][ks] = buffer_load16<kCachePolicyNT>(
+            rk, (uint32_t)col * row_bytes + (uint32_t)(4 * ks + quad) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = 4 * i + quad;
+        vr[gr][i] = buffer_load16<kCachePolicyNT>(
+            rv, (uint32_t)rr * row_bytes + (uint32_t)((col ^ md_vswz(16 * gr + rr)) * 16));
+      }
+    }
+  };
+
+  auto store_v = [&]() {
+#pragma unroll
+    for (int gr = 0; gr < 2; ++gr)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4*>(sv + (16 * gr + 4 * i + quad) * kMdRow + col * 16) = vr[gr][i];
+  };
+
+  auto scores = [&](f32x4 (&sc)[2]) {
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr) {
       sc[gr] = f32x4{};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) sc[gr] = mfma16x16x32<DT>(kf[gr][ks], qf[ks], sc[gr]);
     }
-    if (kb + kMdStepKeys > kend) {  // last, partial step: keys past the range score -inf
+  };
+
+  // Softmax update and O^T += V^T P^T for the step at key kb, keys < kend.
+  auto accumulate = [&](f32x4 (&sc)[2], int kb, int kend) {
+    if (kb + kMdStepKeys > kend) {  // partial step: keys past the range score -inf
 #pragma unroll
       for (int gr = 0; gr < 2; ++gr)
 #pragma unroll
@@ -176,139 +239,97 @@ void decode_mfma_kernel(const DecodeArgs a) {
     }
   };
 
-  // The partition is walked in chunks of at most kTableCap blocks whose ids
-  // are staged in LDS; within a chunk wavefront w takes the 32-key steps
-  // w, w + 4, ... and keeps the next one in flight while it computes.
-  constexpr int kChunkTokens = kTableCap * BS;
-  for (int c0 = t0; c0 < t1; c0 += kChunkTokens) {
-    const int c1 = min(t1, c0 + kChunkTokens);
-    const int lb0 = c0 / BS;
-    const int nchunk_blk = (c1 - c0 + BS - 1) / BS;
-    __syncthreads();  // previous chunk's table reads are done
-    if ((int)threadIdx.x < nchunk_blk) {
-      const int32_t blk = bt[lb0 + threadIdx.x];
-      s_tbl[threadIdx.x] = (blk >= 0 && blk < nb32) ? blk : -1;
+  // Merge the four wavefronts' (m, l, O) and write the partition.
+  auto merge = [&]() {
+    float* s_o = reinterpret_cast<float*>(sv);  // this wavefront's [16][128]
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_o[col * D + 16 * dt + 4 * quad + i] = o[dt][i];
+    if (quad == 0) {
+      s_ml[(wave * 16 + col) * 2] = m;
+      s_ml[(wave * 16 + col) * 2 + 1] = lsum;
     }
-    __syncthreads();
-
-    // K fragments to registers (lane: key col, dims 32 ks + 8 quad ..) and the
-    // V rows this lane will store (row 4 i + quad of each group, chunk col ^
-    // swizzle), for the step at key kb.
-    auto issue = [&](int kb, u32x4 (&kf)[2][4], u32x4 (&vr)[2][4]) {
+    lds_barrier();
+    const float* s_all = reinterpret_cast<const float*>(&s_v[0][0]);  // [4][16][128]
+    // The partition's rows of the G heads are contiguous in part_out.
+    const int64_t prow = ((int64_t)seq * a.num_parts + part) * a.num_heads + h0;
+    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+      const int g = idx / D;
+      const int d = idx - g * D;
+      float M = s_ml[g * 2];
 #pragma unroll
-      for (int gr = 0; gr < 2; ++gr) {
-        const int g0 = kb + 16 * gr;
-        const int lb = g0 / BS;
-        const int32_t blk = __builtin_amdgcn_readfirstlane(s_tbl[min(lb - lb0, nchunk_blk - 1)]);
-        const int nv = min(16, c1 - g0);
-        const bool ok = nv > 0 && blk >= 0;
-        const uint64_t off = ok ? (uint64_t)(uint32_t)blk * block_bytes +
-                                      (uint64_t)(g0 - lb * BS) * row_bytes
-                                : 0ull;
-        const uint32_t nrec = ok ? (uint32_t)(nv - 1) * row_bytes + D * 2 : 0u;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + off, nrec);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + off, nrec);
+      for (int w = 1; w < 4; ++w) M = fmaxf(M, s_ml[(w * 16 + g) * 2]);
+      float den = 0.f, ov = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          kf[gr][ks] = buffer_load16<kCachePolicyNT>(
-              rk, (uint32_t)col * row_bytes + (uint32_t)(4 * ks + quad) * 16);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = 4 * i + quad;
-          vr[gr][i] = buffer_load16<kCachePolicyNT>(
-              rv, (uint32_t)rr * row_bytes + (uint32_t)((col ^ md_vswz(16 * gr + rr)) * 16));
-        }
+      for (int w = 0; w < 4; ++w) {
+        const float f = fast_exp2(s_ml[(w * 16 + g) * 2] - M);
+        den = fmaf(s_ml[(w * 16 + g) * 2 + 1], f, den);
+        ov = fmaf(s_all[(w * 16 + g) * D + d], f, ov);
       }
-    };
-    auto store_v = [&](const u32x4 (&vr)[2][4]) {
-#pragma unroll
-      for (int gr = 0; gr < 2; ++gr)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<u32x4*>(sv + (16 * gr + 4 * i + quad) * kMdRow + col * 16) = vr[gr][i];
-    };
-
-    // The look-ahead issue is unconditional: past the end its buffer
-    // resources have size 0, so the loads return zeros without touching
-    // memory, and every step sees the same count of loads in flight (a
-    // conditional issue would make the compiler wait for all of them).
-    auto patch_new = [&](int kb, u32x4 (&kf)[2][4], u32x4 (&vr)[2][4]) {
-      const int r = L - 1 - kb;  // 0..31: the new token's row in this step
-      const u32x4* kn = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.key_new) + new_row);
-      const u32x4* vn = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.value_new) + new_row);
-#pragma unroll
-      for (int gr = 0; gr < 2; ++gr) {
-        if ((r >> 4) != gr) continue;
-        const int rr = r & 15;
-        if (col == rr) {
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) kf[gr][ks] = kn[4 * ks + quad];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * i + quad == rr) vr[gr][i] = vn[col ^ md_vswz(16 * gr + rr)];
-      }
-    };
-    auto holds_new = [&](int kb) { return new_here && L - 1 >= kb && L - 1 < kb + kMdStepKeys; };
-
-    const int nsteps = (c1 - c0 + kMdStepKeys - 1) / kMdStepKeys;
-    u32x4 kfa[2][4], kfb[2][4], vra[2][4], vrb[2][4];
-    int s = wave;
-    if (s < nsteps) issue(c0 + kMdStepKeys * s, kfa, vra);
-    while (s < nsteps) {
-      issue(c0 + kMdStepKeys * (s + 4), kfb, vrb);
-      if (holds_new(c0 + kMdStepKeys * s)) patch_new(c0 + kMdStepKeys * s, kfa, vra);
-      store_v(vra);
-      compute(c0 + kMdStepKeys * s, kfa, c1);
-      s += 4;
-      if (s >= nsteps) break;
-      issue(c0 + kMdStepKeys * (s + 4), kfa, vra);
-      if (holds_new(c0 + kMdStepKeys * s)) patch_new(c0 + kMdStepKeys * s, kfb, vrb);
-      store_v(vrb);
-      compute(c0 + kMdStepKeys * s, kfb, c1);
-      s += 4;
-    }
-  }
-
-  // ---- merge the four wavefronts through LDS (reusing the V buffers)
-  __syncthreads();
-  float* s_o = reinterpret_cast<float*>(&s_v[0][0]);           // [4][16][128], 32 KB
-  float* s_ml = reinterpret_cast<float*>(&s_tbl[0]);           // [4][16][2]
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_o[(wave * 16 + col) * D + 16 * dt + 4 * quad + i] = o[dt][i];
-  if (quad == 0) {
-    s_ml[(wave * 16 + col) * 2] = m;
-    s_ml[(wave * 16 + col) * 2 + 1] = lsum;
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int g = idx / D;
-    const int d = idx - g * D;
-    float M = s_ml[g * 2];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, s_ml[(w * 16 + g) * 2]);
-    float den = 0.f, ov = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = fast_exp2(s_ml[(w * 16 + g) * 2] - M);
-      den = fmaf(s_ml[(w * 16 + g) * 2 + 1], f, den);
-      ov = fmaf(s_o[(w * 16 + g) * D + d], f, ov);
-    }
-    const float val = ov / den;
-    const int h = h0 + g;
-    if (nparts_seq == 1) {
-      static_cast<uint16_t*>(a.out)[((int64_t)seq * a.num_heads + h) * D + d] = to_u16<DT>(val);
-    } else {
-      const int64_t pidx = ((int64_t)seq * a.num_heads + h) * a.num_parts + part;
-      a.part_out[pidx * D + d] = val;
-      if (d == 0) {
-        a.part_ml[pidx * 2] = M;
-        a.part_ml[pidx * 2 + 1] = den;
+      const float val = ov / den;
+      if (nparts_seq == 1) {
+        static_cast<uint16_t*>(a.out)[((int64_t)seq * a.num_heads + h0 + g) * D + d] = to_u16<DT>(val);
+      } else {
+        a.part_out[prow * D + idx] = to_u16<DT>(val);
       }
     }
+    if (nparts_seq > 1 && (int)threadIdx.x < G) {
+      const int g = threadIdx.x;
+      float M = s_ml[g * 2];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) M = fmaxf(M, s_ml[(w * 16 + g) * 2]);
+      float den = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        den = fmaf(s_ml[(w * 16 + g) * 2 + 1], fast_exp2(s_ml[(w * 16 + g) * 2] - M), den);
+      reinterpret_cast<float2*>(a.part_ml)[prow + g] = make_float2(M, den);
+    }
+  };
+
+  const int nsteps = (t1c - t0 + kMdStepKeys - 1) / kMdStepKeys;
+  int s = wave;
+  if (s < nsteps) {
+    issue(s, ids_first);
+    for (; s < nsteps; s += 4) {
+      // The ids of step s + 8 go out before the K/V of step s + 4, so waiting
+      // for ids never waits for K/V; loads past the partition are harmless
+      // (clamped ids, size-0 resources), so every step sees the same loads in
+      // flight.
+      const int32_t ids_after = load_ids(s + 8);
+      store_v();
+      f32x4 sc[2];
+      scores(sc);
+      issue(s + 4, ids_next);
+      ids_next = ids_after;
+      accumulate(sc, t0 + kMdStepKeys * s, t1c);
+    }
   }
+  if (new_here && wave == (nsteps & 3)) {
+    // The new token, on the wavefront with the fewest steps: row 0 of a
+    // step whose buffer resources span just its rows of key_new / value_new,
+    // so every other row loads as zeros (and scores -inf).
+    const __amdgpu_buffer_rsrc_t rk =
+        make_rsrc(static_cast<const uint16_t*>(a.key_new) + new_row, D * 2);
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc(static_cast<const uint16_t*>(a.value_new) + new_row, D * 2);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      kf[0][ks] = buffer_load16<0>(rk, (uint32_t)col * row_bytes + (uint32_t)(4 * ks + quad) * 16);
+      kf[1][ks] = u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 4 * i + quad;
+      vr[0][i] = buffer_load16<0>(rv, (uint32_t)rr * row_bytes + (uint32_t)((col ^ md_vswz(rr)) * 16));
+      vr[1][i] = u32x4{0u, 0u, 0u, 0u};
+    }
+    store_v();
+    f32x4 sc[2];
+    scores(sc);
+    accumulate(sc, L - 1, L);
+  }
+  merge();
 }
 
 }  // namespace pa

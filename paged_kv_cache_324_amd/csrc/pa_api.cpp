@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <atomic>
 
 #include "pa.h"
 #include "pa_kernels.h"
@@ -37,6 +38,23 @@ int hip_status(hipError_t e, const char* what) {
   return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Compute units of the current device, queried once per device.
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev >= 0 && dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 bool supported_block_size(int b) { return b == 16 || b == 32 || b == 256; }
 bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
@@ -54,7 +72,7 @@ int64_t num_partitions(int max_context_len, int partition_size) {
 size_t workspace_bytes_for(int num_seqs, int num_heads, int head_dim, int64_t parts) {
   if (parts <= 1) return 0;
   const size_t rows = (size_t)num_seqs * (size_t)num_heads * (size_t)parts;
-  return align_up(rows * (size_t)head_dim * sizeof(float)) + align_up(rows * 2 * sizeof(float));
+  return align_up(rows * (size_t)head_dim * sizeof(uint16_t)) + align_up(rows * 2 * sizeof(float));
 }
 
 // Shared checks of the paged-cache description.
@@ -132,6 +150,22 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
                     "reshape_and_cache launch");
 }
 
+int pa_decode_partition_hint(int num_seqs, int num_kv_heads, int max_context_len,
+                             int block_size) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || max_context_len < 0)
+    return fail(PA_ERR_INVALID_ARG, "partition hint: non-positive count or negative length");
+  if (!supported_block_size(block_size))
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported", block_size);
+  ok();
+  const int64_t slots = 2LL * device_cus();  // decode workgroups resident at once
+  const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+  if (pairs >= slots || max_context_len == 0) return 0;
+  const int64_t parts = (4 * slots + pairs - 1) / pairs;  // partitions per longest context
+  int64_t p = std::max<int64_t>(256, (max_context_len + parts - 1) / parts);
+  p = (p + block_size - 1) / block_size * block_size;
+  return p >= max_context_len ? 0 : (int)p;
+}
+
 size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int max_context_len,
                                 int partition_size) {
   if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
@@ -194,9 +228,9 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   const size_t rows = (size_t)num_seqs * num_heads * (size_t)parts;
-  a.part_out = need ? static_cast<float*>(workspace) : nullptr;
+  a.part_out = need ? static_cast<uint16_t*>(workspace) : nullptr;
   a.part_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                             align_up(rows * head_dim * sizeof(float)))
+                                             align_up(rows * head_dim * sizeof(uint16_t)))
                    : nullptr;
   a.seq_order = seq_order;
   a.key_new = nt ? nt->key : nullptr;

@@ -24,8 +24,8 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* part_out;     // [num_seqs][num_heads][num_parts][head_dim], partition-normalised
-  float* part_ml;      // [num_seqs][num_heads][num_parts][2]: log2-domain max, sum
+  uint16_t* part_out;  // [num_seqs][num_parts][num_heads][head_dim], partition-normalised, cache dtype
+  float* part_ml;      // [num_seqs][num_parts][num_heads][2]: log2-domain max, sum
   const int32_t* seq_order;  // optional [num_seqs]: order in which sequences are visited
   // Fused decode step (all null otherwise): this step's token of sequence i is
   // at position context_lens[i] - 1; its K/V rows come from key_new/value_new

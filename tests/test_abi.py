@@ -85,7 +85,24 @@ def test_workspace_size(lib):
     assert lib.pa_decode_workspace_size(128, 16, 128, 512, 512) == 0
     n = lib.pa_decode_workspace_size(128, 16, 128, 2048, 512)
     rows = 128 * 16 * 4
-    assert n >= rows * 128 * 4 + rows * 2 * 4 and n % 256 == 0
+    assert n >= rows * 128 * 2 + rows * 2 * 4 and n % 256 == 0
+
+
+def test_partition_hint(lib):
+    """Split only when the (sequence, KV head) pairs leave compute units idle (256 CUs assumed
+    without a device, as on MI355X)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("hint values below assume 256 compute units and no device")
+    h = lib.pa_decode_partition_hint
+    assert h(128, 8, 2048, 16) == 0            # 1024 pairs: enough workgroups unsplit
+    assert h(64, 8, 8192, 32) == 0             # 512 pairs: two per compute unit
+    assert h(8, 8, 32768, 256) == 1024         # 64 pairs: 32 partitions of the longest context
+    assert h(8, 8, 30000, 16) == 944           # rounded up to a whole block
+    assert h(1, 1, 100, 16) == 0               # shorter than the minimum partition
+    assert h(4, 8, 0, 16) == 0
+    assert h(0, 8, 100, 16) == -1 and h(4, 8, -1, 16) == -1
+    assert h(4, 8, 100, 48) == -2
 
 
 def test_reshape_rejects_bad_arguments(lib):
