@@ -34,7 +34,11 @@ METRIC = "paged-attn decode effective KV GB/s (% of HBM peak) + sequences/s, 1 G
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16/fp16 matrix-core peak
 PROFILES = os.path.join(ROOT, "profiles")
+# Sources of the decode kernels; a counter summary holds their hash and counts
+# only while they are unchanged.
 KERNEL_SOURCES = ["paged_kv_cache_324_amd/csrc/decode_impl.h",
+                  "paged_kv_cache_324_amd/csrc/decode_mfma_impl.h",
+                  "paged_kv_cache_324_amd/csrc/mfma.h",
                   "paged_kv_cache_324_amd/csrc/pa_device.h"]
 
 
@@ -146,6 +150,13 @@ def _events(torch, fn, steps, stream):
     return np.array([s.elapsed_time(e) for s, e in ev])
 
 
+def resolve_partition(pa, cfg, b):
+    """The workload's split-K partition, or the library's choice for this device."""
+    if cfg["partition"] is not None:
+        return cfg["partition"]
+    return pa.pa_decode_partition_hint(b.B, b.Hkv, b.max_context_len, b.BS)
+
+
 def run_decode(pa, torch, b, partition, steps, warmup, unfused, dev):
     d = upload(torch, b, dev)
     out = torch.empty_like(d.q)
@@ -173,9 +184,12 @@ def run_decode(pa, torch, b, partition, steps, warmup, unfused, dev):
         step()
     ms = _timed(torch, step, steps)                       # the timed region
     kernel_ms = _events(torch, decode if unfused else step, steps, stream)
+    # The library runs the matrix-core kernel for 4+ query heads per KV head at
+    # head_dim 128, the vector kernel otherwise.
+    kern = "decode_mfma_kernel" if (b.G >= 4 and b.D == 128) else "decode_partition_kernel"
     name = ("pa_decode" if unfused else "pa_decode_step") + (
-        " (partition + merge kernels)" if partition and b.max_context_len > partition else
-        " (one decode_partition_kernel launch)")
+        f" ({kern} + merge kernel)" if partition and b.max_context_len > partition else
+        f" (one {kern} launch)")
     return {"ms_per_step": ms, "kernel_ms": kernel_ms, "kernel_name": name}
 
 
@@ -213,7 +227,9 @@ def main(argv=None) -> int:
     ap.add_argument("--unfused", action="store_true",
                     help="step = pa_reshape_and_cache + pa_decode (two launches) instead of the "
                          "fused pa_decode_step")
-    ap.add_argument("--secondary", default="chunked_prefill",
+    ap.add_argument("--secondary",
+                    default="llama2_70b_decode_bs16,llama2_70b_decode_bs32,long_splitk_decode,"
+                            "chunked_prefill",
                     help="comma-separated extra workloads reported beside the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -253,13 +269,13 @@ def main(argv=None) -> int:
     if cfg["kind"] != "decode":
         print("bench.py: the headline workload is a decode batch", file=sys.stderr)
         return 2
-    partition = cfg["partition"] if args.partition is None else args.partition
     dev = torch.device("cuda:0")
 
     t_gen = time.perf_counter()
     b = make_config(args.workload)
     print(f"[bench] generated {args.workload} in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
           flush=True)
+    partition = resolve_partition(pa, cfg, b) if args.partition is None else args.partition
     r = run_decode(pa, torch, b, partition, args.steps, args.warmup, args.unfused, dev)
     kv = b.kv_bytes()
     value = kv / (r["ms_per_step"] * 1e-3) / 1e9
@@ -315,7 +331,7 @@ def main(argv=None) -> int:
                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}}
         else:
-            p2 = c2["partition"]
+            p2 = resolve_partition(pa, c2, b2)
             r2 = run_decode(pa, torch, b2, p2, steps2, max(2, args.warmup // 4), False, dev)
             kv2 = b2.kv_bytes()
             ach2 = kv2 / (float(r2["kernel_ms"].mean()) * 1e-3) / 1e9
@@ -327,7 +343,8 @@ def main(argv=None) -> int:
                 "decode_us": _stats_us(r2["kernel_ms"]),
                 "roofline": {"bound": "hbm", "kernel": r2["kernel_name"],
                              "achieved": round(ach2, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                             "frac": round(ach2 / HBM_PEAK_GBPS, 4), "traffic": None}}
+                             "frac": round(ach2 / HBM_PEAK_GBPS, 4),
+                             "traffic": recorded_traffic(name, p2)}}
         del b2
     if secondary:
         result["secondary"] = secondary

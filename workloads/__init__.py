@@ -30,6 +30,9 @@ POISON_U16 = 0xFFFF  # a NaN in both fp16 and bf16: marks slots that hold no tok
 #     sharing for long contexts (same page, section 4),
 #   * 256-token blocks (same page, section 2.2 tuning table),
 #   * chunked prefill (page "vllm-ascend architecture", section 1.1 / 3.1).
+# partition: tokens per split-K partition of a decode (0 = unsplit); None where
+# the workload fixes none: the caller then asks the library for the device's
+# choice (pa_decode_partition_hint).
 CONFIGS = {
     "tiny_decode": dict(
         kind="decode", B=4, Hq=8, Hkv=8, D=64, BS=16, NB=128, lens=(1, 256),
@@ -39,10 +42,10 @@ CONFIGS = {
         dtype="bf16", scale=1.0 / math.sqrt(128), share=0.0, partition=0, seed=324_002),
     "llama2_70b_decode_bs16": dict(
         kind="decode", B=64, Hq=64, Hkv=8, D=128, BS=16, NB=None, lens=(4096, 8192),
-        dtype="bf16", scale=1.0 / math.sqrt(128), share=0.10, partition=512, seed=324_003),
+        dtype="bf16", scale=1.0 / math.sqrt(128), share=0.10, partition=None, seed=324_003),
     "llama2_70b_decode_bs32": dict(
         kind="decode", B=64, Hq=64, Hkv=8, D=128, BS=32, NB=None, lens=(4096, 8192),
-        dtype="bf16", scale=1.0 / math.sqrt(128), share=0.10, partition=512, seed=324_003),
+        dtype="bf16", scale=1.0 / math.sqrt(128), share=0.10, partition=None, seed=324_003),
     "long_splitk_decode": dict(
         kind="decode", B=8, Hq=32, Hkv=8, D=128, BS=256, NB=2048, lens=(16384, 32768),
         dtype="bf16", scale=1.0 / math.sqrt(128), share=0.0, partition=512, seed=324_004),
