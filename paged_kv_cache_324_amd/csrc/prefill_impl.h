@@ -47,6 +47,38 @@ constexpr float kPrefillEmptyMax = -1.0e30f;
 constexpr float kLazyRescale = 8.0f;
 constexpr int kXcds = 8;  // workgroups are dispatched round-robin over the 8 XCDs of an MI355X
 
+// A raw buffer resource as its four descriptor words (base, stride 0,
+// num_records = bytes, the same flags as make_rsrc), wave-uniform.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu),
+               (uint32_t)__builtin_amdgcn_readfirstlane(bytes), (uint32_t)kBufferWord3};
+}
+
+// LDS byte offset of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 with
+// the lds bit): lane l fills LDS bytes [lds_base + 16 l, + 16); lanes past the
+// buffer's size write zeros.  Issued as assembly: the compiler cannot tell
+// which LDS bytes such a copy writes, so for the builtin it waits for the copy
+// before every later LDS read, which would serialise a prefetch with the
+// compute it is meant to overlap.  The caller waits (s_waitcnt vmcnt) before
+// reading the destination; the compiler's own waits stay correct because the
+// counter retires in order.
+__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t lds_base, uint32_t voffset) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voffset), "s"(rsrc)
+      : "memory", "m0");
+}
+
 // Swizzle of the 16-byte chunks of a tile row: chunk c of row r is stored at
 // position c ^ swz(r), with swz(r) the two 2-bit fields of r & 15 swapped.
 // Both read patterns then hit 16 distinct 16-byte bank groups: 16 consecutive
@@ -140,28 +172,32 @@ void prefill_kernel(const PrefillArgs a) {
   const uint64_t block_bytes = (uint64_t)BS * row_bytes;
   const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)kvh * D * 2;
   const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)kvh * D * 2;
-  const int nblk = (L + BS - 1) / BS;
+  const int nblk_last = max(0, (L + BS - 1) / BS - 1);
   const int srow = lane >> 4;  // row within a 1 KB load (4 rows of 256 B)
-  auto stage = [&](int kv0, int buf) {
+  // Block ids, lane-parallel: for window w, lane j holds the id of the block
+  // this wavefront stages in tile 64 w + j (reads clamped to the context).
+  auto load_ids = [&](int w) -> int32_t {
+    const int key0 = (64 * w + lane) * NK + 16 * wave;
+    return bt[min(key0 / BS, nblk_last)];
+  };
+  auto stage = [&](int kv0, int buf, int32_t ids) {
     const int key0 = kv0 + 16 * wave;
     const int lb = key0 / BS;
-    const int32_t blk = bt[min(lb, nblk - 1)];
+    const int32_t blk = __builtin_amdgcn_readlane(ids, (kv0 / NK) & 63);
     const int nvalid = min(16, L - key0);
     const bool ok = nvalid > 0 && blk >= 0 && blk < nb32;
     const uint64_t boff = ok ? (uint64_t)(uint32_t)blk * block_bytes +
                                    (uint64_t)(key0 - lb * BS) * row_bytes
                              : 0ull;
     const uint32_t nrec = ok ? (uint32_t)(nvalid - 1) * row_bytes + D * 2 : 0u;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + boff, nrec);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + boff, nrec);
+    const u32x4 rk = rsrc_words(kbase + boff, nrec);
+    const u32x4 rv = rsrc_words(vbase + boff, nrec);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * i + srow;  // 0..15, also the tile row modulo 16
       const uint32_t voff = (uint32_t)r * row_bytes + (uint32_t)(((lane & 15) ^ swz(r)) * 16);
-      unsigned char* kd = s_kv[buf][0] + (16 * wave + 4 * i) * kPrefillRow;
-      unsigned char* vd = s_kv[buf][1] + (16 * wave + 4 * i) * kPrefillRow;
-      buffer_load16_lds(rk, kd, voff);
-      buffer_load16_lds(rv, vd, voff);
+      lds_dma16(rk, lds_offset(s_kv[buf][0] + (16 * wave + 4 * i) * kPrefillRow), voff);
+      lds_dma16(rv, lds_offset(s_kv[buf][1] + (16 * wave + 4 * i) * kPrefillRow), voff);
     }
   };
 
@@ -185,7 +221,11 @@ void prefill_kernel(const PrefillArgs a) {
     const unsigned char* sk = s_kv[buf][0];
     const unsigned char* sv = s_kv[buf][1];
     // ---- S^T for the tile's two 32-key halves
+    // Matrix phases run at raised wave priority: of the two wavefronts sharing
+    // a SIMD, the one with MFMAs ready issues first and the other's softmax
+    // (vector ALU) fills in behind it.
     f32x16 s[2];
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       s[sub] = f32x16{};
@@ -196,6 +236,7 @@ void prefill_kernel(const PrefillArgs a) {
         s[sub] = mfma32x32x16<DT>(kf, qf[ks], s[sub]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // ---- mask, online softmax (this lane's query; partner lane l ^ 32).  Only
     // tiles that cross some row's causal limit need the mask.  The scale is
     // positive, so the maximum is taken over raw scores and folded into the
@@ -239,6 +280,7 @@ void prefill_kernel(const PrefillArgs a) {
     }
     psum += __shfl_xor(psum, 32);
     lsum += psum;
+    __builtin_amdgcn_s_setprio(1);
     // ---- O^T += V^T P^T over the tile's four 16-key steps
 #pragma unroll
     for (int kk = 0; kk < NK / 16; ++kk) {
@@ -257,16 +299,30 @@ void prefill_kernel(const PrefillArgs a) {
         o[dt] = mfma32x32x16<DT>(u32x4{lo.x, lo.y, hi.x, hi.y}, pf, o[dt]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
-  // ---- pipeline: tile i+1 streams into the other buffer while tile i computes
+  // ---- pipeline: tile i+1 streams into the other buffer while tile i
+  // computes; the copies are waited for only at the end of the iteration.
+  // Block ids of the next window of 64 tiles are loaded a window ahead.
   const int ntiles = (kv_end + NK - 1) / NK;
-  if (ntiles > 0) stage(0, 0);
+  int32_t ids_cur = 0, ids_nxt = 0;
+  if (ntiles > 0) {
+    ids_cur = load_ids(0);
+    ids_nxt = load_ids(1);
+    stage(0, 0, ids_cur);
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int kv0 = it * NK;
-    if (it + 1 < ntiles) stage(kv0 + NK, (it + 1) & 1);
+    if (it + 1 < ntiles) {
+      if (((it + 1) & 63) == 0) {
+        ids_cur = ids_nxt;
+        ids_nxt = load_ids(((it + 1) >> 6) + 1);
+      }
+      stage(kv0 + NK, (it + 1) & 1, ids_cur);
+    }
     if (kv0 < wave_end) compute(kv0, it & 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
