@@ -250,7 +250,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
       s_ml[(wave * 16 + col) * 2] = m;
       s_ml[(wave * 16 + col) * 2 + 1] = lsum;
     }
-    lds_barrier();
+    __syncthreads();
     const float* s_all = reinterpret_cast<const float*>(&s_v[0][0]);  // [4][16][128]
     // The partition's rows of the G heads are contiguous in part_out.
     const int64_t prow = ((int64_t)seq * a.num_parts + part) * a.num_heads + h0;

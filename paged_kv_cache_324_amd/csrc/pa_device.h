@@ -105,13 +105,4 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Workgroup barrier ordering LDS only.  __syncthreads() also orders global
-// memory, which makes every wavefront wait for all of its outstanding vector
-// loads and stores first, including prefetches meant to stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 }  // namespace pa
