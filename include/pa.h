@@ -58,7 +58,8 @@ typedef enum pa_status {
   PA_ERR_INVALID_ARG = -1,  /* null pointer, negative size, inconsistent shape */
   PA_ERR_UNSUPPORTED = -2,  /* head_dim / block_size / group / dtype not built  */
   PA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required      */
-  PA_ERR_HIP = -4           /* a HIP launch reported an error                   */
+  PA_ERR_HIP = -4,          /* a HIP launch reported an error                   */
+  PA_ERR_NO_BLOCKS = -5     /* block manager: too few free blocks (pa_blocks.h)  */
 } pa_status;
 
 typedef enum pa_dtype { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;

@@ -5,11 +5,13 @@ library's C entry points and only marshal torch device tensors into them.
 """
 from ._binding import (  # noqa: F401
     LIB_PATH,
+    BlockManager,
     PA_BF16,
     PA_F16,
     PAError,
     decode_workspace,
     load_library,
+    pa_copy_blocks,
     pa_decode,
     pa_decode_order,
     pa_decode_partition_hint,

@@ -12,6 +12,8 @@ import ctypes
 import os
 import threading
 
+import numpy as np
+
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +61,33 @@ def _declare(lib):
     lib.pa_prefill_chunk.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64,
                                      c_int, c_int, c_int, c_int, c_i64, c_int, c_int, c_f, c_int,
                                      c_vp]
+    c_pp = ctypes.POINTER(c_vp)
+    lib.pa_bm_create.restype = c_int
+    lib.pa_bm_create.argtypes = [c_i64, c_int, c_pp]
+    lib.pa_bm_destroy.restype = None
+    lib.pa_bm_destroy.argtypes = [c_vp]
+    lib.pa_bm_add.restype = c_int
+    lib.pa_bm_add.argtypes = [c_vp, c_i64, c_i64, c_vp]
+    lib.pa_bm_fork.restype = c_int
+    lib.pa_bm_fork.argtypes = [c_vp, c_i64, c_i64, c_i64]
+    lib.pa_bm_append.restype = c_int
+    lib.pa_bm_append.argtypes = [c_vp, c_i64, c_i64, c_vp]
+    lib.pa_bm_free.restype = c_int
+    lib.pa_bm_free.argtypes = [c_vp, c_i64]
+    lib.pa_bm_tables.restype = c_int
+    lib.pa_bm_tables.argtypes = [c_vp, c_vp, c_int, c_int, c_vp, c_vp]
+    lib.pa_bm_take_copies.restype = c_i64
+    lib.pa_bm_take_copies.argtypes = [c_vp, c_vp, c_vp, c_i64]
+    for name in ("pa_bm_num_free", "pa_bm_num_seqs"):
+        getattr(lib, name).restype = c_i64
+        getattr(lib, name).argtypes = [c_vp]
+    lib.pa_bm_num_tokens.restype = c_i64
+    lib.pa_bm_num_tokens.argtypes = [c_vp, c_i64]
+    lib.pa_bm_ref_count.restype = c_int
+    lib.pa_bm_ref_count.argtypes = [c_vp, c_i64]
+    lib.pa_copy_blocks.restype = c_int
+    lib.pa_copy_blocks.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_int, c_int, c_int, c_i64, c_int,
+                                   c_vp]
     return lib
 
 
@@ -249,3 +278,90 @@ def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, context_lens, query
                                 B, T, Hq, Hkv, D, BS, NB, block_tables.shape[1], int(max_query_len),
                                 float(scale), dt, _stream(q, stream)))
     return out
+
+
+class BlockManager:
+    """Host block manager of the library (``pa_bm_*``): physical blocks with
+    reference counts, per-sequence block tables, prefix sharing by ``fork`` and
+    copy on write.  Slot mappings, tables and copy pairs are host numpy arrays;
+    upload them for the device calls."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._lib = load_library()
+        h = ctypes.c_void_p()
+        _check(self._lib.pa_bm_create(num_blocks, block_size, ctypes.byref(h)))
+        self._h = h
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            self._lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def add(self, seq: int, num_tokens: int) -> np.ndarray:
+        slots = np.empty(max(num_tokens, 0), dtype=np.int64)
+        _check(self._lib.pa_bm_add(self._h, seq, num_tokens,
+                                   slots.ctypes.data if num_tokens > 0 else None))
+        return slots
+
+    def fork(self, parent: int, child: int, num_tokens: int) -> None:
+        _check(self._lib.pa_bm_fork(self._h, parent, child, num_tokens))
+
+    def append(self, seq: int, n: int = 1) -> np.ndarray:
+        slots = np.empty(max(n, 0), dtype=np.int64)
+        _check(self._lib.pa_bm_append(self._h, seq, n, slots.ctypes.data if n > 0 else None))
+        return slots
+
+    def free(self, seq: int) -> None:
+        _check(self._lib.pa_bm_free(self._h, seq))
+
+    def tables(self, seqs, max_blocks_per_seq: int):
+        """``(block_tables int32 [B][max_blocks], context_lens int32 [B])``."""
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        bt = np.empty((ids.shape[0], max_blocks_per_seq), dtype=np.int32)
+        lens = np.empty(ids.shape[0], dtype=np.int32)
+        _check(self._lib.pa_bm_tables(self._h, ids.ctypes.data, ids.shape[0], max_blocks_per_seq,
+                                      bt.ctypes.data, lens.ctypes.data))
+        return bt, lens
+
+    def take_copies(self, capacity: int = 1 << 16):
+        """Queued copy-on-write pairs ``(src, dst)`` as int64 arrays (and clears them)."""
+        src = np.empty(capacity, dtype=np.int64)
+        dst = np.empty(capacity, dtype=np.int64)
+        n = int(self._lib.pa_bm_take_copies(self._h, src.ctypes.data, dst.ctypes.data, capacity))
+        if n < 0:
+            _check(n)
+        return src[:n].copy(), dst[:n].copy()
+
+    @property
+    def num_free(self) -> int:
+        return int(self._lib.pa_bm_num_free(self._h))
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self._lib.pa_bm_num_seqs(self._h))
+
+    def num_tokens(self, seq: int) -> int:
+        return int(self._lib.pa_bm_num_tokens(self._h, seq))
+
+    def ref_count(self, block: int) -> int:
+        return int(self._lib.pa_bm_ref_count(self._h, block))
+
+
+def pa_copy_blocks(k_cache, v_cache, src, dst, stream=None) -> None:
+    """Copy whole blocks ``src[i] -> dst[i]`` (int64 device tensors) in both caches
+    ``[NB][BS][Hkv][D]``: the copy-on-write step of :class:`BlockManager`."""
+    lib = load_library()
+    NB, BS, Hkv, D = k_cache.shape
+    if v_cache.shape != k_cache.shape or src.shape != dst.shape or src.dim() != 1:
+        raise ValueError("copy_blocks: inconsistent shapes")
+    dt = _dtype_code(k_cache)
+    _dev(k_cache, "k_cache"); _dev(v_cache, "v_cache", k_cache.dtype)
+    n = src.shape[0]
+    sp = _dev(src, "src", torch.int64) if n else None
+    dp = _dev(dst, "dst", torch.int64) if n else None
+    _check(lib.pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), sp, dp, n, Hkv, D, BS, NB, dt,
+                              _stream(k_cache, stream)))

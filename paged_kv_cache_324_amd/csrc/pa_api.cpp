@@ -14,11 +14,13 @@
 #include <atomic>
 
 #include "pa.h"
+#include "pa_blocks.h"
+#include "pa_internal.h"
 #include "pa_kernels.h"
 
-namespace {
+namespace pa {
 
-thread_local char g_last_error[512] = "";
+static thread_local char g_last_error[512] = "";
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -32,6 +34,13 @@ int ok() {
   g_last_error[0] = '\0';
   return PA_OK;
 }
+
+}  // namespace pa
+
+namespace {
+
+using pa::fail;
+using pa::ok;
 
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
@@ -114,11 +123,36 @@ const char* pa_status_string(int status) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: configuration not built";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: HIP runtime error";
+    case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: too few free blocks";
     default: return "unknown pa_status";
   }
 }
 
-const char* pa_last_error(void) { return g_last_error; }
+const char* pa_last_error(void) { return pa::g_last_error; }
+
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* src, const int64_t* dst,
+                   int64_t num_copies, int num_kv_heads, int head_dim, int block_size,
+                   int64_t num_blocks, int dtype, void* stream) {
+  if (num_copies < 0) return fail(PA_ERR_INVALID_ARG, "num_copies %lld < 0", (long long)num_copies);
+  if (!supported_head_dim(head_dim)) return fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported", head_dim);
+  if (!supported_block_size(block_size))
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported", block_size);
+  if (!supported_dtype(dtype)) return fail(PA_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+  if (num_kv_heads <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "num_kv_heads %d / num_blocks %lld must be positive", num_kv_heads,
+                (long long)num_blocks);
+  if (num_copies == 0) return ok();
+  if (!k_cache || !v_cache || !src || !dst) return fail(PA_ERR_INVALID_ARG, "NULL pointer");
+  pa::CopyBlocksArgs a;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.src = src;
+  a.dst = dst;
+  a.num_copies = num_copies;
+  a.num_blocks = num_blocks;
+  a.block_chunks = (int64_t)block_size * num_kv_heads * head_dim * 2 / 16;
+  return hip_status(pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)), "copy_blocks launch");
+}
 
 int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                          const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,

@@ -17,6 +17,16 @@ struct ReshapeArgs {
   int row_chunks;      // 16-byte chunks in one token's num_kv_heads * head_dim row
 };
 
+struct CopyBlocksArgs {
+  void* k_cache;
+  void* v_cache;
+  const int64_t* src;    // [num_copies] source blocks
+  const int64_t* dst;    // [num_copies] destination blocks
+  int64_t num_copies;
+  int64_t num_blocks;
+  int64_t block_chunks;  // 16-byte chunks in one block of one cache
+};
+
 struct DecodeArgs {
   void* out;
   const void* q;
@@ -68,6 +78,7 @@ struct PrefillArgs {
 };
 
 hipError_t launch_reshape_and_cache(const ReshapeArgs& a, hipStream_t s);
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 
 // dtype DT_F16 / DT_BF16; head_dim 64/128; block_size 16/32/256; group 1/2/4/8.
 hipError_t launch_decode_f16(const DecodeArgs& a, int head_dim, int block_size, int group,
