@@ -18,6 +18,14 @@ Pinned functions (each pin lives in ``tests/test_oracle.py``):
 * ``reshape_and_cache`` -- round trip through independently computed slots,
   padding slots skipped, other slots untouched.
 
+* ``int8_kv`` (INT8 KV cache) -- quantiser closed forms (the row maximum maps to
+  +-127, zero rows, half-way ties to even, error at most half a step), a
+  float64 re-derivation of each code from its exact rational, and decode on the
+  dequantised cache equal to the 16-bit oracle on those values.
+* ``block_manager`` (the block manager model, imported as
+  ``oracle.block_manager``) -- the 63-block example and a content simulation
+  with planted mistakes (``tests/test_block_manager.py``).
+
 Parity unpinned: the grouping convention of query heads onto KV heads beyond
 what torch's ``enable_gqa`` fixes (the pages never mention grouped-query
 attention; contiguous groups are the reading taken).
@@ -42,3 +50,4 @@ from .paged_attention import (  # noqa: F401
     waste_fraction,
 )
 from . import brute_force  # noqa: F401
+from . import int8_kv  # noqa: F401
