@@ -179,6 +179,42 @@ int pa_decode_step(void* out, const void* q, const void* key, const void* value,
                    size_t workspace_bytes, int dtype, void* stream);
 
 /*
+ * INT8 KV cache.  KV-cache compression by INT8 quantisation is the next
+ * optimisation the pages list (page "Nano-vLLM-Ascend", section 4.3) and the
+ * one that raises throughput if the attention scores keep their precision
+ * (page "vLLM-Ascend ...", section 5).  Scheme (symmetric, per token and KV
+ * head, IEEE float32): scale = max_d |x_d| / 127, code_d = rint(x_d / scale)
+ * (ties to even; an all-zero row has scale 0 and codes 0); the value used is
+ * code_d * scale.
+ *
+ *   k_codes, v_codes   : int8 [num_blocks][block_size][num_kv_heads][head_dim]
+ *   k_scales, v_scales : float32 [num_blocks][num_kv_heads][block_size]
+ *
+ * pa_reshape_and_cache_int8: quantise key/value [num_tokens][num_kv_heads]
+ * [head_dim] (16-bit, dtype) into the slots of slot_mapping, as
+ * pa_reshape_and_cache (negative or out-of-pool slots are skipped).
+ * Supported: head_dim in {64, 128}, block_size in {16, 32, 256}.
+ */
+int pa_reshape_and_cache_int8(const void* key, const void* value, void* k_codes, void* v_codes,
+                              float* k_scales, float* v_scales, const int64_t* slot_mapping,
+                              int64_t num_tokens, int num_kv_heads, int head_dim, int block_size,
+                              int64_t num_blocks, int dtype, void* stream);
+
+/*
+ * pa_decode_int8: pa_decode over an INT8 cache: out[i][h] = softmax(scale *
+ * q[i][h] . K'_j) . V'_j with K'_j, V'_j the dequantised rows; q and out are
+ * 16-bit (dtype).  Arguments, partitions, workspace (pa_decode_workspace_size)
+ * and seq_order as for pa_decode.  Supported: head_dim 128; num_heads /
+ * num_kv_heads in {1, 2, 4, 8}; block_size in {16, 32, 256}.
+ */
+int pa_decode_int8(void* out, const void* q, const void* k_codes, const void* v_codes,
+                   const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                   const int32_t* context_lens, const int32_t* seq_order, int num_seqs,
+                   int num_heads, int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                   int max_blocks_per_seq, int max_context_len, float scale, int partition_size,
+                   void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/*
  * pa_decode_order: host-side helper (HOST pointers, no GPU work).  Writes to
  * order[0..num_seqs) the sequence indices sorted by decreasing
  * context_lens[i], equal lengths in index order -- the longest-first visiting

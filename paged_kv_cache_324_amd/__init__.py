@@ -13,11 +13,13 @@ from ._binding import (  # noqa: F401
     load_library,
     pa_copy_blocks,
     pa_decode,
+    pa_decode_int8,
     pa_decode_order,
     pa_decode_partition_hint,
     pa_decode_step,
     pa_decode_workspace_size,
     pa_prefill_chunk,
     pa_reshape_and_cache,
+    pa_reshape_and_cache_int8,
     pa_version,
 )

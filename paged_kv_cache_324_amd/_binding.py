@@ -85,6 +85,13 @@ def _declare(lib):
     lib.pa_bm_num_tokens.argtypes = [c_vp, c_i64]
     lib.pa_bm_ref_count.restype = c_int
     lib.pa_bm_ref_count.argtypes = [c_vp, c_i64]
+    lib.pa_reshape_and_cache_int8.restype = c_int
+    lib.pa_reshape_and_cache_int8.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_int,
+                                              c_int, c_int, c_i64, c_int, c_vp]
+    lib.pa_decode_int8.restype = c_int
+    lib.pa_decode_int8.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int,
+                                   c_int, c_int, c_int, c_i64, c_int, c_int, c_f, c_int, c_vp, c_sz,
+                                   c_int, c_vp]
     lib.pa_copy_blocks.restype = c_int
     lib.pa_copy_blocks.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_int, c_int, c_int, c_i64, c_int,
                                    c_vp]
@@ -184,7 +191,7 @@ def pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None
 
 
 def _decode_common(q, k_cache, v_cache, block_tables, context_lens, seq_order, out,
-                   max_context_len, partition_size, workspace):
+                   max_context_len, partition_size, workspace, cache_dtype=None):
     lib = load_library()
     B, Hq, D = q.shape
     NB, BS, Hkv, D2 = k_cache.shape
@@ -195,8 +202,9 @@ def _decode_common(q, k_cache, v_cache, block_tables, context_lens, seq_order, o
     if seq_order is not None and seq_order.shape != (B,):
         raise ValueError("decode: seq_order must be [B]")
     dt = _dtype_code(q)
-    for n, x in (("out", out), ("k_cache", k_cache), ("v_cache", v_cache)):
-        _dev(x, n, q.dtype)
+    _dev(out, "out", q.dtype)
+    for n, x in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(x, n, q.dtype if cache_dtype is None else cache_dtype)
     need = lib.pa_decode_workspace_size(B, Hq, D, max_context_len, partition_size)
     ws_ptr, ws_bytes = None, 0
     if need:
@@ -365,3 +373,46 @@ def pa_copy_blocks(k_cache, v_cache, src, dst, stream=None) -> None:
     dp = _dev(dst, "dst", torch.int64) if n else None
     _check(lib.pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), sp, dp, n, Hkv, D, BS, NB, dt,
                               _stream(k_cache, stream)))
+
+
+def pa_reshape_and_cache_int8(key, value, k_codes, v_codes, k_scales, v_scales, slot_mapping,
+                              stream=None) -> None:
+    """Quantise key/value ``[T][Hkv][D]`` (16-bit) into an INT8 cache at ``slot_mapping``:
+    codes ``int8 [NB][BS][Hkv][D]``, scales ``float32 [NB][Hkv][BS]``."""
+    lib = load_library()
+    T, Hkv, D = key.shape
+    NB, BS, Hkv2, D2 = k_codes.shape
+    if (value.shape != key.shape or v_codes.shape != k_codes.shape or (Hkv2, D2) != (Hkv, D)
+            or k_scales.shape != (NB, Hkv, BS) or v_scales.shape != k_scales.shape):
+        raise ValueError("reshape_and_cache_int8: inconsistent shapes")
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    dt = _dtype_code(key)
+    _dev(value, "value", key.dtype)
+    for n, x in (("k_codes", k_codes), ("v_codes", v_codes)):
+        _dev(x, n, torch.int8)
+    for n, x in (("k_scales", k_scales), ("v_scales", v_scales)):
+        _dev(x, n, torch.float32)
+    _check(lib.pa_reshape_and_cache_int8(
+        _dev(key, "key"), value.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(),
+        k_scales.data_ptr(), v_scales.data_ptr(), _dev(slot_mapping, "slot_mapping", torch.int64),
+        T, Hkv, D, BS, NB, dt, _stream(key, stream)))
+
+
+def pa_decode_int8(out, q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens,
+                   scale: float, max_context_len: int, partition_size: int = 512, workspace=None,
+                   seq_order=None, stream=None) -> torch.Tensor:
+    """Paged decode over an INT8 cache (see :func:`pa_reshape_and_cache_int8`)."""
+    lib, B, Hq, Hkv, D, BS, NB, dt, ws_ptr, ws_bytes, order_ptr = _decode_common(
+        q, k_codes, v_codes, block_tables, context_lens, seq_order, out, max_context_len,
+        partition_size, workspace, cache_dtype=torch.int8)
+    if k_scales.shape != (NB, Hkv, BS) or v_scales.shape != k_scales.shape:
+        raise ValueError("decode_int8: scales must be [num_blocks][num_kv_heads][block_size]")
+    ks = _dev(k_scales, "k_scales", torch.float32)
+    vs = _dev(v_scales, "v_scales", torch.float32)
+    _check(lib.pa_decode_int8(
+        out.data_ptr(), q.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(), ks, vs,
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        order_ptr, B, Hq, Hkv, D, BS, NB, block_tables.shape[1], max_context_len, scale,
+        partition_size, ws_ptr, ws_bytes, dt, _stream(q, stream)))
+    return out

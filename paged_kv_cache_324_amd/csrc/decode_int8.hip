@@ -1,0 +1,331 @@
+// Paged-attention decode over an INT8 KV cache (head_dim 128).
+//
+// Same computation as the 16-bit decode kernels, over the dequantised cache:
+// out[i][h] = softmax(scale q K'^T) V' with K'[j] = code_K[j] * sK[j] and
+// V'[j] = code_V[j] * sV[j] per token j and KV head (page "Nano-vLLM-Ascend",
+// sections 2.1 and 2.2.1; fp32 softmax statistics, page "vLLM-Ascend ...",
+// section 3.1, problem 2; INT8 as the next KV-cache compression, page
+// "Nano-vLLM-Ascend", section 4.3, and page "vLLM-Ascend ...", section 5).
+// Caches: codes int8 [num_blocks][block_size][num_kv_heads][128], scales
+// float32 [num_blocks][num_kv_heads][block_size] (pa_reshape_and_cache_int8).
+//
+// The structure is that of decode_mfma_kernel (decode_mfma_impl.h): one
+// workgroup of 4 wavefronts per (sequence, KV head, partition), 32-key steps
+// taken round-robin, one step of K/V in flight per wavefront, block ids two
+// steps ahead, scores S^T = K Q^T on 16x16x32 MFMA and O^T += V^T P^T on
+// 16x16x16 MFMA from a transposed LDS tile, a merge of the wavefronts through
+// LDS.  What differs:
+//   * a key row is 128 bytes: lane (key col, quad) loads the 32 contiguous
+//     bytes of dims 32 quad .. 32 quad + 31 and MFMA step ks takes dims
+//     32 quad + 8 ks .. + 7; the query fragments follow the same dim order (a
+//     dot product does not depend on the order of its terms);
+//   * codes are exact in fp16 and bf16 (|code| <= 127), so each is converted in
+//     registers to the query's 16-bit type; the key scale multiplies the
+//     fp32 score, the value scale multiplies p after the softmax sum (so the
+//     denominator is unchanged) before p is rounded for the value product;
+//   * V rows arrive as 16-byte chunks of 16 codes and are written to LDS as
+//     two 16-byte chunks of 16-bit values, in the swizzled layout the
+//     transposed reads expect.
+#include "decode_impl.h"
+#include "mfma.h"
+
+namespace pa {
+
+constexpr int kI8Row = 256;                   // bytes of one converted (16-bit) V row in LDS
+constexpr int kI8StepKeys = 32;
+constexpr int kI8Step = kI8StepKeys * kI8Row;
+constexpr float kI8LazyRescale = 8.0f;
+
+__device__ __forceinline__ int i8_vswz(int r) { return (2 * r) & 15; }
+
+// Codes b[2k], b[2k+1] of a dword (signed bytes) as a packed 16-bit pair, exactly.
+template <int DT>
+__device__ __forceinline__ uint32_t i8_pair(uint32_t w, int k) {
+  const float lo = (float)(int8_t)(w >> (16 * k));
+  const float hi = (float)(int8_t)(w >> (16 * k + 8));
+  return pack2<DT>(lo, hi);
+}
+
+template <int DT>
+__device__ __forceinline__ u32x4 i8_to_16(uint32_t w0, uint32_t w1) {
+  return u32x4{i8_pair<DT>(w0, 0), i8_pair<DT>(w0, 1), i8_pair<DT>(w1, 0), i8_pair<DT>(w1, 1)};
+}
+
+template <int DT, int BS, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_int8_kernel(const DecodeArgs a) {
+  constexpr int D = 128;
+  static_assert(G >= 1 && G <= 16, "heads of a group fill the 16 MFMA columns");
+  static_assert(BS % 16 == 0, "a 16-key group lies in one block");
+  __shared__ __attribute__((aligned(16))) unsigned char s_v[4][kI8Step];  // 32 KB
+  __shared__ float s_ml[4 * 16 * 2];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15;
+  const int quad = lane >> 4;
+
+  const int per_part = a.num_seqs * a.num_kv_heads;
+  const int part = blockIdx.x / per_part;
+  const int rest = blockIdx.x - part * per_part;
+  const int rank = rest / a.num_kv_heads;
+  const int kvh = rest - rank * a.num_kv_heads;
+  const int seq = a.seq_order ? a.seq_order[rank] : rank;
+  if (seq < 0 || seq >= a.num_seqs) return;
+  const int h0 = kvh * G;
+  const int t0 = part * a.part_tokens;
+
+  const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks;
+  const int lbA = t0 / BS;
+  auto load_ids = [&](int s) -> int32_t {
+    return bt[min(lbA + (kI8StepKeys * s + 16 * (lane & 1)) / BS, a.max_blocks - 1)];
+  };
+  const int32_t ids_first = load_ids(wave);
+  int32_t ids_next = load_ids(wave + 4);
+
+  // Q^T fragment for step ks: head col (columns past G repeat head h0), dims
+  // 32 quad + 8 ks .. + 7, the order the key codes are loaded in.
+  u32x4 qf[4];
+  {
+    const u32x4* qp = reinterpret_cast<const u32x4*>(
+        static_cast<const uint16_t*>(a.q) + ((int64_t)seq * a.num_heads + h0 + (col < G ? col : 0)) * D);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = qp[4 * quad + ks];
+  }
+
+  const int L = clamp_context(a, seq);
+  if (L == 0) {
+    if (part == 0) {
+      uint16_t* o = static_cast<uint16_t*>(a.out) + ((int64_t)seq * a.num_heads + h0) * D;
+      for (int idx = threadIdx.x; idx < G * D; idx += 256) o[idx] = 0;
+    }
+    return;
+  }
+  if (t0 >= L) return;
+  const int t1 = (int)min((int64_t)L, (int64_t)t0 + a.part_tokens);
+  const int nparts_seq = 1 + (L - 1) / a.part_tokens;
+
+  const int32_t nb32 = a.num_blocks > INT32_MAX ? INT32_MAX : (int32_t)a.num_blocks;
+  const uint32_t row_bytes = (uint32_t)a.num_kv_heads * D;  // one token's codes, all heads
+  const uint64_t block_bytes = (uint64_t)BS * row_bytes;
+  const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)kvh * D;
+  const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)kvh * D;
+  const char* ksbase = reinterpret_cast<const char*>(a.k_scales) + (size_t)kvh * BS * 4;
+  const char* vsbase = reinterpret_cast<const char*>(a.v_scales) + (size_t)kvh * BS * 4;
+  const uint64_t sblock_bytes = (uint64_t)a.num_kv_heads * BS * 4;
+
+  float m = kEmptyMax, lsum = 0.f;
+  f32x4 o[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{};
+  unsigned char* const sv = s_v[wave];
+  u32x4 kr[2][2], vr[2][2], ksc[2], vsc[2];
+
+  // Codes and scales of step s (ids: the step's block ids, lane l holds group
+  // l & 1).  Past the partition the resources have size 0 (zeros, no memory).
+  auto issue = [&](int s, int32_t ids) {
+#pragma unroll
+    for (int gr = 0; gr < 2; ++gr) {
+      const int g0 = t0 + kI8StepKeys * s + 16 * gr;
+      const int lb = g0 / BS;
+      const int32_t blk = __builtin_amdgcn_readlane(ids, gr);
+      const int nv = min(16, t1 - g0);
+      const bool ok = nv > 0 && blk >= 0 && blk < nb32;
+      const int off_in_blk = g0 - lb * BS;
+      const uint64_t off = ok ? (uint64_t)(uint32_t)blk * block_bytes + (uint64_t)off_in_blk * row_bytes : 0ull;
+      const uint32_t nrec = ok ? (uint32_t)(nv - 1) * row_bytes + D : 0u;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + off, nrec);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + off, nrec);
+      const uint64_t soff = ok ? (uint64_t)(uint32_t)blk * sblock_bytes + (uint64_t)off_in_blk * 4 : 0ull;
+      const uint32_t snrec = ok ? (uint32_t)nv * 4 : 0u;
+      const __amdgpu_buffer_rsrc_t rks = make_rsrc(ksbase + soff, snrec);
+      const __amdgpu_buffer_rsrc_t rvs = make_rsrc(vsbase + soff, snrec);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        kr[gr][j] = buffer_load16<kCachePolicyNT>(rk, (uint32_t)col * row_bytes + (uint32_t)(32 * quad + 16 * j));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        vr[gr][j] = buffer_load16<kCachePolicyNT>(
+            rv, (uint32_t)(8 * j + (lane >> 3)) * row_bytes + (uint32_t)((lane & 7) * 16));
+      ksc[gr] = buffer_load16<kCachePolicyNT>(rks, (uint32_t)(16 * quad));
+      vsc[gr] = buffer_load16<kCachePolicyNT>(rvs, (uint32_t)(16 * quad));
+    }
+  };
+
+  // V codes -> 16-bit rows of this wavefront's LDS tile (row 16 gr + 8 j +
+  // lane / 8 of the step, dims 16 (lane % 8) .. + 15 = chunks 2 (lane % 8), +1).
+  auto store_v = [&]() {
+#pragma unroll
+    for (int gr = 0; gr < 2; ++gr)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = 16 * gr + 8 * j + (lane >> 3);
+        const int c = 2 * (lane & 7);
+        unsigned char* rowp = sv + r * kI8Row;
+        *reinterpret_cast<u32x4*>(rowp + ((c ^ i8_vswz(r)) * 16)) = i8_to_16<DT>(vr[gr][j].x, vr[gr][j].y);
+        *reinterpret_cast<u32x4*>(rowp + (((c + 1) ^ i8_vswz(r)) * 16)) = i8_to_16<DT>(vr[gr][j].z, vr[gr][j].w);
+      }
+  };
+
+  auto scores = [&](f32x4 (&sc)[2], f32x4 (&kscale)[2], f32x4 (&vscale)[2]) {
+#pragma unroll
+    for (int gr = 0; gr < 2; ++gr) {
+      sc[gr] = f32x4{};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 w = kr[gr][ks >> 1];
+        const u32x4 kf = (ks & 1) ? i8_to_16<DT>(w.z, w.w) : i8_to_16<DT>(w.x, w.y);
+        sc[gr] = mfma16x16x32<DT>(kf, qf[ks], sc[gr]);
+      }
+      kscale[gr] = __builtin_bit_cast(f32x4, ksc[gr]);
+      vscale[gr] = __builtin_bit_cast(f32x4, vsc[gr]);
+    }
+  };
+
+  auto accumulate = [&](f32x4 (&sc)[2], const f32x4 (&kscale)[2], const f32x4 (&vscale)[2], int kb,
+                        int kend) {
+#pragma unroll
+    for (int gr = 0; gr < 2; ++gr) sc[gr] *= kscale[gr];  // key j's score x sK[j]
+    if (kb + kI8StepKeys > kend) {
+#pragma unroll
+      for (int gr = 0; gr < 2; ++gr)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kb + 16 * gr + 4 * quad + i >= kend) sc[gr][i] = -__builtin_inff();
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > m + kI8LazyRescale)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int gr = 0; gr < 2; ++gr)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = fast_exp2(fmaf(sc[gr][i], a.scale_log2, -m));
+        psum += p;
+        sc[gr][i] = p * vscale[gr][i];  // the value scale, outside the denominator
+      }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    lsum += psum;
+#pragma unroll
+    for (int gr = 0; gr < 2; ++gr) {
+      const u32x2 pf = {pack2<DT>(sc[gr][0], sc[gr][1]), pack2<DT>(sc[gr][2], sc[gr][3])};
+      const int rr = 16 * gr + 4 * quad + (col >> 2);
+      const unsigned char* rowp = sv + rr * kI8Row + 8 * (col & 1);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const int chunk = 2 * dt + ((col & 3) >> 1);
+        const u32x2 vf = lds_read_tr16(rowp + ((chunk ^ i8_vswz(rr)) * 16));
+        o[dt] = mfma16x16x16<DT>(vf, pf, o[dt]);
+      }
+    }
+  };
+
+  const int nsteps = (t1 - t0 + kI8StepKeys - 1) / kI8StepKeys;
+  int s = wave;
+  if (s < nsteps) {
+    issue(s, ids_first);
+    for (; s < nsteps; s += 4) {
+      const int32_t ids_after = load_ids(s + 8);
+      store_v();
+      f32x4 sc[2], kscale[2], vscale[2];
+      scores(sc, kscale, vscale);
+      issue(s + 4, ids_next);
+      ids_next = ids_after;
+      accumulate(sc, kscale, vscale, t0 + kI8StepKeys * s, t1);
+    }
+  }
+
+  // Merge the four wavefronts' (m, l, O) and write the partition.
+  float* s_o = reinterpret_cast<float*>(sv);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_o[col * D + 16 * dt + 4 * quad + i] = o[dt][i];
+  if (quad == 0) {
+    s_ml[(wave * 16 + col) * 2] = m;
+    s_ml[(wave * 16 + col) * 2 + 1] = lsum;
+  }
+  __syncthreads();
+  const float* s_all = reinterpret_cast<const float*>(&s_v[0][0]);
+  const int64_t prow = ((int64_t)seq * a.num_parts + part) * a.num_heads + h0;
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int g = idx / D;
+    const int d = idx - g * D;
+    float M = s_ml[g * 2];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, s_ml[(w * 16 + g) * 2]);
+    float den = 0.f, ov = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = fast_exp2(s_ml[(w * 16 + g) * 2] - M);
+      den = fmaf(s_ml[(w * 16 + g) * 2 + 1], f, den);
+      ov = fmaf(s_all[(w * 16 + g) * D + d], f, ov);
+    }
+    const float val = ov / den;
+    if (nparts_seq == 1) {
+      static_cast<uint16_t*>(a.out)[((int64_t)seq * a.num_heads + h0 + g) * D + d] = to_u16<DT>(val);
+    } else {
+      a.part_out[prow * D + idx] = to_u16<DT>(val);
+    }
+  }
+  if (nparts_seq > 1 && (int)threadIdx.x < G) {
+    const int g = threadIdx.x;
+    float M = s_ml[g * 2];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, s_ml[(w * 16 + g) * 2]);
+    float den = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      den = fmaf(s_ml[(w * 16 + g) * 2 + 1], fast_exp2(s_ml[(w * 16 + g) * 2] - M), den);
+    reinterpret_cast<float2*>(a.part_ml)[prow + g] = make_float2(M, den);
+  }
+}
+
+template <int DT, int BS, int G>
+hipError_t launch_int8_t(const DecodeArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_parts);
+  hipLaunchKernelGGL((decode_int8_kernel<DT, BS, G>), dim3(grid), dim3(256), 0, s, a);
+  if (a.num_parts > 1)
+    hipLaunchKernelGGL((decode_merge_kernel<DT, 128>), dim3((unsigned)(a.num_seqs * a.num_heads)),
+                       dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, int BS>
+hipError_t launch_int8_g(const DecodeArgs& a, int group, hipStream_t s) {
+  switch (group) {
+    case 1: return launch_int8_t<DT, BS, 1>(a, s);
+    case 2: return launch_int8_t<DT, BS, 2>(a, s);
+    case 4: return launch_int8_t<DT, BS, 4>(a, s);
+    case 8: return launch_int8_t<DT, BS, 8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DT>
+hipError_t launch_int8_dt(const DecodeArgs& a, int block_size, int group, hipStream_t s) {
+  switch (block_size) {
+    case 16: return launch_int8_g<DT, 16>(a, group, s);
+    case 32: return launch_int8_g<DT, 32>(a, group, s);
+    case 256: return launch_int8_g<DT, 256>(a, group, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_int8(const DecodeArgs& a, int dtype, int block_size, int group,
+                              hipStream_t s) {
+  return dtype == DT_BF16 ? launch_int8_dt<DT_BF16>(a, block_size, group, s)
+                          : launch_int8_dt<DT_F16>(a, block_size, group, s);
+}
+
+}  // namespace pa

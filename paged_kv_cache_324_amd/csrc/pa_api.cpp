@@ -219,9 +219,16 @@ struct NewTokens {
   void* v_cache;
 };
 
+// Per-row scales of an INT8 cache (pa_decode_int8); null for 16-bit caches.
+struct Int8Scales {
+  const float* k;
+  const float* v;
+};
+
 int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* block_tables, const int32_t* context_lens,
-                const int32_t* seq_order, const NewTokens* nt, int num_seqs, int num_heads,
+                const int32_t* seq_order, const NewTokens* nt, const Int8Scales* i8,
+                int num_seqs, int num_heads,
                 int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
                 int max_blocks_per_seq, int max_context_len, float scale, int partition_size,
                 void* workspace, size_t workspace_bytes, int dtype, void* stream) {
@@ -241,6 +248,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (nt && (!nt->key || !nt->value || !nt->slot_mapping || !nt->k_cache || !nt->v_cache))
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (i8 && (!i8->k || !i8->v)) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   const int64_t parts = num_partitions(max_context_len, partition_size);
   const int64_t grid = (int64_t)num_seqs * num_kv_heads * parts;
   if (grid > INT32_MAX || (int64_t)num_seqs * num_heads > INT32_MAX)
@@ -272,6 +280,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.slot_mapping = nt ? nt->slot_mapping : nullptr;
   a.k_cache_w = nt ? nt->k_cache : nullptr;
   a.v_cache_w = nt ? nt->v_cache : nullptr;
+  a.k_scales = i8 ? i8->k : nullptr;
+  a.v_scales = i8 ? i8->v : nullptr;
   a.num_slots = num_blocks * (int64_t)block_size;
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
@@ -284,8 +294,10 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   const int group = num_heads / num_kv_heads;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = dtype == PA_BF16 ? pa::launch_decode_bf16(a, head_dim, block_size, group, s)
-                                  : pa::launch_decode_f16(a, head_dim, block_size, group, s);
+  // PA_F16 / PA_BF16 are the kernels' dtype codes.
+  hipError_t e = i8 ? pa::launch_decode_int8(a, dtype, block_size, group, s)
+                 : dtype == PA_BF16 ? pa::launch_decode_bf16(a, head_dim, block_size, group, s)
+                                    : pa::launch_decode_f16(a, head_dim, block_size, group, s);
   return hip_status(e, "decode launch");
 }
 
@@ -299,7 +311,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int64_t num_blocks, int max_blocks_per_seq, int max_context_len, float scale,
               int partition_size, void* workspace, size_t workspace_bytes, int dtype,
               void* stream) {
-  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, seq_order, nullptr,
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, seq_order, nullptr, nullptr,
                      num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
                      workspace_bytes, dtype, stream);
@@ -313,7 +325,54 @@ int pa_decode_step(void* out, const void* q, const void* key, const void* value,
                    int max_context_len, float scale, int partition_size, void* workspace,
                    size_t workspace_bytes, int dtype, void* stream) {
   NewTokens nt{key, value, slot_mapping, k_cache, v_cache};
-  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, seq_order, &nt,
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, seq_order, &nt, nullptr,
+                     num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
+                     workspace_bytes, dtype, stream);
+}
+
+int pa_reshape_and_cache_int8(const void* key, const void* value, void* k_codes, void* v_codes,
+                              float* k_scales, float* v_scales, const int64_t* slot_mapping,
+                              int64_t num_tokens, int num_kv_heads, int head_dim, int block_size,
+                              int64_t num_blocks, int dtype, void* stream) {
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens must be >= 0");
+  if (num_kv_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
+  if (!supported_head_dim(head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not in {64,128}", head_dim);
+  if (!supported_block_size(block_size))
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not in {16,32,256}", block_size);
+  if (!supported_dtype(dtype)) return fail(PA_ERR_UNSUPPORTED, "dtype %d not PA_F16/PA_BF16", dtype);
+  if (num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !k_codes || !v_codes || !k_scales || !v_scales || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if ((int64_t)num_kv_heads * head_dim > INT32_MAX / 4)
+    return fail(PA_ERR_INVALID_ARG, "token row too large");
+  pa::ReshapeInt8Args a;
+  a.key = key;
+  a.value = value;
+  a.k_codes = k_codes;
+  a.v_codes = v_codes;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_slots = num_blocks * (int64_t)block_size;
+  a.num_kv_heads = num_kv_heads;
+  a.block_size = block_size;
+  return hip_status(pa::launch_reshape_int8(a, dtype, head_dim, static_cast<hipStream_t>(stream)),
+                    "reshape_and_cache_int8 launch");
+}
+
+int pa_decode_int8(void* out, const void* q, const void* k_codes, const void* v_codes,
+                   const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                   const int32_t* context_lens, const int32_t* seq_order, int num_seqs,
+                   int num_heads, int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                   int max_blocks_per_seq, int max_context_len, float scale, int partition_size,
+                   void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  if (head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "INT8 decode supports head_dim 128 only");
+  const Int8Scales i8{k_scales, v_scales};
+  return decode_impl(out, q, k_codes, v_codes, block_tables, context_lens, seq_order, nullptr, &i8,
                      num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
                      workspace_bytes, dtype, stream);

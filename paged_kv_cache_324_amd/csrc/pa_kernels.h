@@ -17,6 +17,20 @@ struct ReshapeArgs {
   int row_chunks;      // 16-byte chunks in one token's num_kv_heads * head_dim row
 };
 
+struct ReshapeInt8Args {
+  const void* key;       // [num_tokens][num_kv_heads][head_dim], 16-bit
+  const void* value;
+  void* k_codes;         // int8 [num_blocks][block_size][num_kv_heads][head_dim]
+  void* v_codes;
+  float* k_scales;       // [num_blocks][num_kv_heads][block_size]
+  float* v_scales;
+  const int64_t* slot_mapping;
+  int64_t num_tokens;
+  int64_t num_slots;
+  int num_kv_heads;
+  int block_size;
+};
+
 struct CopyBlocksArgs {
   void* k_cache;
   void* v_cache;
@@ -45,6 +59,8 @@ struct DecodeArgs {
   const int64_t* slot_mapping;
   void* k_cache_w;
   void* v_cache_w;
+  const float* k_scales;  // INT8 caches only: [num_blocks][num_kv_heads][block_size]
+  const float* v_scales;
   int64_t num_slots;   // num_blocks * block_size
   int64_t num_blocks;
   int num_seqs;
@@ -79,6 +95,11 @@ struct PrefillArgs {
 
 hipError_t launch_reshape_and_cache(const ReshapeArgs& a, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
+hipError_t launch_reshape_int8(const ReshapeInt8Args& a, int dtype, int head_dim, hipStream_t s);
+// INT8 decode: DecodeArgs with k_cache / v_cache pointing at the int8 codes and
+// the per-row scales in k_scales / v_scales.
+hipError_t launch_decode_int8(const DecodeArgs& a, int dtype, int block_size, int group,
+                              hipStream_t s);
 
 // dtype DT_F16 / DT_BF16; head_dim 64/128; block_size 16/32/256; group 1/2/4/8.
 hipError_t launch_decode_f16(const DecodeArgs& a, int head_dim, int block_size, int group,
