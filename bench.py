@@ -193,6 +193,60 @@ def run_decode(pa, torch, b, partition, steps, warmup, unfused, dev):
     return {"ms_per_step": ms, "kernel_ms": kernel_ms, "kernel_name": name}
 
 
+def int8_kv_bytes(b) -> int:
+    """Bytes of the quantised K and V one decode reads: a code per element and one fp32
+    scale per (token, KV head), for keys and values."""
+    return int(b.context_lens.astype(np.int64).sum()) * b.Hkv * (b.D + 4) * 2
+
+
+def run_decode_int8(pa, torch, b, partition, steps, warmup, dev):
+    """Decode over an INT8 cache: each step quantises the new tokens into their slots
+    (pa_reshape_and_cache_int8) and attends (pa_decode_int8).  The cache is filled with the
+    batch's cached tokens, quantised by the library, before timing."""
+    dt = torch.bfloat16 if b.dtype == "bf16" else torch.float16
+
+    def dev16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(dt)
+
+    kc = torch.zeros((b.NB, b.Hkv, b.BS, b.D), dtype=torch.int8, device=dev)   # head-major
+    vc = torch.zeros_like(kc)
+    ks = torch.zeros((b.NB, b.Hkv, b.BS), dtype=torch.float32, device=dev)
+    vs = torch.zeros_like(ks)
+    comp = []
+    for i in range(b.B):                      # cached positions, each physical slot once
+        t = np.arange(int(b.context_lens[i]) - int(b.n_new[i]))
+        comp.append(b.block_tables_compact[i, t // b.BS].astype(np.int64) * b.BS + t % b.BS)
+    comp = np.unique(np.concatenate(comp))
+    for lo in range(0, comp.size, 1 << 18):
+        c = comp[lo:lo + (1 << 18)]
+        phys = b.phys_ids[c // b.BS].astype(np.int64) * b.BS + c % b.BS
+        pa.pa_reshape_and_cache_int8(dev16(b.k_blocks.reshape(-1, b.Hkv, b.D)[c]),
+                                     dev16(b.v_blocks.reshape(-1, b.Hkv, b.D)[c]), kc, vc, ks, vs,
+                                     torch.from_numpy(phys).to(dev))
+    q, knew, vnew = dev16(b.q), dev16(b.key_new), dev16(b.value_new)
+    slot = torch.from_numpy(b.slot_mapping).to(dev)
+    tables = torch.from_numpy(b.block_tables).to(dev)
+    lens = torch.from_numpy(b.context_lens).to(dev)
+    out = torch.empty_like(q)
+    workspace = pa.decode_workspace(b.B, b.Hq, b.D, b.max_context_len, partition, dev)
+    stream = torch.cuda.current_stream(dev)
+    order = torch.from_numpy(pa.pa_decode_order(b.context_lens)).to(dev)
+    torch.cuda.synchronize(dev)
+
+    def step():
+        pa.pa_reshape_and_cache_int8(knew, vnew, kc, vc, ks, vs, slot, stream=stream)
+        pa.pa_decode_int8(out, q, kc, vc, ks, vs, tables, lens, b.scale, b.max_context_len,
+                          partition, workspace=workspace, seq_order=order, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    ms = _timed(torch, step, steps)
+    kernel_ms = _events(torch, step, steps, stream)
+    name = "pa_reshape_and_cache_int8 + pa_decode_int8 (decode_int8_kernel" + (
+        " + merge kernel)" if partition and b.max_context_len > partition else ")")
+    return {"ms_per_step": ms, "kernel_ms": kernel_ms, "kernel_name": name}
+
+
 def run_prefill(pa, torch, b, steps, warmup, dev):
     d = upload(torch, b, dev)
     out = torch.empty_like(d.q)
@@ -229,8 +283,10 @@ def main(argv=None) -> int:
                          "fused pa_decode_step")
     ap.add_argument("--secondary",
                     default="llama2_70b_decode_bs16,llama2_70b_decode_bs32,long_splitk_decode,"
-                            "chunked_prefill",
-                    help="comma-separated extra workloads reported beside the headline")
+                            "chunked_prefill,qwen3_0p6b_decode:int8,llama2_70b_decode_bs16:int8,"
+                            "long_splitk_decode:int8",
+                    help="comma-separated extra workloads reported beside the headline; "
+                         "a ':int8' suffix runs the workload over an INT8 KV cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-kernel-bytes", type=int, default=0,
@@ -310,13 +366,30 @@ def main(argv=None) -> int:
                      "traffic": recorded_traffic(args.workload, partition)},
     }
     secondary = {}
-    for name in [x for x in args.secondary.split(",") if x]:
+    for entry in [x for x in args.secondary.split(",") if x]:
+        name, _, variant = entry.partition(":")
         c2 = CONFIGS[name]
         t_gen = time.perf_counter()
         b2 = make_config(name)
         print(f"[bench] generated {name} in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
               flush=True)
         steps2 = max(5, args.steps // 10)
+        if variant == "int8":
+            p2 = resolve_partition(pa, c2, b2)
+            r2 = run_decode_int8(pa, torch, b2, p2, steps2, max(2, args.warmup // 4), dev)
+            kb = int8_kv_bytes(b2)
+            ach2 = kb / (float(r2["kernel_ms"].mean()) * 1e-3) / 1e9
+            secondary[entry] = {
+                "step": "pa_reshape_and_cache_int8 + pa_decode_int8", "partition_size": p2,
+                "steps": steps2, "ms_per_step": round(r2["ms_per_step"], 5),
+                "int8_kv_bytes": kb, "effective_GBps": round(kb / (r2["ms_per_step"] * 1e-3) / 1e9, 2),
+                "bf16_equivalent_GBps": round(b2.kv_bytes() / (r2["ms_per_step"] * 1e-3) / 1e9, 2),
+                "seqs_per_s": round(b2.B / (r2["ms_per_step"] * 1e-3), 1),
+                "decode_us": _stats_us(r2["kernel_ms"]),
+                "roofline": {"bound": "hbm", "kernel": r2["kernel_name"], "achieved": round(ach2, 2),
+                             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": round(ach2 / HBM_PEAK_GBPS, 4), "traffic": None}}
+            continue
         if c2["kind"] == "prefill":
             r2 = run_prefill(pa, torch, b2, steps2, max(2, args.warmup // 4), dev)
             flops = prefill_flops(b2)

@@ -187,8 +187,12 @@ int pa_decode_step(void* out, const void* q, const void* key, const void* value,
  * (ties to even; an all-zero row has scale 0 and codes 0); the value used is
  * code_d * scale.
  *
- *   k_codes, v_codes   : int8 [num_blocks][block_size][num_kv_heads][head_dim]
+ *   k_codes, v_codes   : int8 [num_blocks][num_kv_heads][block_size][head_dim]
  *   k_scales, v_scales : float32 [num_blocks][num_kv_heads][block_size]
+ *
+ * Unlike the 16-bit caches, the INT8 caches are head-major within a block: the
+ * block_size rows of one KV head are contiguous, so a decode reads each
+ * (block, head) as one run.
  *
  * pa_reshape_and_cache_int8: quantise key/value [num_tokens][num_kv_heads]
  * [head_dim] (16-bit, dtype) into the slots of slot_mapping, as

@@ -18,8 +18,8 @@ keeps each score's precision local:
   reaches the same codes and scales bit for bit;
 * the value used by attention is ``code_d * scale`` (exact in float64).
 
-Cache layout (the library's): codes ``int8 [NB][BS][Hkv][D]``; scales
-``float32 [NB][Hkv][BS]`` (one head's scales of a block contiguous).
+Cache layout (the library's), head-major within a block: codes
+``int8 [NB][Hkv][BS][D]``; scales ``float32 [NB][Hkv][BS]``.
 """
 from __future__ import annotations
 
@@ -49,10 +49,10 @@ def reshape_and_cache_int8(key, value, k_codes, v_codes, k_scales, v_scales, slo
                            dtype: str) -> None:
     """Quantise this step's rows ``[T][Hkv][D]`` (16-bit bits) into their slots, in place.
 
-    Caches: codes ``[NB][BS][Hkv][D]`` int8, scales ``[NB][Hkv][BS]`` float32.
+    Caches: codes ``[NB][Hkv][BS][D]`` int8, scales ``[NB][Hkv][BS]`` float32.
     Slots < 0 (padding) and slots outside the pool are skipped.
     """
-    NB, BS = k_codes.shape[0], k_codes.shape[1]
+    NB, BS = k_codes.shape[0], k_codes.shape[2]
     kq, ks = quantize_rows(key, dtype)
     vq, vs = quantize_rows(value, dtype)
     for t, slot in enumerate(np.asarray(slot_mapping)):
@@ -60,19 +60,19 @@ def reshape_and_cache_int8(key, value, k_codes, v_codes, k_scales, v_scales, slo
         if slot < 0 or slot >= NB * BS:
             continue
         b, o = slot // BS, slot % BS
-        k_codes[b, o] = kq[t]
-        v_codes[b, o] = vq[t]
+        k_codes[b, :, o] = kq[t]
+        v_codes[b, :, o] = vq[t]
         k_scales[b, :, o] = ks[t]
         v_scales[b, :, o] = vs[t]
 
 
 def gather_int8(codes, scales, block_table_row, L: int) -> np.ndarray:
     """Dequantised logical rows 0..L-1 of one sequence, ``[L][Hkv][D]`` float64."""
-    BS = codes.shape[1]
+    BS = codes.shape[2]
     parts = []
     for j in range(blocks_needed(L, BS)):
         b = int(block_table_row[j])
-        parts.append(dequantize(codes[b], scales[b].T))       # [BS][Hkv][D]
+        parts.append(dequantize(codes[b], scales[b]).transpose(1, 0, 2))  # [BS][Hkv][D]
     return np.concatenate(parts)[:L]
 
 
@@ -82,7 +82,7 @@ def paged_decode_int8(q, k_codes, v_codes, k_scales, v_scales, block_tables, con
     ``K'`` = code x scale per token and head; q is 16-bit bits ``[B][Hq][D]``;
     a sequence of length 0 gives a zero row.  Returns ``[B][Hq][D]`` float64."""
     B, Hq, D = q.shape
-    Hkv = k_codes.shape[2]
+    Hkv = k_codes.shape[1]
     out = np.zeros((B, Hq, D))
     for i in range(B):
         L = int(context_lens[i])

@@ -191,10 +191,13 @@ def pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None
 
 
 def _decode_common(q, k_cache, v_cache, block_tables, context_lens, seq_order, out,
-                   max_context_len, partition_size, workspace, cache_dtype=None):
+                   max_context_len, partition_size, workspace, cache_dtype=None, head_major=False):
     lib = load_library()
     B, Hq, D = q.shape
-    NB, BS, Hkv, D2 = k_cache.shape
+    if head_major:
+        NB, Hkv, BS, D2 = k_cache.shape
+    else:
+        NB, BS, Hkv, D2 = k_cache.shape
     if out.shape != q.shape or v_cache.shape != k_cache.shape or D2 != D:
         raise ValueError("decode: inconsistent shapes")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
@@ -378,10 +381,10 @@ def pa_copy_blocks(k_cache, v_cache, src, dst, stream=None) -> None:
 def pa_reshape_and_cache_int8(key, value, k_codes, v_codes, k_scales, v_scales, slot_mapping,
                               stream=None) -> None:
     """Quantise key/value ``[T][Hkv][D]`` (16-bit) into an INT8 cache at ``slot_mapping``:
-    codes ``int8 [NB][BS][Hkv][D]``, scales ``float32 [NB][Hkv][BS]``."""
+    codes ``int8 [NB][Hkv][BS][D]`` (head-major), scales ``float32 [NB][Hkv][BS]``."""
     lib = load_library()
     T, Hkv, D = key.shape
-    NB, BS, Hkv2, D2 = k_codes.shape
+    NB, Hkv2, BS, D2 = k_codes.shape
     if (value.shape != key.shape or v_codes.shape != k_codes.shape or (Hkv2, D2) != (Hkv, D)
             or k_scales.shape != (NB, Hkv, BS) or v_scales.shape != k_scales.shape):
         raise ValueError("reshape_and_cache_int8: inconsistent shapes")
@@ -405,7 +408,7 @@ def pa_decode_int8(out, q, k_codes, v_codes, k_scales, v_scales, block_tables, c
     """Paged decode over an INT8 cache (see :func:`pa_reshape_and_cache_int8`)."""
     lib, B, Hq, Hkv, D, BS, NB, dt, ws_ptr, ws_bytes, order_ptr = _decode_common(
         q, k_codes, v_codes, block_tables, context_lens, seq_order, out, max_context_len,
-        partition_size, workspace, cache_dtype=torch.int8)
+        partition_size, workspace, cache_dtype=torch.int8, head_major=True)
     if k_scales.shape != (NB, Hkv, BS) or v_scales.shape != k_scales.shape:
         raise ValueError("decode_int8: scales must be [num_blocks][num_kv_heads][block_size]")
     ks = _dev(k_scales, "k_scales", torch.float32)

@@ -6,13 +6,14 @@
 // sections 2.1 and 2.2.1; fp32 softmax statistics, page "vLLM-Ascend ...",
 // section 3.1, problem 2; INT8 as the next KV-cache compression, page
 // "Nano-vLLM-Ascend", section 4.3, and page "vLLM-Ascend ...", section 5).
-// Caches: codes int8 [num_blocks][block_size][num_kv_heads][128], scales
-// float32 [num_blocks][num_kv_heads][block_size] (pa_reshape_and_cache_int8).
+// Caches, head-major within a block: codes int8 [num_blocks][num_kv_heads]
+// [block_size][128], scales float32 [num_blocks][num_kv_heads][block_size]
+// (pa_reshape_and_cache_int8): a 16-key group of one head is one contiguous
+// 2 KB run (the token-major 16-bit layout would leave 16 runs of 128 bytes).
 //
 // The structure is that of decode_mfma_kernel (decode_mfma_impl.h): one
 // workgroup of 4 wavefronts per (sequence, KV head, partition), 32-key steps
-// taken round-robin, one step of K/V in flight per wavefront, block ids two
-// steps ahead, scores S^T = K Q^T on 16x16x32 MFMA and O^T += V^T P^T on
+// taken round-robin, scores S^T = K Q^T on 16x16x32 MFMA and O^T += V^T P^T on
 // 16x16x16 MFMA from a transposed LDS tile, a merge of the wavefronts through
 // LDS.  What differs:
 //   * a key row is 128 bytes: lane (key col, quad) loads the 32 contiguous
@@ -25,7 +26,9 @@
 //     denominator is unchanged) before p is rounded for the value product;
 //   * V rows arrive as 16-byte chunks of 16 codes and are written to LDS as
 //     two 16-byte chunks of 16-bit values, in the swizzled layout the
-//     transposed reads expect.
+//     transposed reads expect;
+//   * a step carries half the bytes, so each wavefront keeps two steps in
+//     flight (two register sets) instead of one.
 #include "decode_impl.h"
 #include "mfma.h"
 
@@ -80,7 +83,8 @@ void decode_int8_kernel(const DecodeArgs a) {
     return bt[min(lbA + (kI8StepKeys * s + 16 * (lane & 1)) / BS, a.max_blocks - 1)];
   };
   const int32_t ids_first = load_ids(wave);
-  int32_t ids_next = load_ids(wave + 4);
+  const int32_t ids_second = load_ids(wave + 4);
+  int32_t ids_next = load_ids(wave + 8);
 
   // Q^T fragment for step ks: head col (columns past G repeat head h0), dims
   // 32 quad + 8 ks .. + 7, the order the key codes are loaded in.
@@ -105,10 +109,10 @@ void decode_int8_kernel(const DecodeArgs a) {
   const int nparts_seq = 1 + (L - 1) / a.part_tokens;
 
   const int32_t nb32 = a.num_blocks > INT32_MAX ? INT32_MAX : (int32_t)a.num_blocks;
-  const uint32_t row_bytes = (uint32_t)a.num_kv_heads * D;  // one token's codes, all heads
-  const uint64_t block_bytes = (uint64_t)BS * row_bytes;
-  const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)kvh * D;
-  const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)kvh * D;
+  const uint32_t row_bytes = (uint32_t)D;  // consecutive keys of one head
+  const uint64_t block_bytes = (uint64_t)a.num_kv_heads * BS * D;
+  const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)kvh * BS * D;
+  const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)kvh * BS * D;
   const char* ksbase = reinterpret_cast<const char*>(a.k_scales) + (size_t)kvh * BS * 4;
   const char* vsbase = reinterpret_cast<const char*>(a.v_scales) + (size_t)kvh * BS * 4;
   const uint64_t sblock_bytes = (uint64_t)a.num_kv_heads * BS * 4;
@@ -118,11 +122,16 @@ void decode_int8_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{};
   unsigned char* const sv = s_v[wave];
-  u32x4 kr[2][2], vr[2][2], ksc[2], vsc[2];
+  // Two register sets of codes and scales: the steps s + 4 and s + 8 of a
+  // wavefront are in flight while step s computes.
+  struct Regs {
+    u32x4 kr[2][2], vr[2][2], ksc[2], vsc[2];
+  };
+  Regs ra, rb;
 
   // Codes and scales of step s (ids: the step's block ids, lane l holds group
   // l & 1).  Past the partition the resources have size 0 (zeros, no memory).
-  auto issue = [&](int s, int32_t ids) {
+  auto issue = [&](int s, int32_t ids, Regs& r) {
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr) {
       const int g0 = t0 + kI8StepKeys * s + 16 * gr;
@@ -141,43 +150,44 @@ void decode_int8_kernel(const DecodeArgs a) {
       const __amdgpu_buffer_rsrc_t rvs = make_rsrc(vsbase + soff, snrec);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        kr[gr][j] = buffer_load16<kCachePolicyNT>(rk, (uint32_t)col * row_bytes + (uint32_t)(32 * quad + 16 * j));
+        r.kr[gr][j] = buffer_load16<kCachePolicyNT>(rk, (uint32_t)col * row_bytes + (uint32_t)(32 * quad + 16 * j));
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        vr[gr][j] = buffer_load16<kCachePolicyNT>(
+        r.vr[gr][j] = buffer_load16<kCachePolicyNT>(
             rv, (uint32_t)(8 * j + (lane >> 3)) * row_bytes + (uint32_t)((lane & 7) * 16));
-      ksc[gr] = buffer_load16<kCachePolicyNT>(rks, (uint32_t)(16 * quad));
-      vsc[gr] = buffer_load16<kCachePolicyNT>(rvs, (uint32_t)(16 * quad));
+      r.ksc[gr] = buffer_load16<kCachePolicyNT>(rks, (uint32_t)(16 * quad));
+      r.vsc[gr] = buffer_load16<kCachePolicyNT>(rvs, (uint32_t)(16 * quad));
     }
   };
 
   // V codes -> 16-bit rows of this wavefront's LDS tile (row 16 gr + 8 j +
   // lane / 8 of the step, dims 16 (lane % 8) .. + 15 = chunks 2 (lane % 8), +1).
-  auto store_v = [&]() {
+  auto store_v = [&](const Regs& r) {
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int r = 16 * gr + 8 * j + (lane >> 3);
+        const int row = 16 * gr + 8 * j + (lane >> 3);
         const int c = 2 * (lane & 7);
-        unsigned char* rowp = sv + r * kI8Row;
-        *reinterpret_cast<u32x4*>(rowp + ((c ^ i8_vswz(r)) * 16)) = i8_to_16<DT>(vr[gr][j].x, vr[gr][j].y);
-        *reinterpret_cast<u32x4*>(rowp + (((c + 1) ^ i8_vswz(r)) * 16)) = i8_to_16<DT>(vr[gr][j].z, vr[gr][j].w);
+        unsigned char* rowp = sv + row * kI8Row;
+        const u32x4 w = r.vr[gr][j];
+        *reinterpret_cast<u32x4*>(rowp + ((c ^ i8_vswz(row)) * 16)) = i8_to_16<DT>(w.x, w.y);
+        *reinterpret_cast<u32x4*>(rowp + (((c + 1) ^ i8_vswz(row)) * 16)) = i8_to_16<DT>(w.z, w.w);
       }
   };
 
-  auto scores = [&](f32x4 (&sc)[2], f32x4 (&kscale)[2], f32x4 (&vscale)[2]) {
+  auto scores = [&](const Regs& r, f32x4 (&sc)[2], f32x4 (&kscale)[2], f32x4 (&vscale)[2]) {
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr) {
       sc[gr] = f32x4{};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 w = kr[gr][ks >> 1];
+        const u32x4 w = r.kr[gr][ks >> 1];
         const u32x4 kf = (ks & 1) ? i8_to_16<DT>(w.z, w.w) : i8_to_16<DT>(w.x, w.y);
         sc[gr] = mfma16x16x32<DT>(kf, qf[ks], sc[gr]);
       }
-      kscale[gr] = __builtin_bit_cast(f32x4, ksc[gr]);
-      vscale[gr] = __builtin_bit_cast(f32x4, vsc[gr]);
+      kscale[gr] = __builtin_bit_cast(f32x4, r.ksc[gr]);
+      vscale[gr] = __builtin_bit_cast(f32x4, r.vsc[gr]);
     }
   };
 
@@ -230,18 +240,31 @@ void decode_int8_kernel(const DecodeArgs a) {
     }
   };
 
+  // Step s computes from one register set, which then takes step s + 8; the
+  // other set holds step s + 4.  Block ids run a step ahead of the loads that
+  // use them.  Look-ahead loads are unconditional (clamped ids, size-0
+  // resources past the partition), so every step waits for the same loads.
   const int nsteps = (t1 - t0 + kI8StepKeys - 1) / kI8StepKeys;
+  auto step = [&](int s, Regs& r) {
+    const int32_t ids_after = load_ids(s + 12);
+    store_v(r);
+    f32x4 sc[2], kscale[2], vscale[2];
+    scores(r, sc, kscale, vscale);
+    issue(s + 8, ids_next, r);
+    ids_next = ids_after;
+    accumulate(sc, kscale, vscale, t0 + kI8StepKeys * s, t1);
+  };
   int s = wave;
   if (s < nsteps) {
-    issue(s, ids_first);
-    for (; s < nsteps; s += 4) {
-      const int32_t ids_after = load_ids(s + 8);
-      store_v();
-      f32x4 sc[2], kscale[2], vscale[2];
-      scores(sc, kscale, vscale);
-      issue(s + 4, ids_next);
-      ids_next = ids_after;
-      accumulate(sc, kscale, vscale, t0 + kI8StepKeys * s, t1);
+    issue(s, ids_first, ra);
+    issue(s + 4, ids_second, rb);
+    while (true) {
+      step(s, ra);
+      s += 4;
+      if (s >= nsteps) break;
+      step(s, rb);
+      s += 4;
+      if (s >= nsteps) break;
     }
   }
 

@@ -20,7 +20,7 @@ struct ReshapeArgs {
 struct ReshapeInt8Args {
   const void* key;       // [num_tokens][num_kv_heads][head_dim], 16-bit
   const void* value;
-  void* k_codes;         // int8 [num_blocks][block_size][num_kv_heads][head_dim]
+  void* k_codes;         // int8 [num_blocks][num_kv_heads][block_size][head_dim]
   void* v_codes;
   float* k_scales;       // [num_blocks][num_kv_heads][block_size]
   float* v_scales;

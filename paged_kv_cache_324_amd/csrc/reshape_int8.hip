@@ -7,9 +7,11 @@
 // precision as the risk; per-row scales keep every row's error within half a
 // step of that row's own range).
 //
-// Layout: codes int8 [num_blocks][block_size][num_kv_heads][head_dim], scales
-// float32 [num_blocks][num_kv_heads][block_size].  One row is handled by D / 8
-// consecutive lanes, each holding 8 inputs (16 bytes) and writing 8 codes.
+// Layout, head-major within a block: codes int8 [num_blocks][num_kv_heads]
+// [block_size][head_dim], scales float32 [num_blocks][num_kv_heads]
+// [block_size], so one head's rows of a block are one contiguous run.  One row
+// is handled by D / 8 consecutive lanes, each holding 8 inputs (16 bytes) and
+// writing 8 codes.
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(256) void reshape_int8_kernel(ReshapeInt8Args a) {
     const int64_t blk = slot / a.block_size;
     const int off = (int)(slot - blk * a.block_size);
     int8_t* codes = static_cast<int8_t*>(is_v ? a.v_codes : a.k_codes);
-    *reinterpret_cast<uint2*>(codes + (slot * a.num_kv_heads + head) * D + 8 * sub) =
+    *reinterpret_cast<uint2*>(codes + ((blk * a.num_kv_heads + head) * a.block_size + off) * D + 8 * sub) =
         make_uint2(packed[0], packed[1]);
     if (sub == 0) {
       float* scales = is_v ? a.v_scales : a.k_scales;

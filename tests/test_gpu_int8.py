@@ -39,7 +39,7 @@ class Int8Batch:
         dt = torch.bfloat16 if b.dtype == "bf16" else torch.float16
         kr, vr, comp, phys = cached_rows(b)
         NB, BS, Hkv, D = b.NB, b.BS, b.Hkv, b.D
-        self.kc = torch.zeros((NB, BS, Hkv, D), dtype=torch.int8, device="cuda")
+        self.kc = torch.zeros((NB, Hkv, BS, D), dtype=torch.int8, device="cuda")
         self.vc = torch.zeros_like(self.kc)
         self.ks = torch.zeros((NB, Hkv, BS), dtype=torch.float32, device="cuda")
         self.vs = torch.zeros_like(self.ks)
@@ -49,7 +49,7 @@ class Int8Batch:
                                           self.vc, self.ks, self.vs,
                                           torch.from_numpy(np.ascontiguousarray(s)).cuda())
         n = b.k_blocks.shape[0]
-        self.hk = np.zeros((n, BS, Hkv, D), np.int8); self.hv = self.hk.copy()
+        self.hk = np.zeros((n, Hkv, BS, D), np.int8); self.hv = self.hk.copy()
         self.hks = np.zeros((n, Hkv, BS), np.float32); self.hvs = self.hks.copy()
         int8_kv.reshape_and_cache_int8(kr, vr, self.hk, self.hv, self.hks, self.hvs, comp, b.dtype)
         int8_kv.reshape_and_cache_int8(b.key_new, b.value_new, self.hk, self.hv, self.hks, self.hvs,
@@ -102,19 +102,19 @@ def test_reshape_int8_special_rows_and_skipped_slots():
         bits = to_u16(vals, dt)
         tdt = torch.bfloat16 if dt == "bf16" else torch.float16
         slots = np.array([0, 5, 17, 33, -1, NB * BS], np.int64)
-        kc = torch.full((NB, BS, Hkv, D), 99, dtype=torch.int8, device="cuda")
+        kc = torch.full((NB, Hkv, BS, D), 99, dtype=torch.int8, device="cuda")
         vc = kc.clone()
         ks = torch.full((NB, Hkv, BS), -7.0, dtype=torch.float32, device="cuda")
         vs = ks.clone()
         pa_reshape_and_cache_int8(bits_to_device(bits, tdt), bits_to_device(bits, tdt), kc, vc, ks, vs,
                                   torch.from_numpy(slots).cuda())
-        hk = np.full((NB, BS, Hkv, D), 99, np.int8); hv = hk.copy()
+        hk = np.full((NB, Hkv, BS, D), 99, np.int8); hv = hk.copy()
         hks = np.full((NB, Hkv, BS), -7.0, np.float32); hvs = hks.copy()
         int8_kv.reshape_and_cache_int8(bits, bits, hk, hv, hks, hvs, slots, dt)
         torch.cuda.synchronize()
         assert np.array_equal(kc.cpu().numpy(), hk) and np.array_equal(vc.cpu().numpy(), hv)
         assert np.array_equal(ks.cpu().numpy().view(np.uint32), hks.view(np.uint32))
-        assert hk[0, 5, 0, :9].tolist() == [127, 2, 4, -2, -4, 0, 0, 2, 126]
+        assert hk[0, 0, 5, :9].tolist() == [127, 2, 4, -2, -4, 0, 0, 2, 126]
 
 
 # ------------------------------------------------------------------ decode over INT8

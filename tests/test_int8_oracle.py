@@ -61,7 +61,7 @@ def test_codes_rederived_in_float64():
 def _exact_int8_cache(seed, NB, BS, Hkv, D):
     """Codes and power-of-two scales whose products are exact in bf16 (|code| <= 127)."""
     rng = np.random.default_rng(seed)
-    codes = rng.integers(-127, 128, (NB, BS, Hkv, D)).astype(np.int8)
+    codes = rng.integers(-127, 128, (NB, Hkv, BS, D)).astype(np.int8)
     scales = np.ldexp(1.0, rng.integers(-9, -3, (NB, Hkv, BS))).astype(np.float32)
     return codes, scales
 
@@ -70,10 +70,12 @@ def test_decode_equals_16bit_oracle_on_exact_values():
     B, Hq, Hkv, D, BS, NB = 3, 8, 2, 64, 16, 24
     kc, ks = _exact_int8_cache(11, NB, BS, Hkv, D)
     vc, vs = _exact_int8_cache(12, NB, BS, Hkv, D)
-    kbits = to_u16(int8_kv.dequantize(kc, ks.transpose(0, 2, 1)).astype(np.float32), "bf16")
-    vbits = to_u16(int8_kv.dequantize(vc, vs.transpose(0, 2, 1)).astype(np.float32), "bf16")
-    assert np.array_equal(oracle.decode_u16(kbits, "bf16"),
-                          int8_kv.dequantize(kc, ks.transpose(0, 2, 1)))   # exactly representable
+    # the same values in the 16-bit token-major layout [NB][BS][Hkv][D]
+    kf = int8_kv.dequantize(kc, ks).transpose(0, 2, 1, 3)
+    vf = int8_kv.dequantize(vc, vs).transpose(0, 2, 1, 3)
+    kbits = to_u16(kf.astype(np.float32), "bf16")
+    vbits = to_u16(vf.astype(np.float32), "bf16")
+    assert np.array_equal(oracle.decode_u16(kbits, "bf16"), kf)     # exactly representable
     rng = np.random.default_rng(13)
     tables = np.stack([rng.permutation(NB)[:8] for _ in range(B)]).astype(np.int32)
     lens = np.array([1, 77, 128], np.int32)
@@ -87,7 +89,7 @@ def test_reshape_and_cache_int8_writes_slots_and_skips_padding():
     b = make_batch(B=3, Hq=4, Hkv=2, D=64, BS=16, dtype="f16", scale=0.125, seed=20,
                    lens_range=(5, 60))
     NB = b.NB
-    kc = np.zeros((NB, 16, 2, 64), np.int8); vc = kc.copy()
+    kc = np.zeros((NB, 2, 16, 64), np.int8); vc = kc.copy()
     ks = np.full((NB, 2, 16), -1.0, np.float32); vs = ks.copy()
     slots = b.slot_mapping_compact.copy()
     slots[1] = -1
@@ -96,7 +98,7 @@ def test_reshape_and_cache_int8_writes_slots_and_skips_padding():
     for t, s in enumerate(slots):
         if s < 0:
             continue
-        assert np.array_equal(kc[s // 16, s % 16], kq[t])
+        assert np.array_equal(kc[s // 16, :, s % 16], kq[t])
         assert np.array_equal(ks[s // 16, :, s % 16], kscale[t])
     untouched = b.slot_mapping_compact[1]
     assert np.all(ks[untouched // 16, :, untouched % 16] == -1.0)
@@ -118,9 +120,9 @@ def test_pins_catch_planted_mistakes(mutation, monkeypatch):
             return np.trunc(x / s[..., None]).astype(np.int8), s
         monkeypatch.setattr(int8_kv, "quantize_rows", q)
     else:
-        def g(codes, scales, row, L):
-            BS = codes.shape[1]
-            parts = [int8_kv.dequantize(codes[int(row[j])], scales[int(row[j])].reshape(BS, -1))
+        def g(codes, scales, row, L):           # reshape where a transpose is needed
+            Hkv, BS, D = codes.shape[1:]
+            parts = [int8_kv.dequantize(codes[int(row[j])], scales[int(row[j])]).reshape(BS, Hkv, D)
                      for j in range(oracle.blocks_needed(L, BS))]
             return np.concatenate(parts)[:L]
         monkeypatch.setattr(int8_kv, "gather_int8", g)
