@@ -22,6 +22,10 @@ Pinned functions (each pin lives in ``tests/test_oracle.py``):
   +-127, zero rows, half-way ties to even, error at most half a step), a
   float64 re-derivation of each code from its exact rational, and decode on the
   dequantised cache equal to the 16-bit oracle on those values.
+* ``context_parallel`` (shard partials and their merge) -- merged shards equal
+  full-context attention for contiguous and round-robin splits, one shard is the
+  identity, empty shards drop out, the (m, l) scaling freedom, planted mistakes
+  (``tests/test_cp_oracle.py``).
 * ``block_manager`` (the block manager model, imported as
   ``oracle.block_manager``) -- the 63-block example and a content simulation
   with planted mistakes (``tests/test_block_manager.py``).
@@ -50,4 +54,5 @@ from .paged_attention import (  # noqa: F401
     waste_fraction,
 )
 from . import brute_force  # noqa: F401
+from . import context_parallel  # noqa: F401
 from . import int8_kv  # noqa: F401
