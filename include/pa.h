@@ -179,6 +179,57 @@ int pa_decode_step(void* out, const void* q, const void* key, const void* value,
                    size_t workspace_bytes, int dtype, void* stream);
 
 /*
+ * Context parallelism.  A long sequence's context can be split across devices
+ * (page "vllm-ascend architecture", sections 1.1 and 3.1): each device holds
+ * some of the sequence's tokens in its own pool, attends over them, and the
+ * devices' results are merged exactly.  The unit exchanged is a partial row:
+ *
+ *   o   [num_seqs][num_heads][head_dim]  softmax-normalised output over the
+ *                                        shard's keys (same dtype as q)
+ *   ml  [num_seqs][num_heads][2] float32 (m, l): m = the shard's maximum of
+ *                                        scale * q . K_j * log2(e) (or a value
+ *                                        up to 8 below it), l = sum_j
+ *                                        2^(scale * q . K_j * log2(e) - m)
+ *
+ * (m, l) is fixed only up to (m + c, l * 2^-c); l * 2^m is what a consumer
+ * uses.  A shard with no key of a sequence reports (m, l) = (-inf, 0) and a
+ * zero o row.
+ *
+ * pa_decode_partial: pa_decode over the shard's keys (its own block tables and
+ * context lengths, counted in the shard's tokens) writing the partial row
+ * (out = o, out_ml = ml, 8-byte aligned) instead of a final one.  Arguments,
+ * workspace and supported shapes as for pa_decode; out_ml must not be NULL
+ * when num_seqs > 0.
+ */
+int pa_decode_partial(void* out, float* out_ml, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                      const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads,
+                      int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                      int max_context_len, float scale, int partition_size, void* workspace,
+                      size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * pa_merge_partials: merge num_shards partial rows into the attention over the
+ * union of the shards' keys:
+ *   M = max m_n over shards with l_n > 0,  w_n = l_n 2^(m_n - M),
+ *   out = sum_n w_n o_n / sum_n w_n.
+ *
+ *   out        [num_seqs][num_heads][head_dim]             written (dtype)
+ *   out_ml     NULL or [num_seqs][num_heads][2] float32    written: (M, sum_n w_n),
+ *              so merged rows are partial rows again and merges compose
+ *   partial_o  [num_shards][num_seqs][num_heads][head_dim] read (dtype, 4-byte aligned)
+ *   partial_ml [num_shards][num_seqs][num_heads][2]        read (8-byte aligned)
+ *
+ * Shards with l_n <= 0 (or NaN) are left out without reading their o or m into
+ * the arithmetic; a row with no such shard gets zeros and (-inf, 0).  Result
+ * rows are rounded once to dtype.  Supported: head_dim in {64, 128}, dtype
+ * PA_F16 or PA_BF16, any num_shards >= 1.  num_seqs == 0 is a no-op.
+ */
+int pa_merge_partials(void* out, float* out_ml, const void* partial_o, const float* partial_ml,
+                      int num_shards, int num_seqs, int num_heads, int head_dim, int dtype,
+                      void* stream);
+
+/*
  * INT8 KV cache.  KV-cache compression by INT8 quantisation is the next
  * optimisation the pages list (page "Nano-vLLM-Ascend", section 4.3) and the
  * one that raises throughput if the attention scores keep their precision

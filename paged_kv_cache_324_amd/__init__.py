@@ -15,9 +15,11 @@ from ._binding import (  # noqa: F401
     pa_decode,
     pa_decode_int8,
     pa_decode_order,
+    pa_decode_partial,
     pa_decode_partition_hint,
     pa_decode_step,
     pa_decode_workspace_size,
+    pa_merge_partials,
     pa_prefill_chunk,
     pa_reshape_and_cache,
     pa_reshape_and_cache_int8,

@@ -92,6 +92,13 @@ def _declare(lib):
     lib.pa_decode_int8.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int,
                                    c_int, c_int, c_int, c_i64, c_int, c_int, c_f, c_int, c_vp, c_sz,
                                    c_int, c_vp]
+    lib.pa_decode_partial.restype = c_int
+    lib.pa_decode_partial.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int,
+                                      c_int, c_int, c_int, c_i64, c_int, c_int, c_f, c_int, c_vp,
+                                      c_sz, c_int, c_vp]
+    lib.pa_merge_partials.restype = c_int
+    lib.pa_merge_partials.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int,
+                                      c_vp]
     lib.pa_copy_blocks.restype = c_int
     lib.pa_copy_blocks.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_int, c_int, c_int, c_i64, c_int,
                                    c_vp]
@@ -253,6 +260,43 @@ def pa_decode_step(out, q, key, value, slot_mapping, k_cache, v_cache, block_tab
                               B, Hq, Hkv, D, BS, NB, block_tables.shape[1], int(max_context_len),
                               float(scale), int(partition_size), ws_ptr, ws_bytes, dt,
                               _stream(q, stream)))
+    return out
+
+
+def pa_decode_partial(out, out_ml, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                      max_context_len: int, partition_size: int = 0, workspace=None, seq_order=None,
+                      stream=None):
+    """Shard-local decode writing the partial row: normalised ``out [B][Hq][D]`` and float32
+    ``out_ml [B][Hq][2]`` = (log2-domain max, sum) over the shard's keys."""
+    lib, B, Hq, Hkv, D, BS, NB, dt, ws_ptr, ws_bytes, order_ptr = _decode_common(
+        q, k_cache, v_cache, block_tables, context_lens, seq_order, out, max_context_len,
+        partition_size, workspace)
+    if out_ml.shape != (B, Hq, 2):
+        raise ValueError("decode partial: out_ml must be [B][Hq][2]")
+    _check(lib.pa_decode_partial(_dev(out, "out"), _dev(out_ml, "out_ml", torch.float32),
+                                 _dev(q, "q"), k_cache.data_ptr(), v_cache.data_ptr(),
+                                 _dev(block_tables, "block_tables", torch.int32),
+                                 _dev(context_lens, "context_lens", torch.int32), order_ptr,
+                                 B, Hq, Hkv, D, BS, NB, block_tables.shape[1], int(max_context_len),
+                                 float(scale), int(partition_size), ws_ptr, ws_bytes, dt,
+                                 _stream(q, stream)))
+    return out, out_ml
+
+
+def pa_merge_partials(out, partial_o, partial_ml, out_ml=None, stream=None) -> torch.Tensor:
+    """Merge shard partials ``partial_o [N][B][Hq][D]``, ``partial_ml [N][B][Hq][2]`` into
+    ``out [B][Hq][D]`` (and, when given, the merged (max, sum) into ``out_ml [B][Hq][2]``)."""
+    lib = load_library()
+    N, B, Hq, D = partial_o.shape
+    if out.shape != (B, Hq, D) or partial_ml.shape != (N, B, Hq, 2):
+        raise ValueError("merge partials: inconsistent shapes")
+    if out_ml is not None and out_ml.shape != (B, Hq, 2):
+        raise ValueError("merge partials: out_ml must be [B][Hq][2]")
+    dt = _dtype_code(out)
+    ml_ptr = None if out_ml is None else _dev(out_ml, "out_ml", torch.float32)
+    _check(lib.pa_merge_partials(_dev(out, "out"), ml_ptr, _dev(partial_o, "partial_o", out.dtype),
+                                 _dev(partial_ml, "partial_ml", torch.float32), N, B, Hq, D, dt,
+                                 _stream(out, stream)))
     return out
 
 

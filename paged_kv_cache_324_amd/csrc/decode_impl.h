@@ -30,6 +30,11 @@
 // (m_p, l_p); the merge kernel then forms
 //   M = max_p m_p,  w_p = l_p 2^(m_p - M),  out = sum_p w_p o_p / sum_p w_p.
 // Sequences that fit one partition write `out` directly.
+//
+// Partial mode (out_ml set).  Every row also reports its (m, l), the merge
+// writes the merged (M, sum_p w_p), and an empty context gives (-inf, 0), so
+// the rows of several calls over disjoint key sets can be merged afterwards
+// by the same rule (merge_partials.hip).
 #pragma once
 
 #include <type_traits>
@@ -56,6 +61,27 @@ constexpr float kEmptyMax = -1.0e30f;  // finite "no token yet" max: keeps 2^(m 
 __device__ __forceinline__ int clamp_context(const DecodeArgs& a, int seq) {
   const int L = a.context_lens[seq];
   return L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
+}
+
+// A sequence with no context: zero output rows for the G heads of a KV head
+// (and, in partial mode, an empty (max, sum) = (-inf, 0)).
+template <int D, int G>
+__device__ __forceinline__ void write_empty_rows(const DecodeArgs& a, int seq, int h0) {
+  const int64_t row0 = (int64_t)seq * a.num_heads + h0;
+  uint16_t* o = static_cast<uint16_t*>(a.out) + row0 * D;
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) o[idx] = 0;
+  if (a.out_ml && (int)threadIdx.x < G)
+    reinterpret_cast<float2*>(a.out_ml)[row0 + threadIdx.x] = make_float2(-__builtin_inff(), 0.f);
+}
+
+// Where a partition's (max, sum) go: the workspace when the sequence has
+// several partitions, the caller's out_ml in partial mode when it has one,
+// nowhere otherwise.
+__device__ __forceinline__ float2* row_ml_target(const DecodeArgs& a, int nparts_seq, int seq,
+                                                 int h0, int64_t prow) {
+  if (nparts_seq > 1) return reinterpret_cast<float2*>(a.part_ml) + prow;
+  if (a.out_ml) return reinterpret_cast<float2*>(a.out_ml) + (int64_t)seq * a.num_heads + h0;
+  return nullptr;
 }
 
 template <int DT, int D, int BS, int G, int PF, int WAVES_PER_EU, int LOAD_AUX>
@@ -114,10 +140,7 @@ void decode_partition_kernel(const DecodeArgs a) {
   }
   const int L = clamp_context(a, seq);
   if (L == 0) {
-    if (part == 0) {
-      uint16_t* o = static_cast<uint16_t*>(a.out) + ((int64_t)seq * a.num_heads + h0) * D;
-      for (int idx = threadIdx.x; idx < G * D; idx += 256) o[idx] = 0;
-    }
+    if (part == 0) write_empty_rows<D, G>(a, seq, h0);
     return;
   }
   if (t0 >= L) return;
@@ -348,7 +371,8 @@ void decode_partition_kernel(const DecodeArgs a) {
       a.part_out[prow * D + idx] = to_u16<DT>(val);
     }
   }
-  if (nparts_seq > 1 && (int)threadIdx.x < G) {
+  float2* mlp = row_ml_target(a, nparts_seq, seq, h0, prow);
+  if (mlp && (int)threadIdx.x < G) {
     const int g = threadIdx.x;
     float M = s_ml[0][g][0];
 #pragma unroll
@@ -356,7 +380,7 @@ void decode_partition_kernel(const DecodeArgs a) {
     float den = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) den = fmaf(s_ml[w][g][1], fast_exp2(s_ml[w][g][0] - M), den);
-    reinterpret_cast<float2*>(a.part_ml)[prow + g] = make_float2(M, den);
+    mlp[g] = make_float2(M, den);
   }
 }
 
@@ -442,6 +466,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
   const float inv = 1.0f / den;
 #pragma unroll
   for (int e = 0; e < E; ++e) out[e] = to_u16<DT>(acc[e] * inv);
+  if (a.out_ml && lane == 0)
+    reinterpret_cast<float2*>(a.out_ml)[(int64_t)seq * a.num_heads + h] = make_float2(M, den);
 }
 
 template <int DT, int BS, int G>

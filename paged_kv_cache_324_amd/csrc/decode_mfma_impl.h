@@ -103,10 +103,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
 
   const int L = clamp_context(a, seq);
   if (L == 0) {
-    if (part == 0) {
-      uint16_t* o = static_cast<uint16_t*>(a.out) + ((int64_t)seq * a.num_heads + h0) * D;
-      for (int idx = threadIdx.x; idx < G * D; idx += 256) o[idx] = 0;
-    }
+    if (part == 0) write_empty_rows<D, G>(a, seq, h0);
     return;
   }
   if (t0 >= L) return;
@@ -274,7 +271,8 @@ void decode_mfma_kernel(const DecodeArgs a) {
         a.part_out[prow * D + idx] = to_u16<DT>(val);
       }
     }
-    if (nparts_seq > 1 && (int)threadIdx.x < G) {
+    float2* mlp = row_ml_target(a, nparts_seq, seq, h0, prow);
+    if (mlp && (int)threadIdx.x < G) {
       const int g = threadIdx.x;
       float M = s_ml[g * 2];
 #pragma unroll
@@ -283,7 +281,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int w = 0; w < 4; ++w)
         den = fmaf(s_ml[(w * 16 + g) * 2 + 1], fast_exp2(s_ml[(w * 16 + g) * 2] - M), den);
-      reinterpret_cast<float2*>(a.part_ml)[prow + g] = make_float2(M, den);
+      mlp[g] = make_float2(M, den);
     }
   };
 

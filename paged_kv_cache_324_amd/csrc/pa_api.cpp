@@ -228,7 +228,7 @@ struct Int8Scales {
 int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* block_tables, const int32_t* context_lens,
                 const int32_t* seq_order, const NewTokens* nt, const Int8Scales* i8,
-                int num_seqs, int num_heads,
+                float* out_ml, int num_seqs, int num_heads,
                 int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
                 int max_blocks_per_seq, int max_context_len, float scale, int partition_size,
                 void* workspace, size_t workspace_bytes, int dtype, void* stream) {
@@ -249,6 +249,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (nt && (!nt->key || !nt->value || !nt->slot_mapping || !nt->k_cache || !nt->v_cache))
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (i8 && (!i8->k || !i8->v)) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (out_ml && reinterpret_cast<uintptr_t>(out_ml) % 8 != 0)
+    return fail(PA_ERR_INVALID_ARG, "out_ml must be 8-byte aligned");
   const int64_t parts = num_partitions(max_context_len, partition_size);
   const int64_t grid = (int64_t)num_seqs * num_kv_heads * parts;
   if (grid > INT32_MAX || (int64_t)num_seqs * num_heads > INT32_MAX)
@@ -274,6 +276,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.part_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                              align_up(rows * head_dim * sizeof(uint16_t)))
                    : nullptr;
+  a.out_ml = out_ml;
   a.seq_order = seq_order;
   a.key_new = nt ? nt->key : nullptr;
   a.value_new = nt ? nt->value : nullptr;
@@ -311,7 +314,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int64_t num_blocks, int max_blocks_per_seq, int max_context_len, float scale,
               int partition_size, void* workspace, size_t workspace_bytes, int dtype,
               void* stream) {
-  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, seq_order, nullptr, nullptr,
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, seq_order, nullptr, nullptr, nullptr,
                      num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
                      workspace_bytes, dtype, stream);
@@ -325,10 +328,52 @@ int pa_decode_step(void* out, const void* q, const void* key, const void* value,
                    int max_context_len, float scale, int partition_size, void* workspace,
                    size_t workspace_bytes, int dtype, void* stream) {
   NewTokens nt{key, value, slot_mapping, k_cache, v_cache};
-  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, seq_order, &nt, nullptr,
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, seq_order, &nt, nullptr, nullptr,
                      num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
                      workspace_bytes, dtype, stream);
+}
+
+int pa_decode_partial(void* out, float* out_ml, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                      const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads,
+                      int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                      int max_context_len, float scale, int partition_size, void* workspace,
+                      size_t workspace_bytes, int dtype, void* stream) {
+  if (num_seqs > 0 && !out_ml) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, seq_order, nullptr, nullptr,
+                     out_ml, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
+                     workspace_bytes, dtype, stream);
+}
+
+int pa_merge_partials(void* out, float* out_ml, const void* partial_o, const float* partial_ml,
+                      int num_shards, int num_seqs, int num_heads, int head_dim, int dtype,
+                      void* stream) {
+  if (num_shards < 1) return fail(PA_ERR_INVALID_ARG, "num_shards must be >= 1");
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0");
+  if (num_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_heads must be >= 1");
+  if (!supported_head_dim(head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not in {64,128}", head_dim);
+  if (!supported_dtype(dtype)) return fail(PA_ERR_UNSUPPORTED, "dtype %d not PA_F16/PA_BF16", dtype);
+  const int64_t rows = (int64_t)num_seqs * num_heads;
+  if (rows > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "launch grid too large");
+  if (rows == 0) return ok();
+  if (!out || !partial_o || !partial_ml) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (reinterpret_cast<uintptr_t>(partial_ml) % 8 != 0 ||
+      (out_ml && reinterpret_cast<uintptr_t>(out_ml) % 8 != 0))
+    return fail(PA_ERR_INVALID_ARG, "partial_ml and out_ml must be 8-byte aligned");
+  if (reinterpret_cast<uintptr_t>(partial_o) % 4 != 0)
+    return fail(PA_ERR_INVALID_ARG, "partial_o must be 4-byte aligned");
+  pa::MergePartialsArgs a;
+  a.out = out;
+  a.out_ml = out_ml;
+  a.part_o = partial_o;
+  a.part_ml = partial_ml;
+  a.num_rows = rows;
+  a.num_shards = num_shards;
+  return hip_status(pa::launch_merge_partials(a, dtype, head_dim, static_cast<hipStream_t>(stream)),
+                    "merge_partials launch");
 }
 
 int pa_reshape_and_cache_int8(const void* key, const void* value, void* k_codes, void* v_codes,
@@ -372,7 +417,7 @@ int pa_decode_int8(void* out, const void* q, const void* k_codes, const void* v_
                    void* workspace, size_t workspace_bytes, int dtype, void* stream) {
   if (head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "INT8 decode supports head_dim 128 only");
   const Int8Scales i8{k_scales, v_scales};
-  return decode_impl(out, q, k_codes, v_codes, block_tables, context_lens, seq_order, nullptr, &i8,
+  return decode_impl(out, q, k_codes, v_codes, block_tables, context_lens, seq_order, nullptr, &i8, nullptr,
                      num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
                      workspace_bytes, dtype, stream);

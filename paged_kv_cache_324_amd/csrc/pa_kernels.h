@@ -50,6 +50,10 @@ struct DecodeArgs {
   const int32_t* context_lens;
   uint16_t* part_out;  // [num_seqs][num_parts][num_heads][head_dim], partition-normalised, cache dtype
   float* part_ml;      // [num_seqs][num_parts][num_heads][2]: log2-domain max, sum
+  // Partial mode (null otherwise): `out` receives each row's normalised output
+  // and out_ml [num_seqs][num_heads][2] its log2-domain max and sum, so that the
+  // row can later be merged with rows computed over other keys.
+  float* out_ml;
   const int32_t* seq_order;  // optional [num_seqs]: order in which sequences are visited
   // Fused decode step (all null otherwise): this step's token of sequence i is
   // at position context_lens[i] - 1; its K/V rows come from key_new/value_new
@@ -106,6 +110,19 @@ hipError_t launch_decode_f16(const DecodeArgs& a, int head_dim, int block_size, 
                              hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, int head_dim, int block_size, int group,
                               hipStream_t s);
+
+// Merge of partials computed over disjoint key sets (context-parallel shards).
+struct MergePartialsArgs {
+  void* out;               // [num_rows][head_dim], 16-bit
+  float* out_ml;           // optional [num_rows][2]
+  const void* part_o;      // [num_shards][num_rows][head_dim], 16-bit
+  const float* part_ml;    // [num_shards][num_rows][2]
+  int64_t num_rows;        // num_seqs * num_heads
+  int num_shards;
+};
+
+hipError_t launch_merge_partials(const MergePartialsArgs& a, int dtype, int head_dim,
+                                 hipStream_t s);
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int block_size,
                           int group, hipStream_t s);
