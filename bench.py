@@ -247,6 +247,69 @@ def run_decode_int8(pa, torch, b, partition, steps, warmup, dev):
     return {"ms_per_step": ms, "kernel_ms": kernel_ms, "kernel_name": name}
 
 
+def contiguous_shard(b, nshards, s):
+    """Shard s of a context split into nshards contiguous runs of whole blocks: its
+    physical block tables [B][W] (-1 padded) and its per-sequence token counts."""
+    nb = -(-b.context_lens.astype(np.int64) // b.BS)
+    per = -(-nb // nshards)
+    lo, hi = np.minimum(s * per, nb), np.minimum((s + 1) * per, nb)
+    W = max(1, int((hi - lo).max()))
+    tables = np.full((b.B, W), -1, np.int32)
+    lens = np.zeros(b.B, np.int32)
+    for i in range(b.B):
+        tables[i, :hi[i] - lo[i]] = b.block_tables[i, lo[i]:hi[i]]
+        if hi[i] > lo[i]:
+            lens[i] = min(int(b.context_lens[i]), int(hi[i]) * b.BS) - int(lo[i]) * b.BS
+    return tables, lens
+
+
+def run_decode_cp(pa, torch, b, nshards, steps, warmup, dev):
+    """Context-parallel decode as one device of an nshards-way group sees it: the partial
+    decode of its shard (the first, which holds the most tokens) at its real shape, then
+    the merge of all nshards partial rows.  All shards' partials are computed once
+    before timing so the merge reads real rows; the exchange between devices is not
+    part of a one-device step."""
+    d = upload(torch, b, dev)
+    pa.pa_reshape_and_cache(d.key_new, d.value_new, d.k_cache, d.v_cache, d.slot)
+    o = torch.empty((nshards,) + tuple(d.q.shape), dtype=d.q.dtype, device=dev)
+    ml = torch.empty((nshards, b.B, b.Hq, 2), dtype=torch.float32, device=dev)
+    shards = []
+    for s in range(nshards):
+        tables, lens = contiguous_shard(b, nshards, s)
+        mx = max(int(lens.max()), 1)
+        part = pa.pa_decode_partition_hint(b.B, b.Hkv, mx, b.BS)
+        ws = pa.decode_workspace(b.B, b.Hq, b.D, mx, part, dev)
+        shards.append((torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), mx, part,
+                       ws, torch.from_numpy(pa.pa_decode_order(lens)).to(dev), lens))
+        pa.pa_decode_partial(o[s], ml[s], d.q, d.k_cache, d.v_cache, shards[-1][0], shards[-1][1],
+                             b.scale, mx, part, workspace=ws, seq_order=shards[-1][5])
+    tables, lens_d, mx, part, ws, order, lens = shards[0]
+    out = torch.empty_like(d.q)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize(dev)
+
+    def partial():
+        pa.pa_decode_partial(o[0], ml[0], d.q, d.k_cache, d.v_cache, tables, lens_d, b.scale, mx,
+                             part, workspace=ws, seq_order=order, stream=stream)
+
+    def merge():
+        pa.pa_merge_partials(out, o, ml, stream=stream)
+
+    def step():
+        partial()
+        merge()
+
+    for _ in range(warmup):
+        step()
+    ms = _timed(torch, step, steps)
+    shard_bytes = int(lens.astype(np.int64).sum()) * b.Hkv * b.D * 2 * 2
+    merge_bytes = b.B * b.Hq * (nshards * (b.D * 2 + 8) + b.D * 2)
+    return {"ms_per_step": ms, "kernel_ms": _events(torch, partial, steps, stream),
+            "merge_ms": _events(torch, merge, steps, stream), "partition_size": part,
+            "shard_kv_bytes": shard_bytes, "merge_bytes": merge_bytes,
+            "shard_tokens": [int(lens.min()), int(lens.max())]}
+
+
 def run_prefill(pa, torch, b, steps, warmup, dev):
     d = upload(torch, b, dev)
     out = torch.empty_like(d.q)
@@ -284,9 +347,10 @@ def main(argv=None) -> int:
     ap.add_argument("--secondary",
                     default="llama2_70b_decode_bs16,llama2_70b_decode_bs32,long_splitk_decode,"
                             "chunked_prefill,qwen3_0p6b_decode:int8,llama2_70b_decode_bs16:int8,"
-                            "long_splitk_decode:int8",
+                            "long_splitk_decode:int8,long_splitk_decode:cp8",
                     help="comma-separated extra workloads reported beside the headline; "
-                         "a ':int8' suffix runs the workload over an INT8 KV cache")
+                         "a ':int8' suffix runs the workload over an INT8 KV cache, ':cpN' "
+                         "as one device of an N-way context-parallel group")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-kernel-bytes", type=int, default=0,
@@ -374,6 +438,24 @@ def main(argv=None) -> int:
         print(f"[bench] generated {name} in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
               flush=True)
         steps2 = max(5, args.steps // 10)
+        if variant.startswith("cp"):
+            n = int(variant[2:])
+            r2 = run_decode_cp(pa, torch, b2, n, steps2, max(2, args.warmup // 4), dev)
+            kb = r2["shard_kv_bytes"]
+            ach2 = kb / (float(r2["kernel_ms"].mean()) * 1e-3) / 1e9
+            achm = r2["merge_bytes"] / (float(r2["merge_ms"].mean()) * 1e-3) / 1e9
+            kern = "decode_mfma_kernel" if (b2.G >= 4 and b2.D == 128) else "decode_partition_kernel"
+            secondary[entry] = {
+                "step": f"pa_decode_partial (shard 0 of {n}) + pa_merge_partials ({n} shards)",
+                "partition_size": r2["partition_size"], "steps": steps2,
+                "ms_per_step": round(r2["ms_per_step"], 5), "shard_tokens": r2["shard_tokens"],
+                "shard_kv_bytes": kb, "merge_bytes": r2["merge_bytes"],
+                "partial_us": _stats_us(r2["kernel_ms"]), "merge_us": _stats_us(r2["merge_ms"]),
+                "merge_GBps": round(achm, 2),
+                "roofline": {"bound": "hbm", "kernel": f"pa_decode_partial ({kern})",
+                             "achieved": round(ach2, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": round(ach2 / HBM_PEAK_GBPS, 4), "traffic": None}}
+            continue
         if variant == "int8":
             p2 = resolve_partition(pa, c2, b2)
             r2 = run_decode_int8(pa, torch, b2, p2, steps2, max(2, args.warmup // 4), dev)
