@@ -26,9 +26,19 @@ Pinned functions (each pin lives in ``tests/test_oracle.py``):
   full-context attention for contiguous and round-robin splits, one shard is the
   identity, empty shards drop out, the (m, l) scaling freedom, planted mistakes
   (``tests/test_cp_oracle.py``).
+* ``rope`` (rotary embedding fused with the cache write) -- exact quarter turns,
+  equality with complex multiplication by cos + j sin, pair norms, the inverse
+  with -sin (the pages' backward), scores depending on relative position only,
+  the float32 rounding of each product (a case built so a fused multiply-add
+  differs), the 16-bit rounding against brute force, planted mistakes
+  (``tests/test_rope_oracle.py``).
 * ``block_manager`` (the block manager model, imported as
   ``oracle.block_manager``) -- the 63-block example and a content simulation
   with planted mistakes (``tests/test_block_manager.py``).
+
+Reading, not pinned by the pages: the rotary primitive's pairing of dimensions
+(halves, as the Llama/Qwen models the pages serve use; the pages fix only that
+the backward is the same primitive with -sin, which every pairing satisfies).
 
 Parity unpinned: the grouping convention of query heads onto KV heads beyond
 what torch's ``enable_gqa`` fixes (the pages never mention grouped-query
@@ -56,3 +66,4 @@ from .paged_attention import (  # noqa: F401
 from . import brute_force  # noqa: F401
 from . import context_parallel  # noqa: F401
 from . import int8_kv  # noqa: F401
+from . import rope  # noqa: F401

@@ -144,6 +144,15 @@ def to_u16(x: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+def rope_tables(max_position: int, head_dim: int, base: float = 1.0e6):
+    """Rotary tables as a model supplies them: cos and sin of p * base^(-2i/head_dim) for
+    positions p < max_position and pair index i < head_dim / 2, computed in float64 and
+    stored as float32 [max_position][head_dim / 2].  (Qwen3 uses base 1e6.)"""
+    inv_freq = base ** (-np.arange(0, head_dim, 2, dtype=np.float64) / head_dim)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * inv_freq[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
 def _normal_u16(rng: np.random.Generator, shape, dtype: str, chunk: int = 1 << 24) -> np.ndarray:
     """N(0,1) values rounded to ``dtype``; drawn in fixed chunks of 2**24 values."""
     n = int(np.prod(shape))
