@@ -94,6 +94,41 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
                          void* stream);
 
 /*
+ * pa_rope_reshape_and_cache: rotary position embedding fused with
+ * pa_reshape_and_cache.  The pages apply the rotary embedding through a
+ * primitive of (x, cos, sin) whose backward is the same primitive with -sin
+ * (page "Nano-vLLM-Ascend", section 5.1) and name operator fusion as a way to
+ * save passes (page "vLLM-Ascend ...", section 5).  Rotation of a row x at
+ * position p: with h = head_dim / 2, for i < h
+ *   y_i     = x_i c - x_{i+h} s,   y_{i+h} = x_{i+h} c + x_i s,
+ *   c = cos_table[p][i], s = sin_table[p][i],
+ * each product and the sum or difference rounded to float32 separately (no
+ * fused multiply-add) and the result rounded once to dtype, nearest even.
+ *
+ *   q          NULL, or [num_tokens][num_heads][head_dim]   rotated in place
+ *   key, value [num_tokens][num_kv_heads][head_dim]         read
+ *   k_cache, v_cache  as for pa_reshape_and_cache           written at the slots
+ *   positions  [num_tokens] int64                           read
+ *   cos_table, sin_table  float32 [max_position][head_dim/2] read
+ *   slot_mapping [num_tokens] int64                         read
+ *
+ * For each token t with 0 <= positions[t] < max_position: its query rows (if q
+ * is given) are rotated in place; if 0 <= slot_mapping[t] < num_blocks *
+ * block_size, its rotated key rows go to k_cache and its value rows, unchanged,
+ * to v_cache at that slot.  A token with a position outside the table changes
+ * nothing.  q must not overlap the other arrays; all device arrays except
+ * positions and slot_mapping 16-byte aligned.  num_tokens == 0 is a no-op.
+ * Supported: head_dim in {64, 128}, block_size in {16, 32, 256}, dtype PA_F16
+ * or PA_BF16.
+ */
+int pa_rope_reshape_and_cache(void* q, const void* key, const void* value, void* k_cache,
+                              void* v_cache, const int64_t* positions, const float* cos_table,
+                              const float* sin_table, const int64_t* slot_mapping,
+                              int64_t num_tokens, int num_heads, int num_kv_heads, int head_dim,
+                              int block_size, int64_t num_blocks, int64_t max_position, int dtype,
+                              void* stream);
+
+/*
  * Bytes of device workspace pa_decode needs for these sizes (0 when the
  * context fits one partition, i.e. partition_size == 0 or
  * max_context_len <= partition_size).  Pure host arithmetic.

@@ -23,5 +23,6 @@ from ._binding import (  # noqa: F401
     pa_prefill_chunk,
     pa_reshape_and_cache,
     pa_reshape_and_cache_int8,
+    pa_rope_reshape_and_cache,
     pa_version,
 )

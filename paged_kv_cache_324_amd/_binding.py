@@ -92,6 +92,10 @@ def _declare(lib):
     lib.pa_decode_int8.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int,
                                    c_int, c_int, c_int, c_i64, c_int, c_int, c_f, c_int, c_vp, c_sz,
                                    c_int, c_vp]
+    lib.pa_rope_reshape_and_cache.restype = c_int
+    lib.pa_rope_reshape_and_cache.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                              c_i64, c_int, c_int, c_int, c_int, c_i64, c_i64,
+                                              c_int, c_vp]
     lib.pa_decode_partial.restype = c_int
     lib.pa_decode_partial.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int,
                                       c_int, c_int, c_int, c_i64, c_int, c_int, c_f, c_int, c_vp,
@@ -195,6 +199,36 @@ def pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None
     _check(lib.pa_reshape_and_cache(_dev(key, "key"), value.data_ptr(), k_cache.data_ptr(),
                                     v_cache.data_ptr(), _dev(slot_mapping, "slot_mapping", torch.int64),
                                     T, Hkv, D, BS, NB, dt, _stream(key, stream)))
+
+
+def pa_rope_reshape_and_cache(q, key, value, k_cache, v_cache, positions, cos, sin, slot_mapping,
+                              stream=None) -> None:
+    """Rotate keys (and ``q`` in place, if given) by the rotary tables at ``positions`` and
+    write keys and values into caches ``[NB][BS][Hkv][D]`` at ``slot_mapping``."""
+    lib = load_library()
+    T, Hkv, D = key.shape
+    NB, BS, Hkv2, D2 = k_cache.shape
+    if value.shape != key.shape or v_cache.shape != k_cache.shape or (Hkv2, D2) != (Hkv, D):
+        raise ValueError("rope_reshape_and_cache: inconsistent shapes")
+    if positions.shape != (T,) or slot_mapping.shape != (T,):
+        raise ValueError("positions and slot_mapping must be [num_tokens]")
+    if cos.dim() != 2 or cos.shape[1] != D // 2 or sin.shape != cos.shape:
+        raise ValueError("cos/sin must be [max_position][head_dim / 2]")
+    Hq = 0
+    if q is not None:
+        if q.dim() != 3 or q.shape[0] != T or q.shape[2] != D:
+            raise ValueError("q must be [num_tokens][num_heads][head_dim]")
+        Hq = q.shape[1]
+        _dev(q, "q", key.dtype)
+    dt = _dtype_code(key)
+    for n, x in (("value", value), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(x, n, key.dtype)
+    _check(lib.pa_rope_reshape_and_cache(
+        None if q is None else q.data_ptr(), _dev(key, "key"), value.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), _dev(positions, "positions", torch.int64),
+        _dev(cos, "cos", torch.float32), _dev(sin, "sin", torch.float32),
+        _dev(slot_mapping, "slot_mapping", torch.int64), T, Hq, Hkv, D, BS, NB, cos.shape[0], dt,
+        _stream(key, stream)))
 
 
 def _decode_common(q, k_cache, v_cache, block_tables, context_lens, seq_order, out,

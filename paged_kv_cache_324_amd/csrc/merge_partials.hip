@@ -9,10 +9,11 @@
 // l_n = 0 and is left out; its o_n and m_n are never used in arithmetic).  A
 // row that no shard holds keys for gets zeros and (M, sum) = (-inf, 0).
 //
-// One wavefront per row.  Lanes first take the max over shards (lane n looks
-// at shards n, n + 64, ...), then the shards are walked in batches of eight:
-// (m, l) of a shard is one uniform load, each lane owns D/64 consecutive
-// dimensions of o.  The merged (M, sum w) can be written too, so merges
+// One wavefront per row; each lane owns D/64 consecutive dimensions of o.  The
+// first eight shards' outputs and lane n's (m_n, l_n) are loaded in one round;
+// the max and the weights follow by cross-lane operations (shards past 64, if
+// any, are read again one by one), and the shards are summed in batches of
+// eight.  The merged (M, sum w) can be written too, so merges
 // compose (shards of shards).  HBM-bound: num_shards * (D * 2 + 8) bytes read
 // and D * 2 (+ 8) written per row.
 #include <type_traits>
@@ -35,36 +36,47 @@ __global__ __launch_bounds__(64) void merge_partials_kernel(const MergePartialsA
   const RawE* po = reinterpret_cast<const RawE*>(static_cast<const uint16_t*>(a.part_o) + row * D) + lane;
   const int64_t ostride = a.num_rows * (D / E);  // RawE words between shards
 
-  float M = -__builtin_inff();
-  for (int n = lane; n < N; n += 64) {
+  // One round of loads: the first batch of outputs together with every
+  // lane's own (m, l) (shard = lane).
+  RawE pv[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) pv[j] = j < N ? po[j * ostride] : RawE(0);
+  const float2 own = lane < N ? ml[lane * a.num_rows] : make_float2(0.f, 0.f);
+
+  float M = own.y > 0.f ? own.x : -__builtin_inff();
+  for (int n = lane + 64; n < N; n += 64) {  // only with more than 64 shards
     const float2 v = ml[n * a.num_rows];
     if (v.y > 0.f) M = fmaxf(M, v.x);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const bool any = M != -__builtin_inff();
+  // Lane n's weight w_n (shards below 64); shards with l <= 0 (or NaN) weigh 0.
+  const float w_own = (any && own.y > 0.f) ? own.y * fast_exp2(own.x - M) : 0.f;
 
   floatE acc = {};
   float den = 0.f;
-  if (M != -__builtin_inff()) {
-    for (int n0 = 0; n0 < N; n0 += NB) {
-      RawE pv[NB];
-      float w[NB];
+  for (int n0 = 0; any && n0 < N; n0 += NB) {
+    if (n0 > 0) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int n = n0 + j;
-        pv[j] = n < N ? po[n * ostride] : RawE(0);
-        const float2 v = n < N ? ml[n * a.num_rows] : make_float2(0.f, 0.f);
-        w[j] = v.y > 0.f ? v.y * fast_exp2(v.x - M) : 0.f;
+      for (int j = 0; j < NB; ++j) pv[j] = n0 + j < N ? po[(n0 + j) * ostride] : RawE(0);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int n = n0 + j;
+      float w = 0.f;
+      if (n < 64) {
+        w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_own), n));
+      } else if (n < N) {
+        const float2 v = ml[n * a.num_rows];
+        w = v.y > 0.f ? v.y * fast_exp2(v.x - M) : 0.f;
       }
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        if (w[j] > 0.f) {
-          floatE f;
-          f[0] = lo_f32<DT>((uint32_t)pv[j]);
-          if constexpr (E == 2) f[1] = hi_f32<DT>((uint32_t)pv[j]);
-          acc += w[j] * f;
-          den += w[j];
-        }
+      if (n < N && w > 0.f) {
+        floatE f;
+        f[0] = lo_f32<DT>((uint32_t)pv[j]);
+        if constexpr (E == 2) f[1] = hi_f32<DT>((uint32_t)pv[j]);
+        acc += w * f;
+        den += w;
       }
     }
   }

@@ -334,6 +334,51 @@ int pa_decode_step(void* out, const void* q, const void* key, const void* value,
                      workspace_bytes, dtype, stream);
 }
 
+int pa_rope_reshape_and_cache(void* q, const void* key, const void* value, void* k_cache,
+                              void* v_cache, const int64_t* positions, const float* cos_table,
+                              const float* sin_table, const int64_t* slot_mapping,
+                              int64_t num_tokens, int num_heads, int num_kv_heads, int head_dim,
+                              int block_size, int64_t num_blocks, int64_t max_position, int dtype,
+                              void* stream) {
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens must be >= 0");
+  if (num_kv_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
+  if (q && num_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_heads must be >= 1 with q");
+  if (!supported_head_dim(head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not in {64,128}", head_dim);
+  if (!supported_block_size(block_size))
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not in {16,32,256}", block_size);
+  if (!supported_dtype(dtype)) return fail(PA_ERR_UNSUPPORTED, "dtype %d not PA_F16/PA_BF16", dtype);
+  if (num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  if (max_position < 1) return fail(PA_ERR_INVALID_ARG, "max_position must be >= 1");
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !k_cache || !v_cache || !positions || !cos_table || !sin_table ||
+      !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  const void* ptrs[] = {q, key, value, k_cache, v_cache, cos_table, sin_table};
+  for (const void* p : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+      return fail(PA_ERR_INVALID_ARG, "q, key, value, caches and tables must be 16-byte aligned");
+  const int64_t rows = (q ? (int64_t)num_heads : 0) + 2 * (int64_t)num_kv_heads;
+  if (rows * head_dim > INT32_MAX / 2) return fail(PA_ERR_INVALID_ARG, "token rows too large");
+  pa::RopeReshapeArgs a;
+  a.q = q;
+  a.key = key;
+  a.value = value;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.positions = positions;
+  a.cos = cos_table;
+  a.sin = sin_table;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_slots = num_blocks * (int64_t)block_size;
+  a.max_position = max_position;
+  a.num_heads = q ? num_heads : 0;
+  a.num_kv_heads = num_kv_heads;
+  return hip_status(pa::launch_rope_reshape(a, dtype, head_dim, static_cast<hipStream_t>(stream)),
+                    "rope_reshape_and_cache launch");
+}
+
 int pa_decode_partial(void* out, float* out_ml, const void* q, const void* k_cache,
                       const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
                       const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads,

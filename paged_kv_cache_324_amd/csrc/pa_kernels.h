@@ -17,6 +17,23 @@ struct ReshapeArgs {
   int row_chunks;      // 16-byte chunks in one token's num_kv_heads * head_dim row
 };
 
+struct RopeReshapeArgs {
+  void* q;                 // [num_tokens][num_heads][head_dim], rotated in place; or null
+  const void* key;         // [num_tokens][num_kv_heads][head_dim]
+  const void* value;
+  void* k_cache;           // [num_blocks][block_size][num_kv_heads][head_dim]
+  void* v_cache;
+  const int64_t* positions;  // [num_tokens]
+  const float* cos;        // [max_position][head_dim / 2]
+  const float* sin;
+  const int64_t* slot_mapping;
+  int64_t num_tokens;
+  int64_t num_slots;
+  int64_t max_position;
+  int num_heads;
+  int num_kv_heads;
+};
+
 struct ReshapeInt8Args {
   const void* key;       // [num_tokens][num_kv_heads][head_dim], 16-bit
   const void* value;
@@ -98,6 +115,7 @@ struct PrefillArgs {
 };
 
 hipError_t launch_reshape_and_cache(const ReshapeArgs& a, hipStream_t s);
+hipError_t launch_rope_reshape(const RopeReshapeArgs& a, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 hipError_t launch_reshape_int8(const ReshapeInt8Args& a, int dtype, int head_dim, hipStream_t s);
 // INT8 decode: DecodeArgs with k_cache / v_cache pointing at the int8 codes and

@@ -1,0 +1,125 @@
+// rope_reshape_and_cache: rotary position embedding fused with the cache write.
+//
+// The pages apply the rotary embedding through a device primitive taking
+// (x, cos, sin), whose backward is the same primitive with -sin (page
+// "Nano-vLLM-Ascend", section 5.1), and they name operator fusion as the way to
+// save passes over memory (page "vLLM-Ascend ...", section 5).  Here the keys of
+// this step's tokens are rotated on their way into the cache, so the rotated
+// key never makes a round trip through HBM; the queries are rotated in place in
+// the same launch.
+//
+// Rotation: the head dimension is cut into halves, and pair (x_i, x_{i+D/2}) of
+// a token at position p becomes
+//   (x_i c - x_{i+D/2} s,  x_{i+D/2} c + x_i s),  c = cos[p][i], s = sin[p][i],
+// each product and the sum/difference rounded to fp32 on its own (no fused
+// multiply-add), then rounded once to the 16-bit type (nearest even).
+//
+// Work items: per token, every query row, key row and value row is split into
+// D/16 items; item c of a row owns elements [8c, 8c+8) of the first half and
+// the same range of the second half (two 16-byte chunks), so consecutive
+// threads read and write whole contiguous rows.  Value items copy their two
+// chunks to the cache bit for bit.  A token whose position is outside the
+// table changes nothing; a negative or out-of-pool slot skips the cache write
+// (the query is still rotated).
+#include "pa_device.h"
+#include "pa_kernels.h"
+
+namespace pa {
+
+template <int DT>
+__device__ __forceinline__ void rotate8(const u32x4& a, const u32x4& b, const float* cs,
+                                        const float* sn, u32x4& ya, u32x4& yb) {
+#pragma clang fp contract(off)
+  const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+  const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+  uint32_t ra[4], rb[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float x1l = lo_f32<DT>(aw[w]), x1h = hi_f32<DT>(aw[w]);
+    const float x2l = lo_f32<DT>(bw[w]), x2h = hi_f32<DT>(bw[w]);
+    const float cl = cs[2 * w], ch = cs[2 * w + 1], sl = sn[2 * w], sh = sn[2 * w + 1];
+    const float y1l = x1l * cl - x2l * sl, y1h = x1h * ch - x2h * sh;
+    const float y2l = x2l * cl + x1l * sl, y2h = x2h * ch + x1h * sh;
+    ra[w] = pack2<DT>(y1l, y1h);
+    rb[w] = pack2<DT>(y2l, y2h);
+  }
+  ya = u32x4{ra[0], ra[1], ra[2], ra[3]};
+  yb = u32x4{rb[0], rb[1], rb[2], rb[3]};
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(256) void rope_reshape_kernel(RopeReshapeArgs a) {
+  constexpr int P = D / 16;          // items per row
+  constexpr int H2 = D / 2;          // elements per half
+  const int hq = a.q ? a.num_heads : 0;
+  const int rows = hq + 2 * a.num_kv_heads;
+  const int64_t per_token = (int64_t)rows * P;
+  const int64_t total = a.num_tokens * per_token;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
+    const int64_t t = idx / per_token;
+    const int rem = (int)(idx - t * per_token);
+    const int row = rem / P;
+    const int c = rem - row * P;
+    const int64_t pos = a.positions[t];
+    if (pos < 0 || pos >= a.max_position) continue;    // the token is left alone
+    const bool is_q = row < hq;
+    const int kvh = is_q ? 0 : (row - hq) % a.num_kv_heads;
+    const bool is_v = !is_q && row - hq >= a.num_kv_heads;
+    int64_t slot = 0;
+    if (!is_q) {
+      slot = a.slot_mapping[t];
+      if (slot < 0 || slot >= a.num_slots) continue;   // padding token / outside the pool
+    }
+    const int64_t dst_row = (slot * a.num_kv_heads + kvh) * D;     // element offset in a cache
+    if (is_v) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.value) +
+                                                        (t * a.num_kv_heads + kvh) * D);
+      u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.v_cache) + dst_row);
+      __builtin_nontemporal_store(__builtin_nontemporal_load(src + c), dst + c);
+      __builtin_nontemporal_store(__builtin_nontemporal_load(src + P + c), dst + P + c);
+      continue;
+    }
+    const uint16_t* src = is_q ? static_cast<const uint16_t*>(a.q) + (t * hq + row) * D
+                               : static_cast<const uint16_t*>(a.key) + (t * a.num_kv_heads + kvh) * D;
+    const u32x4 x1 = reinterpret_cast<const u32x4*>(src)[c];
+    const u32x4 x2 = reinterpret_cast<const u32x4*>(src + H2)[c];
+    const float4* cp = reinterpret_cast<const float4*>(a.cos + pos * H2 + 8 * c);
+    const float4* sp = reinterpret_cast<const float4*>(a.sin + pos * H2 + 8 * c);
+    const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+    const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    u32x4 y1, y2;
+    rotate8<DT>(x1, x2, cs, sn, y1, y2);
+    if (is_q) {
+      uint16_t* qrow = static_cast<uint16_t*>(a.q) + (t * hq + row) * D;
+      reinterpret_cast<u32x4*>(qrow)[c] = y1;
+      reinterpret_cast<u32x4*>(qrow + H2)[c] = y2;
+    } else {
+      uint16_t* krow = static_cast<uint16_t*>(a.k_cache) + dst_row;
+      __builtin_nontemporal_store(y1, reinterpret_cast<u32x4*>(krow) + c);
+      __builtin_nontemporal_store(y2, reinterpret_cast<u32x4*>(krow + H2) + c);
+    }
+  }
+}
+
+hipError_t launch_rope_reshape(const RopeReshapeArgs& a, int dtype, int head_dim, hipStream_t s) {
+  const int hq = a.q ? a.num_heads : 0;
+  const int64_t total = a.num_tokens * (int64_t)(hq + 2 * a.num_kv_heads) * (head_dim / 16);
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > (1 << 20)) blocks = 1 << 20;
+  const dim3 grid((unsigned)blocks), block(256);
+  if (dtype == DT_BF16) {
+    if (head_dim == 128) hipLaunchKernelGGL((rope_reshape_kernel<DT_BF16, 128>), grid, block, 0, s, a);
+    else if (head_dim == 64) hipLaunchKernelGGL((rope_reshape_kernel<DT_BF16, 64>), grid, block, 0, s, a);
+    else return hipErrorInvalidValue;
+  } else {
+    if (head_dim == 128) hipLaunchKernelGGL((rope_reshape_kernel<DT_F16, 128>), grid, block, 0, s, a);
+    else if (head_dim == 64) hipLaunchKernelGGL((rope_reshape_kernel<DT_F16, 64>), grid, block, 0, s, a);
+    else return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa
