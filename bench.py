@@ -310,6 +310,42 @@ def run_decode_cp(pa, torch, b, nshards, steps, warmup, dev):
             "shard_tokens": [int(lens.min()), int(lens.max())]}
 
 
+def rope_bytes(b) -> int:
+    """Algorithmic bytes of the fused rotary step over the workload's new tokens: queries
+    read and written, keys and values read and written to the cache, and one cos and one
+    sin row (float32, head_dim / 2) per token."""
+    T = len(b.slot_mapping)
+    return T * (b.Hq * b.D * 2 * 2 + b.Hkv * b.D * 2 * 4 + b.D // 2 * 4 * 2)
+
+
+def run_rope(pa, torch, b, steps, warmup, dev):
+    """pa_rope_reshape_and_cache over the workload's new tokens at their positions (queries
+    rotated in place), beside the plain pa_reshape_and_cache of the same tokens."""
+    from workloads import rope_tables
+    d = upload(torch, b, dev)
+    T = len(b.slot_mapping)
+    pos = np.concatenate([np.arange(int(L) - int(n), int(L))
+                          for L, n in zip(b.context_lens, b.n_new)]).astype(np.int64)
+    cos, sin = rope_tables(int(pos.max()) + 1, b.D)
+    cos_d, sin_d = torch.from_numpy(cos).to(dev), torch.from_numpy(sin).to(dev)
+    pos_d = torch.from_numpy(pos).to(dev)
+    q = d.q if d.q.shape[0] == T else torch.zeros((T, b.Hq, b.D), dtype=d.q.dtype, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def fused():
+        pa.pa_rope_reshape_and_cache(q, d.key_new, d.value_new, d.k_cache, d.v_cache, pos_d, cos_d,
+                                     sin_d, d.slot, stream=stream)
+
+    def plain():
+        pa.pa_reshape_and_cache(d.key_new, d.value_new, d.k_cache, d.v_cache, d.slot, stream=stream)
+
+    for _ in range(warmup):
+        fused()
+    ms = _timed(torch, fused, steps)
+    return {"ms_per_step": ms, "kernel_ms": _events(torch, fused, steps, stream),
+            "plain_ms": _events(torch, plain, steps, stream), "tokens": T}
+
+
 def run_prefill(pa, torch, b, steps, warmup, dev):
     d = upload(torch, b, dev)
     out = torch.empty_like(d.q)
@@ -347,10 +383,12 @@ def main(argv=None) -> int:
     ap.add_argument("--secondary",
                     default="llama2_70b_decode_bs16,llama2_70b_decode_bs32,long_splitk_decode,"
                             "chunked_prefill,qwen3_0p6b_decode:int8,llama2_70b_decode_bs16:int8,"
-                            "long_splitk_decode:int8,long_splitk_decode:cp8",
+                            "long_splitk_decode:int8,long_splitk_decode:cp8,chunked_prefill:rope,"
+                            "qwen3_0p6b_decode:rope",
                     help="comma-separated extra workloads reported beside the headline; "
                          "a ':int8' suffix runs the workload over an INT8 KV cache, ':cpN' "
-                         "as one device of an N-way context-parallel group")
+                         "as one device of an N-way context-parallel group, ':rope' times the "
+                         "fused rotary embedding + cache write of its new tokens")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-kernel-bytes", type=int, default=0,
@@ -453,6 +491,20 @@ def main(argv=None) -> int:
                 "partial_us": _stats_us(r2["kernel_ms"]), "merge_us": _stats_us(r2["merge_ms"]),
                 "merge_GBps": round(achm, 2),
                 "roofline": {"bound": "hbm", "kernel": f"pa_decode_partial ({kern})",
+                             "achieved": round(ach2, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": round(ach2 / HBM_PEAK_GBPS, 4), "traffic": None}}
+            continue
+        if variant == "rope":
+            r2 = run_rope(pa, torch, b2, max(20, steps2), max(2, args.warmup // 4), dev)
+            rb = rope_bytes(b2)
+            ach2 = rb / (float(r2["kernel_ms"].mean()) * 1e-3) / 1e9
+            secondary[entry] = {
+                "step": "pa_rope_reshape_and_cache (queries rotated in place, keys rotated into "
+                        "the cache, values copied)", "tokens": r2["tokens"],
+                "ms_per_step": round(r2["ms_per_step"], 5), "algorithmic_bytes": rb,
+                "rope_us": _stats_us(r2["kernel_ms"]),
+                "plain_reshape_and_cache_us": _stats_us(r2["plain_ms"]),
+                "roofline": {"bound": "hbm", "kernel": "rope_reshape_kernel",
                              "achieved": round(ach2, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                              "frac": round(ach2 / HBM_PEAK_GBPS, 4), "traffic": None}}
             continue
