@@ -1,0 +1,85 @@
+"""Decode at the extremes of its supported sizes: a 128k-token context on one sequence, a
+batch of thousands of short sequences, and the INT8 and context-parallel paths at the long
+end, against the CPU oracle on sampled rows, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import context_parallel as cp
+from paged_kv_cache_324_amd import (pa_decode, pa_decode_partial, pa_decode_partition_hint,
+                                    pa_merge_partials, pa_reshape_and_cache)
+from workloads import make_batch
+
+from _gpu import check_close, host_caches_after_write, log, to_f64, upload
+from _shards import split_context
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode(b, d, partition):
+    pa_reshape_and_cache(d.key_new, d.value_new, d.k_cache, d.v_cache, d.slot_mapping)
+    out = torch.empty_like(d.q)
+    pa_decode(out, d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, b.scale,
+              b.max_context_len, partition)
+    torch.cuda.synchronize()
+    return to_f64(out)
+
+
+@pytest.mark.parametrize("G,partition", [(8, "hint"), (8, 0), (1, "hint"), (4, 2048)])
+def test_128k_context(G, partition):
+    """One sequence of 131072 tokens (512 blocks of 256) beside short ones; with the hint the
+    long context is cut into hundreds of partitions, unsplit one workgroup walks it all."""
+    lens = [131072, 1, 300, 70000]
+    b = make_batch(B=4, Hq=G, Hkv=1, D=128, BS=256, dtype="bf16", scale=128 ** -0.5,
+                   seed=9950 + G, lens=lens)
+    p = pa_decode_partition_hint(b.B, b.Hkv, b.max_context_len, b.BS) if partition == "hint" \
+        else partition
+    log(f"128k context: G={G} partition={p}")
+    got = _decode(b, upload(b), p)
+    kc, vc = host_caches_after_write(b)
+    ref = oracle.paged_decode(b.q, kc, vc, b.block_tables_compact, b.context_lens, b.scale, b.dtype)
+    mx, rel = check_close(got, ref, f"128k G{G} p{p}")
+    log(f"  max_abs={mx:.3e} rel_l2={rel:.3e}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 8])
+def test_thousands_of_sequences(G):
+    """4096 sequences of 1-64 tokens (up to 4 blocks each, block 16): 8192+ workgroups."""
+    b = make_batch(B=4096, Hq=2 * G, Hkv=2, D=128, BS=16, dtype="f16", scale=128 ** -0.5,
+                   seed=9960 + G, lens_range=(1, 64))
+    got = _decode(b, upload(b), 0)
+    rows = np.sort(np.random.default_rng(G).choice(b.B, 96, replace=False))
+    kc, vc = host_caches_after_write(b)
+    ref = oracle.paged_decode(b.q[rows], kc, vc, b.block_tables_compact[rows], b.context_lens[rows],
+                              b.scale, b.dtype)
+    check_close(got[rows], ref, f"4096 sequences G{G}")
+    assert np.all(np.isfinite(got))
+
+
+def test_context_parallel_128k_over_16_shards():
+    """The 128k context split round robin over 16 shards, merged; against full attention."""
+    b = make_batch(B=2, Hq=8, Hkv=1, D=128, BS=256, dtype="bf16", scale=128 ** -0.5, seed=9970,
+                   lens=[131072, 5000])
+    d = upload(b)
+    pa_reshape_and_cache(d.key_new, d.value_new, d.k_cache, d.v_cache, d.slot_mapping)
+    shards = split_context(b, 16, "round_robin")
+    o = torch.empty((16, b.B, b.Hq, b.D), dtype=d.q.dtype, device="cuda")
+    ml = torch.empty((16, b.B, b.Hq, 2), dtype=torch.float32, device="cuda")
+    for n, (_, tp, lens) in enumerate(shards):
+        mx = max(int(lens.max()), 1)
+        pa_decode_partial(o[n], ml[n], d.q, d.k_cache, d.v_cache, torch.from_numpy(tp).cuda(),
+                          torch.from_numpy(lens).cuda(), b.scale, mx,
+                          pa_decode_partition_hint(b.B, b.Hkv, mx, b.BS))
+    out = torch.empty_like(d.q)
+    pa_merge_partials(out, o, ml)
+    torch.cuda.synchronize()
+    kc, vc = host_caches_after_write(b)
+    ref = oracle.paged_decode(b.q, kc, vc, b.block_tables_compact, b.context_lens, b.scale, b.dtype)
+    check_close(to_f64(out), ref, "128k over 16 shards")
+    # the merged (m, l) of one shard row reproduces that shard's log-sum-exp
+    tc, _, lens = shards[5]
+    _, rm, rl = cp.shard_partial(b.q, kc, vc, tc, lens, b.scale, b.dtype)
+    g = ml[5].cpu().numpy().astype(np.float64)
+    lse = g[..., 0] + np.log2(g[..., 1])
+    assert np.abs(lse - (rm + np.log2(rl))).max() < 2e-3
