@@ -11,17 +11,24 @@
 
 namespace pa {
 
+// One workgroup per group of tokens: TPB = max(1, 256 / per_token) tokens of
+// per_token = 2 row_chunks 16-byte chunks each (K row then V row); when a
+// token has more than 256 chunks its workgroup loops over them.  The slot is
+// read once per token and every index is 32-bit within the workgroup.
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(ReshapeArgs a) {
-  const int64_t per_token = 2 * (int64_t)a.row_chunks;
-  const int64_t total = a.num_tokens * per_token;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
-    const int64_t t = idx / per_token;
-    const int rem = (int)(idx - t * per_token);
-    const bool is_v = rem >= a.row_chunks;
-    const int chunk = is_v ? rem - a.row_chunks : rem;
+  const int per_token = 2 * a.row_chunks;
+  const int tpb = per_token >= 256 ? 1 : 256 / per_token;
+  const int64_t tbase = (int64_t)blockIdx.x * tpb;
+  const int span = tpb * per_token;
+  for (int local = threadIdx.x; local < span; local += 256) {
+    const int lt = local / per_token;
+    const int rem = local - lt * per_token;
+    const int64_t t = tbase + lt;
+    if (t >= a.num_tokens) break;
     const int64_t slot = a.slot_mapping[t];
     if (slot < 0 || slot >= a.num_slots) continue;  // padding token / outside the pool
+    const bool is_v = rem >= a.row_chunks;
+    const int chunk = is_v ? rem - a.row_chunks : rem;
     const u32x4* src = reinterpret_cast<const u32x4*>(is_v ? a.value : a.key) +
                        t * a.row_chunks + chunk;
     u32x4* dst = reinterpret_cast<u32x4*>(is_v ? a.v_cache : a.k_cache) +
@@ -31,10 +38,11 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(ReshapeArgs a) {
 }
 
 hipError_t launch_reshape_and_cache(const ReshapeArgs& a, hipStream_t s) {
-  const int64_t total = a.num_tokens * 2 * (int64_t)a.row_chunks;
-  if (total == 0) return hipSuccess;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > (1 << 20)) blocks = 1 << 20;
+  if (a.num_tokens == 0) return hipSuccess;
+  const int per_token = 2 * a.row_chunks;
+  const int64_t tpb = per_token >= 256 ? 1 : 256 / per_token;
+  const int64_t blocks = (a.num_tokens + tpb - 1) / tpb;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -17,8 +17,8 @@
 // Work items: per token, every query row, key row and value row is split into
 // D/16 items; item c of a row owns elements [8c, 8c+8) of the first half and
 // the same range of the second half (two 16-byte chunks), so consecutive
-// threads read and write whole contiguous rows.  Value items copy their two
-// chunks to the cache bit for bit.  A token whose position is outside the
+// threads read and write whole contiguous rows; one workgroup per token.
+// Value items copy their two chunks to the cache bit for bit.  A token whose position is outside the
 // table changes nothing; a negative or out-of-pool slot skips the cache write
 // (the query is still rotated).
 #include "pa_device.h"
@@ -47,30 +47,31 @@ __device__ __forceinline__ void rotate8(const u32x4& a, const u32x4& b, const fl
   yb = u32x4{rb[0], rb[1], rb[2], rb[3]};
 }
 
+// One workgroup per token (blockDim = its item count rounded up to whole
+// wavefronts, at most 1024; a token with more items loops).  The token's
+// position and slot are read once, as scalars.
 template <int DT, int D>
-__global__ __launch_bounds__(256) void rope_reshape_kernel(RopeReshapeArgs a) {
+__global__ __launch_bounds__(1024) void rope_reshape_kernel(RopeReshapeArgs a) {
   constexpr int P = D / 16;          // items per row
   constexpr int H2 = D / 2;          // elements per half
+  const int64_t t = blockIdx.x;
+  const int64_t pos = a.positions[t];
+  if (pos < 0 || pos >= a.max_position) return;    // the token is left alone
   const int hq = a.q ? a.num_heads : 0;
-  const int rows = hq + 2 * a.num_kv_heads;
-  const int64_t per_token = (int64_t)rows * P;
-  const int64_t total = a.num_tokens * per_token;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
-    const int64_t t = idx / per_token;
-    const int rem = (int)(idx - t * per_token);
-    const int row = rem / P;
-    const int c = rem - row * P;
-    const int64_t pos = a.positions[t];
-    if (pos < 0 || pos >= a.max_position) continue;    // the token is left alone
+  const int items = (hq + 2 * a.num_kv_heads) * P;
+  const int64_t slot_raw = a.slot_mapping[t];
+  const bool cache_ok = slot_raw >= 0 && slot_raw < a.num_slots;  // else padding / outside the pool
+  const int64_t slot = cache_ok ? slot_raw : 0;
+  const float* cos_row = a.cos + pos * H2;
+  const float* sin_row = a.sin + pos * H2;
+  for (int it = threadIdx.x; it < items; it += blockDim.x) {
+    const int row = it / P;
+    const int c = it - row * P;
     const bool is_q = row < hq;
-    const int kvh = is_q ? 0 : (row - hq) % a.num_kv_heads;
-    const bool is_v = !is_q && row - hq >= a.num_kv_heads;
-    int64_t slot = 0;
-    if (!is_q) {
-      slot = a.slot_mapping[t];
-      if (slot < 0 || slot >= a.num_slots) continue;   // padding token / outside the pool
-    }
+    if (!is_q && !cache_ok) continue;
+    const int kr = row - hq;                           // key rows, then value rows
+    const bool is_v = kr >= a.num_kv_heads;
+    const int kvh = is_v ? kr - a.num_kv_heads : kr;
     const int64_t dst_row = (slot * a.num_kv_heads + kvh) * D;     // element offset in a cache
     if (is_v) {
       const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.value) +
@@ -84,8 +85,8 @@ __global__ __launch_bounds__(256) void rope_reshape_kernel(RopeReshapeArgs a) {
                                : static_cast<const uint16_t*>(a.key) + (t * a.num_kv_heads + kvh) * D;
     const u32x4 x1 = reinterpret_cast<const u32x4*>(src)[c];
     const u32x4 x2 = reinterpret_cast<const u32x4*>(src + H2)[c];
-    const float4* cp = reinterpret_cast<const float4*>(a.cos + pos * H2 + 8 * c);
-    const float4* sp = reinterpret_cast<const float4*>(a.sin + pos * H2 + 8 * c);
+    const float4* cp = reinterpret_cast<const float4*>(cos_row + 8 * c);
+    const float4* sp = reinterpret_cast<const float4*>(sin_row + 8 * c);
     const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
     const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
     const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
@@ -104,12 +105,12 @@ __global__ __launch_bounds__(256) void rope_reshape_kernel(RopeReshapeArgs a) {
 }
 
 hipError_t launch_rope_reshape(const RopeReshapeArgs& a, int dtype, int head_dim, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  if (a.num_tokens > INT32_MAX) return hipErrorInvalidValue;
   const int hq = a.q ? a.num_heads : 0;
-  const int64_t total = a.num_tokens * (int64_t)(hq + 2 * a.num_kv_heads) * (head_dim / 16);
-  if (total == 0) return hipSuccess;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > (1 << 20)) blocks = 1 << 20;
-  const dim3 grid((unsigned)blocks), block(256);
+  const int64_t items = (int64_t)(hq + 2 * a.num_kv_heads) * (head_dim / 16);
+  const int threads = (int)(items >= 1024 ? 1024 : (items + 63) / 64 * 64);
+  const dim3 grid((unsigned)a.num_tokens), block(threads);
   if (dtype == DT_BF16) {
     if (head_dim == 128) hipLaunchKernelGGL((rope_reshape_kernel<DT_BF16, 128>), grid, block, 0, s, a);
     else if (head_dim == 64) hipLaunchKernelGGL((rope_reshape_kernel<DT_BF16, 64>), grid, block, 0, s, a);
