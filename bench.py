@@ -157,7 +157,7 @@ def resolve_partition(pa, cfg, b):
     return pa.pa_decode_partition_hint(b.B, b.Hkv, b.max_context_len, b.BS)
 
 
-def run_decode(pa, torch, b, partition, steps, warmup, unfused, dev):
+def run_decode(pa, torch, b, partition, steps, warmup, unfused, dev, cold_iters=0):
     d = upload(torch, b, dev)
     out = torch.empty_like(d.q)
     workspace = pa.decode_workspace(b.B, b.Hq, b.D, b.max_context_len, partition, dev)
@@ -184,13 +184,24 @@ def run_decode(pa, torch, b, partition, steps, warmup, unfused, dev):
         step()
     ms = _timed(torch, step, steps)                       # the timed region
     kernel_ms = _events(torch, decode if unfused else step, steps, stream)
+    # Cold calls: a 1 GiB read (four times the 256 MB Infinity Cache) before
+    # each one, so no K/V byte is served from the MALL or an L2, and no dirty
+    # line is left to be written back during the call; only the call is timed.
+    cold = []
+    if cold_iters > 0:
+        flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        for _ in range(cold_iters):
+            flush.sum()
+            cold.append(float(_events(torch, decode if unfused else step, 1, stream)[0]))
+        del flush
     # The library runs the matrix-core kernel for 4+ query heads per KV head at
     # head_dim 128, the vector kernel otherwise.
     kern = "decode_mfma_kernel" if (b.G >= 4 and b.D == 128) else "decode_partition_kernel"
     name = ("pa_decode" if unfused else "pa_decode_step") + (
         f" ({kern} + merge kernel)" if partition and b.max_context_len > partition else
         f" (one {kern} launch)")
-    return {"ms_per_step": ms, "kernel_ms": kernel_ms, "kernel_name": name}
+    return {"ms_per_step": ms, "kernel_ms": kernel_ms, "kernel_name": name,
+            "cold_ms": np.array(cold)}
 
 
 def int8_kv_bytes(b) -> int:
@@ -434,7 +445,8 @@ def main(argv=None) -> int:
     print(f"[bench] generated {args.workload} in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
           flush=True)
     partition = resolve_partition(pa, cfg, b) if args.partition is None else args.partition
-    r = run_decode(pa, torch, b, partition, args.steps, args.warmup, args.unfused, dev)
+    r = run_decode(pa, torch, b, partition, args.steps, args.warmup, args.unfused, dev,
+                   cold_iters=20)
     kv = b.kv_bytes()
     value = kv / (r["ms_per_step"] * 1e-3) / 1e9
     achieved = kv / (float(r["kernel_ms"].mean()) * 1e-3) / 1e9
@@ -462,6 +474,8 @@ def main(argv=None) -> int:
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "seqs_per_s": round(b.B / (r["ms_per_step"] * 1e-3), 1),
         "decode_us": _stats_us(r["kernel_ms"]),
+        "decode_cold_us": _stats_us(r["cold_ms"]),
+        "cold_GBps_p50": round(kv / (float(np.median(r["cold_ms"])) * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "kernel": r["kernel_name"],
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -533,6 +547,9 @@ def main(argv=None) -> int:
                 "steps": steps2, "ms_per_step": round(r2["ms_per_step"], 5),
                 "prefill_us": _stats_us(r2["kernel_ms"]),
                 "reshape_and_cache_us": _stats_us(r2["reshape_ms"]),
+                "reshape_and_cache_GBps": round(
+                    2 * 2 * len(b2.slot_mapping) * b2.Hkv * b2.D * 2
+                    / (float(np.median(r2["reshape_ms"])) * 1e-3) / 1e9, 1),
                 "algorithmic_gflop": round(flops / 1e9, 2),
                 "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tfl, 2),
                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
