@@ -178,3 +178,78 @@ def test_bench_refuses_several_gpus():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0 and "one GPU" in r.stderr
+
+
+def test_new_entry_points_have_bindings():
+    for name in ("pa_decode_partial", "pa_merge_partials", "pa_rope_reshape_and_cache",
+                 "pa_decode_int8", "pa_reshape_and_cache_int8", "pa_copy_blocks",
+                 "pa_decode_partition_hint"):
+        assert callable(getattr(pa, name)), name
+
+
+def test_decode_partial_rejects_bad_arguments(lib):
+    f = lib.pa_decode_partial
+    base = [P, P, P, P, P, P, P, None, 2, 16, 8, 128, 16, 100, 10, 160, 0.1, 0, None, 0,
+            pa.PA_BF16, None]
+    bad = list(base)
+    bad[1] = None                          # out_ml
+    assert f(*bad) == -1 and "null" in lib.pa_last_error().decode()
+    bad = list(base)
+    bad[1] = ctypes.c_void_p(0x1004)       # out_ml not 8-byte aligned
+    assert f(*bad) == -1 and "aligned" in lib.pa_last_error().decode()
+    bad = list(base)
+    bad[11] = 96                           # head_dim
+    assert f(*bad) == -2
+    bad = list(base)
+    bad[17] = 32                           # needs a workspace
+    assert f(*bad) == -3
+    empty = list(base)
+    empty[0] = empty[1] = None
+    empty[8] = 0                           # no sequences: nothing to do
+    assert f(*empty) == 0
+
+
+@pytest.mark.parametrize("index,value,code", [
+    (4, 0, -1),                            # num_shards
+    (5, -1, -1),                           # num_seqs
+    (6, 0, -1),                            # num_heads
+    (7, 80, -2),                           # head_dim
+    (8, 5, -2),                            # dtype
+    (0, None, -1),                         # out
+    (3, ctypes.c_void_p(0x1004), -1),      # partial_ml alignment
+    (2, ctypes.c_void_p(0x1002), -1),      # partial_o alignment
+    (1, ctypes.c_void_p(0x1004), -1),      # out_ml alignment
+])
+def test_merge_partials_rejects_bad_arguments(lib, index, value, code):
+    args = [P, None, P, P, 4, 2, 16, 128, pa.PA_BF16, None]
+    args[index] = value
+    assert lib.pa_merge_partials(*args) == code
+
+
+def test_merge_partials_empty_batch_is_a_noop(lib):
+    assert lib.pa_merge_partials(None, None, None, None, 4, 0, 16, 128, pa.PA_BF16, None) == 0
+
+
+@pytest.mark.parametrize("index,value,code", [
+    (10, 0, -1),                           # q given with num_heads 0
+    (1, None, -1),                         # key
+    (5, None, -1),                         # positions
+    (12, 96, -2),                          # head_dim
+    (13, 8, -2),                           # block_size
+    (15, 0, -1),                           # max_position
+    (6, ctypes.c_void_p(0x1004), -1),      # cos table alignment
+    (9, -1, -1),                           # num_tokens
+    (16, 9, -2),                           # dtype
+])
+def test_rope_rejects_bad_arguments(lib, index, value, code):
+    args = [P, P, P, P, P, P, P, P, P, 4, 16, 8, 128, 16, 100, 4096, pa.PA_BF16, None]
+    args[index] = value
+    assert lib.pa_rope_reshape_and_cache(*args) == code
+
+
+def test_rope_without_tokens_or_queries(lib):
+    f = lib.pa_rope_reshape_and_cache
+    assert f(None, None, None, None, None, None, None, None, None, 0, 0, 8, 128, 16, 100, 10,
+             pa.PA_F16, None) == 0
+    # no queries: num_heads is ignored, a bad key still rejected
+    assert f(None, None, P, P, P, P, P, P, P, 4, 0, 8, 128, 16, 100, 10, pa.PA_F16, None) == -1
