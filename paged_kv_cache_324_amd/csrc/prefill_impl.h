@@ -30,7 +30,10 @@
 // order, which leaves the sum unchanged.
 //
 // Softmax statistics are fp32 (page "vLLM-Ascend ...", section 3.1, problem
-// 2); the probabilities are rounded to the input dtype for the PV product.
+// 2); the probabilities are rounded to the input dtype for the PV product.  The
+// row sum is one more MFMA per 16-key step, ones^T P^T accumulated in fp32: it
+// sums exactly the rounded probabilities the numerator uses and takes the
+// additions off the vector ALU (the matrix cores have the spare cycles).
 #pragma once
 
 #include "mfma.h"
@@ -161,7 +164,10 @@ void prefill_kernel(const PrefillArgs a) {
   f32x16 o[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
-  float m = kPrefillEmptyMax, lsum = 0.f;
+  float m = kPrefillEmptyMax;
+  f32x16 lacc = f32x16{};  // row sums of the rounded P, every row of the lane's column
+  const uint32_t one2 = pack2<DT>(1.f, 1.f);
+  const u32x4 ones = {one2, one2, one2, one2};
 
   // ---- staging: wavefront w moves keys kv0 + 16 w .. + 15 (one block) of K
   // and of V with four 1 KB buffer loads each; lane l of load i brings key row
@@ -264,22 +270,15 @@ void prefill_kernel(const PrefillArgs a) {
       const float m_new = fmaxf(m, mx);
       const float alpha = fast_exp2(m - m_new);
       m = m_new;
-      lsum *= alpha;
+      lacc *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
     }
-    float psum = 0.f;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float p = fast_exp2(fmaf(s[sub][j], a.scale_log2, -m));
-        s[sub][j] = p;
-        psum += p;
-      }
+      for (int j = 0; j < 16; ++j) s[sub][j] = fast_exp2(fmaf(s[sub][j], a.scale_log2, -m));
     }
-    psum += __shfl_xor(psum, 32);
-    lsum += psum;
     __builtin_amdgcn_s_setprio(1);
     // ---- O^T += V^T P^T over the tile's four 16-key steps
 #pragma unroll
@@ -288,6 +287,7 @@ void prefill_kernel(const PrefillArgs a) {
       const int jb = 8 * (kk & 1);
       const u32x4 pf = {pack2<DT>(ps[jb + 0], ps[jb + 1]), pack2<DT>(ps[jb + 2], ps[jb + 3]),
                         pack2<DT>(ps[jb + 4], ps[jb + 5]), pack2<DT>(ps[jb + 6], ps[jb + 7])};
+      lacc = mfma32x32x16<DT>(ones, pf, lacc);
       const int r1 = 16 * kk + 4 * half + (p16 >> 2);
       const int r2 = r1 + 8;
 #pragma unroll
@@ -330,6 +330,7 @@ void prefill_kernel(const PrefillArgs a) {
 
   // ---- normalise and store: lane holds dims 32 dt + 8 (j/4) + 4 half + (j%4)
   if (!row_valid) return;
+  const float lsum = lacc[0];
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;  // no visible key: zero row
   uint16_t* op = static_cast<uint16_t*>(a.out) + ((int64_t)(s0 + t) * a.num_heads + h) * D;
 #pragma unroll
