@@ -408,8 +408,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the decode path shards by sequence or KV head with no exchange, see DESIGN.md",
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); decode shards "
+              "by sequence or KV head with no exchange, so N GPUs run N independent batches",
               file=sys.stderr)
         return 2
 
