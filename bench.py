@@ -40,25 +40,32 @@ KERNEL_SOURCES = ["paged_kv_cache_324_amd/csrc/decode_impl.h",
                   "paged_kv_cache_324_amd/csrc/decode_mfma_impl.h",
                   "paged_kv_cache_324_amd/csrc/mfma.h",
                   "paged_kv_cache_324_amd/csrc/pa_device.h"]
+# Sources of the INT8 decode kernel (its merge is the 16-bit one).
+KERNEL_SOURCES_INT8 = ["paged_kv_cache_324_amd/csrc/decode_int8.hip",
+                       "paged_kv_cache_324_amd/csrc/decode_impl.h",
+                       "paged_kv_cache_324_amd/csrc/mfma.h",
+                       "paged_kv_cache_324_amd/csrc/pa_device.h"]
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(sources=None) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in (KERNEL_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str, partition: int):
+def recorded_traffic(workload: str, partition: int, int8: bool = False):
     """HBM bytes per decode launch from the committed counter summary, if it is current."""
-    path = os.path.join(PROFILES, f"decode_{workload}_p{partition}_counters.md")
+    tag = "_int8" if int8 else ""
+    path = os.path.join(PROFILES, f"decode_{workload}{tag}_p{partition}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     sha = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", text)
     val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not sha or not val or sha.group(1) != kernel_source_sha():
+    current = kernel_source_sha(KERNEL_SOURCES_INT8 if int8 else None)
+    if not sha or not val or sha.group(1) != current:
         return None
     return float(val.group(1))
 
@@ -244,16 +251,19 @@ def run_decode_int8(pa, torch, b, partition, steps, warmup, dev):
     order = torch.from_numpy(pa.pa_decode_order(b.context_lens)).to(dev)
     torch.cuda.synchronize(dev)
 
-    def step():
-        pa.pa_reshape_and_cache_int8(knew, vnew, kc, vc, ks, vs, slot, stream=stream)
+    def decode():
         pa.pa_decode_int8(out, q, kc, vc, ks, vs, tables, lens, b.scale, b.max_context_len,
                           partition, workspace=workspace, seq_order=order, stream=stream)
+
+    def step():
+        pa.pa_reshape_and_cache_int8(knew, vnew, kc, vc, ks, vs, slot, stream=stream)
+        decode()
 
     for _ in range(warmup):
         step()
     ms = _timed(torch, step, steps)
-    kernel_ms = _events(torch, step, steps, stream)
-    name = "pa_reshape_and_cache_int8 + pa_decode_int8 (decode_int8_kernel" + (
+    kernel_ms = _events(torch, decode, steps, stream)     # the decode launch(es) alone
+    name = "pa_decode_int8 (decode_int8_kernel" + (
         " + merge kernel)" if partition and b.max_context_len > partition else ")")
     return {"ms_per_step": ms, "kernel_ms": kernel_ms, "kernel_name": name}
 
@@ -536,7 +546,8 @@ def main(argv=None) -> int:
                 "decode_us": _stats_us(r2["kernel_ms"]),
                 "roofline": {"bound": "hbm", "kernel": r2["kernel_name"], "achieved": round(ach2, 2),
                              "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                             "frac": round(ach2 / HBM_PEAK_GBPS, 4), "traffic": None}}
+                             "frac": round(ach2 / HBM_PEAK_GBPS, 4),
+                             "traffic": recorded_traffic(name, p2, int8=True)}}
             continue
         if c2["kind"] == "prefill":
             r2 = run_prefill(pa, torch, b2, steps2, max(2, args.warmup // 4), dev)
