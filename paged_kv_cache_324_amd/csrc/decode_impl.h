@@ -387,8 +387,9 @@ void decode_partition_kernel(const DecodeArgs a) {
 // One wavefront per (sequence, query head): merge that row's partitions.
 // Lane p folds the (m, l) of partitions p, p+64, ...; the partial outputs are
 // fetched in batches of 8 partitions, each lane owning D/64 consecutive
-// dimensions.  The first batch and all (m, l) are loaded before the context
-// length is known; entries of partitions past the context are never used.
+// dimensions, one batch ahead of the sum.  The first batch and all (m, l) are
+// loaded before the context length is known; entries of partitions past the
+// context are never used.
 template <int DT, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
   constexpr int E = D / 64;
@@ -440,13 +441,15 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
 
+  // Batches of PB partitions, the next batch's outputs loaded while the
+  // current one is summed.  The loads are unconditional (indices clamped to
+  // the last partition of the grid, always inside the workspace) so that no
+  // wait for them lands at a branch join.
   floatE acc = {};
   for (int p0 = 0; p0 < n; p0 += PB) {
-    if (p0 > 0) {
+    RawE pn[PB];
 #pragma unroll
-      for (int j = 0; j < PB; ++j)
-        pv[j] = p0 + j < n ? po[(p0 + j) * rstride] : RawE(0);
-    }
+    for (int j = 0; j < PB; ++j) pn[j] = po[min(p0 + PB + j, P - 1) * rstride];
 #pragma unroll
     for (int j = 0; j < PB; ++j) {
       const int p = p0 + j;
@@ -461,6 +464,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
         acc += w * widen(pv[j]);
       }
     }
+#pragma unroll
+    for (int j = 0; j < PB; ++j) pv[j] = pn[j];
   }
   uint16_t* out = static_cast<uint16_t*>(a.out) + ((int64_t)seq * a.num_heads + h) * D + lane * E;
   const float inv = 1.0f / den;
