@@ -367,6 +367,43 @@ def run_rope(pa, torch, b, steps, warmup, dev):
             "plain_ms": _events(torch, plain, steps, stream), "tokens": T}
 
 
+def run_graph(pa, torch, b, steps, warmup, dev):
+    """A serving-style decode step of two launches -- the rotary embedding with the cache
+    write of this step's tokens (queries rotated in place), then decode -- timed as eager
+    launches and as replays of the same step captured in a HIP graph."""
+    from workloads import rope_tables
+    d = upload(torch, b, dev)
+    pos = torch.from_numpy(b.context_lens.astype(np.int64) - 1).to(dev)
+    cos, sin = rope_tables(int(b.max_context_len) + 1, b.D)
+    cos_d, sin_d = torch.from_numpy(cos).to(dev), torch.from_numpy(sin).to(dev)
+    out = torch.empty_like(d.q)
+    partition = pa.pa_decode_partition_hint(b.B, b.Hkv, b.max_context_len, b.BS)
+    ws = pa.decode_workspace(b.B, b.Hq, b.D, b.max_context_len, partition, dev)
+    order = torch.from_numpy(pa.pa_decode_order(b.context_lens)).to(dev)
+
+    def step():
+        pa.pa_rope_reshape_and_cache(d.q, d.key_new, d.value_new, d.k_cache, d.v_cache, pos, cos_d,
+                                     sin_d, d.slot)
+        pa.pa_decode(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, b.scale, b.max_context_len,
+                     partition, workspace=ws, seq_order=order)
+
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for _ in range(warmup):
+            step()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+    eager_ms = _timed(torch, step, steps)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    graph_ms = _timed(torch, g.replay, steps)
+    return {"eager_ms": eager_ms, "graph_ms": graph_ms, "partition_size": partition}
+
+
 def run_prefill(pa, torch, b, steps, warmup, dev):
     d = upload(torch, b, dev)
     out = torch.empty_like(d.q)
@@ -405,11 +442,12 @@ def main(argv=None) -> int:
                     default="llama2_70b_decode_bs16,llama2_70b_decode_bs32,long_splitk_decode,"
                             "chunked_prefill,qwen3_0p6b_decode:int8,llama2_70b_decode_bs16:int8,"
                             "long_splitk_decode:int8,long_splitk_decode:cp8,chunked_prefill:rope,"
-                            "qwen3_0p6b_decode:rope",
+                            "qwen3_0p6b_decode:rope,tiny_decode:graph,qwen3_0p6b_decode:graph",
                     help="comma-separated extra workloads reported beside the headline; "
                          "a ':int8' suffix runs the workload over an INT8 KV cache, ':cpN' "
                          "as one device of an N-way context-parallel group, ':rope' times the "
-                         "fused rotary embedding + cache write of its new tokens")
+                         "fused rotary embedding + cache write of its new tokens, ':graph' a "
+                         "rotary + decode step eager and as HIP-graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-kernel-bytes", type=int, default=0,
@@ -517,6 +555,17 @@ def main(argv=None) -> int:
                 "roofline": {"bound": "hbm", "kernel": f"pa_decode_partial ({kern})",
                              "achieved": round(ach2, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                              "frac": round(ach2 / HBM_PEAK_GBPS, 4), "traffic": None}}
+            continue
+        if variant == "graph":
+            r2 = run_graph(pa, torch, b2, max(50, steps2), max(5, args.warmup // 4), dev)
+            kv2 = b2.kv_bytes()
+            secondary[entry] = {
+                "step": "pa_rope_reshape_and_cache + pa_decode (two launches), eager vs HIP-graph replay",
+                "partition_size": r2["partition_size"], "steps": max(50, steps2),
+                "eager_us_per_step": round(r2["eager_ms"] * 1e3, 2),
+                "graph_us_per_step": round(r2["graph_ms"] * 1e3, 2),
+                "graph_speedup": round(r2["eager_ms"] / r2["graph_ms"], 3),
+                "graph_effective_GBps": round(kv2 / (r2["graph_ms"] * 1e-3) / 1e9, 2)}
             continue
         if variant == "rope":
             r2 = run_rope(pa, torch, b2, max(20, steps2), max(2, args.warmup // 4), dev)
