@@ -265,6 +265,28 @@ int pa_merge_partials(void* out, float* out_ml, const void* partial_o, const flo
                       void* stream);
 
 /*
+ * pa_decode_step_rope: pa_decode_step with the rotary embedding of
+ * pa_rope_reshape_and_cache folded in.  The query rows of sequence i and its
+ * new key row are rotated by row positions[i] of cos_table / sin_table
+ * (float32 [max_position][head_dim / 2], 16-byte aligned) with exactly the
+ * arithmetic of pa_rope_reshape_and_cache, then used as in pa_decode_step: the
+ * rotated key (and the value, unchanged) is stored at slot_mapping[i] and
+ * attended to at position context_lens[i] - 1.  q itself is only read.  A
+ * position outside [0, max_position) leaves that sequence's rows unrotated.
+ * Results equal pa_rope_reshape_and_cache (on a copy of q) followed by
+ * pa_decode_step on the rotated rows, bit for bit; one launch fewer.  Other
+ * arguments, workspace rules and supported shapes as for pa_decode_step.
+ */
+int pa_decode_step_rope(void* out, const void* q, const void* key, const void* value,
+                        const int64_t* slot_mapping, const int64_t* positions, const float* cos_table,
+                        const float* sin_table, int64_t max_position, void* k_cache, void* v_cache,
+                        const int32_t* block_tables, const int32_t* context_lens,
+                        const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads,
+                        int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                        int max_context_len, float scale, int partition_size, void* workspace,
+                        size_t workspace_bytes, int dtype, void* stream);
+
+/*
  * INT8 KV cache.  KV-cache compression by INT8 quantisation is the next
  * optimisation the pages list (page "Nano-vLLM-Ascend", section 4.3) and the
  * one that raises throughput if the attention scores keep their precision

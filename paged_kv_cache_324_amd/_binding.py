@@ -96,6 +96,10 @@ def _declare(lib):
     lib.pa_rope_reshape_and_cache.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                               c_i64, c_int, c_int, c_int, c_int, c_i64, c_i64,
                                               c_int, c_vp]
+    lib.pa_decode_step_rope.restype = c_int
+    lib.pa_decode_step_rope.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp,
+                                        c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int,
+                                        c_i64, c_int, c_int, c_f, c_int, c_vp, c_sz, c_int, c_vp]
     lib.pa_decode_partial.restype = c_int
     lib.pa_decode_partial.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int,
                                       c_int, c_int, c_int, c_i64, c_int, c_int, c_f, c_int, c_vp,
@@ -331,6 +335,32 @@ def pa_merge_partials(out, partial_o, partial_ml, out_ml=None, stream=None) -> t
     _check(lib.pa_merge_partials(_dev(out, "out"), ml_ptr, _dev(partial_o, "partial_o", out.dtype),
                                  _dev(partial_ml, "partial_ml", torch.float32), N, B, Hq, D, dt,
                                  _stream(out, stream)))
+    return out
+
+
+def pa_decode_step_rope(out, q, key, value, slot_mapping, positions, cos, sin, k_cache, v_cache,
+                        block_tables, context_lens, scale: float, max_context_len: int,
+                        partition_size: int = 512, workspace=None, seq_order=None,
+                        stream=None) -> torch.Tensor:
+    """pa_decode_step with the rotary embedding of q and of the new key (rows ``positions`` of
+    the float32 tables ``cos``/``sin`` [max_position][D/2]) folded into the same launch."""
+    lib, B, Hq, Hkv, D, BS, NB, dt, ws_ptr, ws_bytes, order_ptr = _decode_common(
+        q, k_cache, v_cache, block_tables, context_lens, seq_order, out, max_context_len,
+        partition_size, workspace)
+    if key.shape != (B, Hkv, D) or value.shape != key.shape or slot_mapping.shape != (B,):
+        raise ValueError("decode step: key/value must be [B][Hkv][D], slot_mapping [B]")
+    if positions.shape != (B,) or cos.dim() != 2 or cos.shape[1] != D // 2 or sin.shape != cos.shape:
+        raise ValueError("positions must be [B], cos/sin [max_position][D/2]")
+    _dev(key, "key", q.dtype)
+    _dev(value, "value", q.dtype)
+    _check(lib.pa_decode_step_rope(
+        _dev(out, "out"), _dev(q, "q"), key.data_ptr(), value.data_ptr(),
+        _dev(slot_mapping, "slot_mapping", torch.int64), _dev(positions, "positions", torch.int64),
+        _dev(cos, "cos", torch.float32), _dev(sin, "sin", torch.float32), cos.shape[0],
+        k_cache.data_ptr(), v_cache.data_ptr(), _dev(block_tables, "block_tables", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32), order_ptr, B, Hq, Hkv, D, BS, NB,
+        block_tables.shape[1], int(max_context_len), float(scale), int(partition_size), ws_ptr,
+        ws_bytes, dt, _stream(q, stream)))
     return out
 
 

@@ -84,7 +84,7 @@ __device__ __forceinline__ float2* row_ml_target(const DecodeArgs& a, int nparts
   return nullptr;
 }
 
-template <int DT, int D, int BS, int G, int PF, int WAVES_PER_EU, int LOAD_AUX>
+template <int DT, int D, int BS, int G, int PF, int WAVES_PER_EU, int LOAD_AUX, bool ROPE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_EU, 8)))
 void decode_partition_kernel(const DecodeArgs a) {
   constexpr int LPR = D / 8;           // lanes per token row
@@ -127,6 +127,18 @@ void decode_partition_kernel(const DecodeArgs a) {
   const int lb_first = t0 / BS;
   const int32_t tbl_first =
       lb_first + (int)threadIdx.x < a.max_blocks ? bt[lb_first + threadIdx.x] : -1;
+  // Rotary tables of the step's position (fused rotary step): lane c of a row
+  // slot rotates dims 8 (c % (LPR/2)) .. + 7 of its half with the same dims of
+  // the other half, held by lane c ^ (LPR/2).
+  float rcs[8], rsn[8];
+  bool rope_ok = false;
+  if constexpr (ROPE) {
+    const int64_t pos = a.positions[seq];
+    rope_ok = pos >= 0 && pos < a.max_position;
+    const int cr = (threadIdx.x & 63) % LPR;
+    rope_row8(a.rope_cos, rope_ok ? pos : 0, D / 2, 8 * (cr % (LPR / 2)), rcs);
+    rope_row8(a.rope_sin, rope_ok ? pos : 0, D / 2, 8 * (cr % (LPR / 2)), rsn);
+  }
   uint32_t qv[G][4];
   {
     const int c = (threadIdx.x & 63) % LPR;
@@ -156,6 +168,30 @@ void decode_partition_kernel(const DecodeArgs a) {
     const int64_t row = ((int64_t)seq * a.num_kv_heads + kvh) * D;
     k_new = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.key_new) + row)[c];
     v_new = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.value_new) + row)[c];
+  }
+  if constexpr (ROPE) {
+    if (new_here && wave == 0) {  // rotate the new key (row slot 0 holds it)
+      const u32x4 partner = {(uint32_t)__shfl_xor((int)k_new.x, LPR / 2),
+                             (uint32_t)__shfl_xor((int)k_new.y, LPR / 2),
+                             (uint32_t)__shfl_xor((int)k_new.z, LPR / 2),
+                             (uint32_t)__shfl_xor((int)k_new.w, LPR / 2)};
+      if (rope_ok && r == 0) k_new = rope_half8<DT>(k_new, partner, rcs, rsn, c < LPR / 2);
+    }
+  }
+
+  if constexpr (ROPE) {  // rotate the queries (used from the first step on)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const u32x4 own = {qv[g][0], qv[g][1], qv[g][2], qv[g][3]};
+      const u32x4 partner = {(uint32_t)__shfl_xor((int)own.x, LPR / 2),
+                             (uint32_t)__shfl_xor((int)own.y, LPR / 2),
+                             (uint32_t)__shfl_xor((int)own.z, LPR / 2),
+                             (uint32_t)__shfl_xor((int)own.w, LPR / 2)};
+      if (rope_ok) {
+        const u32x4 y = rope_half8<DT>(own, partner, rcs, rsn, c < LPR / 2);
+        qv[g][0] = y.x; qv[g][1] = y.y; qv[g][2] = y.z; qv[g][3] = y.w;
+      }
+    }
   }
 
   const uint32_t row_stride = (uint32_t)a.num_kv_heads * D * 2;
@@ -475,7 +511,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
     reinterpret_cast<float2*>(a.out_ml)[(int64_t)seq * a.num_heads + h] = make_float2(M, den);
 }
 
-template <int DT, int BS, int G>
+template <int DT, int BS, int G, bool ROPE>
 __global__ void decode_mfma_kernel(const DecodeArgs a);
 
 // Matrix cores take the score/value products once a KV head serves 4 or more
@@ -485,16 +521,25 @@ constexpr bool decode_uses_mfma() {
   return D == 128 && G >= 4;
 }
 
-template <int DT, int D, int BS, int G>
-hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
+template <int DT, int D, int BS, int G, bool ROPE>
+void launch_partitions(const DecodeArgs& a, unsigned grid, hipStream_t s) {
   constexpr int PF = (G <= 2) ? PA_DECODE_PF : 4;
   constexpr int WPE = (G <= 4) ? PA_DECODE_WPE : 2;
-  const unsigned grid = (unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_parts);
   if constexpr (decode_uses_mfma<D, G>()) {
-    hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, G>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, G, ROPE>), dim3(grid), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, PF, WPE, PA_DECODE_AUX>), dim3(grid),
-                       dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, PF, WPE, PA_DECODE_AUX, ROPE>),
+                       dim3(grid), dim3(256), 0, s, a);
+  }
+}
+
+template <int DT, int D, int BS, int G>
+hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_parts);
+  if (a.rope_cos) {
+    launch_partitions<DT, D, BS, G, true>(a, grid, s);
+  } else {
+    launch_partitions<DT, D, BS, G, false>(a, grid, s);
   }
   if (a.num_parts > 1) {
     hipLaunchKernelGGL((decode_merge_kernel<DT, D>), dim3((unsigned)(a.num_seqs * a.num_heads)),

@@ -49,7 +49,7 @@ constexpr float kMdLazyRescale = 8.0f;
 // then touch 16 distinct bank groups.
 __device__ __forceinline__ int md_vswz(int r) { return (2 * r) & 15; }
 
-template <int DT, int BS, int G>
+template <int DT, int BS, int G, bool ROPE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_mfma_kernel(const DecodeArgs a) {
   constexpr int D = 128;
@@ -100,6 +100,28 @@ void decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[ks] = qp[4 * ks + quad];
   }
+  // Fused rotary step: fragment ks holds 16-byte chunk 4 ks + quad, so chunks
+  // j and j + 8 (dims 8 j .. + 7 of the two halves) are fragments ks and ks + 2
+  // of the same lane; table entries of pair index 8 (4 ks + quad), ks = 0, 1.
+  float rcs[2][8], rsn[2][8];
+  bool rope_ok = false;
+  if constexpr (ROPE) {
+    const int64_t pos = a.positions[seq];
+    rope_ok = pos >= 0 && pos < a.max_position;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      rope_row8(a.rope_cos, rope_ok ? pos : 0, D / 2, 8 * (4 * ks + quad), rcs[ks]);
+      rope_row8(a.rope_sin, rope_ok ? pos : 0, D / 2, 8 * (4 * ks + quad), rsn[ks]);
+    }
+  }
+  auto rotate_frags = [&](u32x4 (&f)[4]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 x1 = f[ks], x2 = f[ks + 2];
+      f[ks] = rope_half8<DT>(x1, x2, rcs[ks], rsn[ks], true);
+      f[ks + 2] = rope_half8<DT>(x2, x1, rcs[ks], rsn[ks], false);
+    }
+  };
 
   const int L = clamp_context(a, seq);
   if (L == 0) {
@@ -121,9 +143,24 @@ void decode_mfma_kernel(const DecodeArgs a) {
     if (slot >= 0 && slot < a.num_slots) {
       const void* src = lane < 16 ? a.key_new : a.value_new;
       void* dst = lane < 16 ? a.k_cache_w : a.v_cache_w;
+      const u32x4* srow = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + new_row);
+      u32x4 chunk = srow[col];
+      if constexpr (ROPE) {
+        if (lane < 16 && rope_ok) {  // the stored key is the rotated one
+          float cs[8], sn[8];
+          const int64_t pos = a.positions[seq];
+          rope_row8(a.rope_cos, pos, D / 2, 8 * (col & 7), cs);
+          rope_row8(a.rope_sin, pos, D / 2, 8 * (col & 7), sn);
+          chunk = rope_half8<DT>(chunk, srow[col ^ 8], cs, sn, col < 8);
+        }
+      }
       reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + (slot * a.num_kv_heads + kvh) * D)[col] =
-          reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + new_row)[col];
+          chunk;
     }
+  }
+
+  if constexpr (ROPE) {
+    if (rope_ok) rotate_frags(qf);
   }
 
   const int32_t nb32 = a.num_blocks > INT32_MAX ? INT32_MAX : (int32_t)a.num_blocks;
@@ -315,6 +352,9 @@ void decode_mfma_kernel(const DecodeArgs a) {
     for (int ks = 0; ks < 4; ++ks) {
       kf[0][ks] = buffer_load16<0>(rk, (uint32_t)col * row_bytes + (uint32_t)(4 * ks + quad) * 16);
       kf[1][ks] = u32x4{0u, 0u, 0u, 0u};
+    }
+    if constexpr (ROPE) {
+      if (rope_ok) rotate_frags(kf[0]);  // rows other than 0 are zeros and stay zeros
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -217,6 +217,11 @@ struct NewTokens {
   const int64_t* slot_mapping;
   void* k_cache;
   void* v_cache;
+  // Rotary embedding of the step (pa_decode_step_rope); null otherwise.
+  const int64_t* positions = nullptr;
+  const float* cos_table = nullptr;
+  const float* sin_table = nullptr;
+  int64_t max_position = 0;
 };
 
 // Per-row scales of an INT8 cache (pa_decode_int8); null for 16-bit caches.
@@ -285,6 +290,10 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.v_cache_w = nt ? nt->v_cache : nullptr;
   a.k_scales = i8 ? i8->k : nullptr;
   a.v_scales = i8 ? i8->v : nullptr;
+  a.positions = nt ? nt->positions : nullptr;
+  a.rope_cos = nt ? nt->cos_table : nullptr;
+  a.rope_sin = nt ? nt->sin_table : nullptr;
+  a.max_position = nt ? nt->max_position : 0;
   a.num_slots = num_blocks * (int64_t)block_size;
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
@@ -419,6 +428,30 @@ int pa_merge_partials(void* out, float* out_ml, const void* partial_o, const flo
   a.num_shards = num_shards;
   return hip_status(pa::launch_merge_partials(a, dtype, head_dim, static_cast<hipStream_t>(stream)),
                     "merge_partials launch");
+}
+
+int pa_decode_step_rope(void* out, const void* q, const void* key, const void* value,
+                        const int64_t* slot_mapping, const int64_t* positions, const float* cos_table,
+                        const float* sin_table, int64_t max_position, void* k_cache, void* v_cache,
+                        const int32_t* block_tables, const int32_t* context_lens,
+                        const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads,
+                        int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                        int max_context_len, float scale, int partition_size, void* workspace,
+                        size_t workspace_bytes, int dtype, void* stream) {
+  if (num_seqs > 0) {
+    if (!positions || !cos_table || !sin_table)
+      return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+    if (max_position < 1) return fail(PA_ERR_INVALID_ARG, "max_position must be >= 1");
+    if (reinterpret_cast<uintptr_t>(cos_table) % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(sin_table) % 16 != 0)
+      return fail(PA_ERR_INVALID_ARG, "cos/sin tables must be 16-byte aligned");
+  }
+  NewTokens nt{key, value, slot_mapping, k_cache, v_cache, positions, cos_table, sin_table,
+               max_position};
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, seq_order, &nt, nullptr,
+                     nullptr, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
+                     workspace_bytes, dtype, stream);
 }
 
 int pa_reshape_and_cache_int8(const void* key, const void* value, void* k_codes, void* v_codes,

@@ -86,6 +86,40 @@ __device__ __forceinline__ uint16_t to_u16(float a) {
   }
 }
 
+// ---- rotary embedding ------------------------------------------------------------
+// Eight dimensions of one half of a rotated row: `own` holds them, `partner`
+// the same eight dimensions of the other half, cs / sn the table entries of
+// their pair index.  First half: own c - partner s; second half:
+// own c + partner s.  Each product and the sum or difference is rounded to fp32
+// on its own (no fused multiply-add), then the result to the 16-bit type, so
+// every kernel that rotates produces the same bits.
+template <int DT>
+__device__ __forceinline__ u32x4 rope_half8(const u32x4& own, const u32x4& partner, const float* cs,
+                                            const float* sn, bool first_half) {
+#pragma clang fp contract(off)
+  const uint32_t ow[4] = {own.x, own.y, own.z, own.w};
+  const uint32_t pw[4] = {partner.x, partner.y, partner.z, partner.w};
+  uint32_t r[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float ol = lo_f32<DT>(ow[w]), oh = hi_f32<DT>(ow[w]);
+    const float pl = lo_f32<DT>(pw[w]), ph = hi_f32<DT>(pw[w]);
+    const float cl = cs[2 * w], ch = cs[2 * w + 1], sl = sn[2 * w], sh = sn[2 * w + 1];
+    const float al = ol * cl, ah = oh * ch, bl = pl * sl, bh = ph * sh;
+    r[w] = first_half ? pack2<DT>(al - bl, ah - bh) : pack2<DT>(al + bl, ah + bh);
+  }
+  return u32x4{r[0], r[1], r[2], r[3]};
+}
+
+// The eight table entries (cos or sin) starting at pair index i0 of row pos.
+__device__ __forceinline__ void rope_row8(const float* table, int64_t pos, int half_dim, int i0,
+                                          float* out) {
+  const float4* p = reinterpret_cast<const float4*>(table + pos * half_dim + i0);
+  const float4 a = p[0], b = p[1];
+  out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
 // ---- cross-lane sums within a DPP row ------------------------------------------
 #define PA_DPP(x, ctrl) \
   __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), (ctrl), 0xF, 0xF, false))

@@ -82,6 +82,14 @@ struct DecodeArgs {
   void* v_cache_w;
   const float* k_scales;  // INT8 caches only: [num_blocks][num_kv_heads][block_size]
   const float* v_scales;
+  // Fused rotary embedding (fused step only; null otherwise): the query and the
+  // new key of sequence i are rotated by row positions[i] of the float32
+  // tables [max_position][head_dim / 2] before use (rows outside the table:
+  // no rotation).
+  const int64_t* positions;
+  const float* rope_cos;
+  const float* rope_sin;
+  int64_t max_position;
   int64_t num_slots;   // num_blocks * block_size
   int64_t num_blocks;
   int num_seqs;

@@ -26,27 +26,6 @@
 
 namespace pa {
 
-template <int DT>
-__device__ __forceinline__ void rotate8(const u32x4& a, const u32x4& b, const float* cs,
-                                        const float* sn, u32x4& ya, u32x4& yb) {
-#pragma clang fp contract(off)
-  const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-  const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
-  uint32_t ra[4], rb[4];
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float x1l = lo_f32<DT>(aw[w]), x1h = hi_f32<DT>(aw[w]);
-    const float x2l = lo_f32<DT>(bw[w]), x2h = hi_f32<DT>(bw[w]);
-    const float cl = cs[2 * w], ch = cs[2 * w + 1], sl = sn[2 * w], sh = sn[2 * w + 1];
-    const float y1l = x1l * cl - x2l * sl, y1h = x1h * ch - x2h * sh;
-    const float y2l = x2l * cl + x1l * sl, y2h = x2h * ch + x1h * sh;
-    ra[w] = pack2<DT>(y1l, y1h);
-    rb[w] = pack2<DT>(y2l, y2h);
-  }
-  ya = u32x4{ra[0], ra[1], ra[2], ra[3]};
-  yb = u32x4{rb[0], rb[1], rb[2], rb[3]};
-}
-
 // One workgroup per token (blockDim = its item count rounded up to whole
 // wavefronts, at most 1024; a token with more items loops).  The token's
 // position and slot are read once, as scalars.
@@ -90,8 +69,8 @@ __global__ __launch_bounds__(1024) void rope_reshape_kernel(RopeReshapeArgs a) {
     const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
     const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
     const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-    u32x4 y1, y2;
-    rotate8<DT>(x1, x2, cs, sn, y1, y2);
+    const u32x4 y1 = rope_half8<DT>(x1, x2, cs, sn, true);
+    const u32x4 y2 = rope_half8<DT>(x2, x1, cs, sn, false);
     if (is_q) {
       uint16_t* qrow = static_cast<uint16_t*>(a.q) + (t * hq + row) * D;
       reinterpret_cast<u32x4*>(qrow)[c] = y1;
