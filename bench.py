@@ -368,9 +368,10 @@ def run_rope(pa, torch, b, steps, warmup, dev):
 
 
 def run_graph(pa, torch, b, steps, warmup, dev):
-    """A serving-style decode step of two launches -- the rotary embedding with the cache
-    write of this step's tokens (queries rotated in place), then decode -- timed as eager
-    launches and as replays of the same step captured in a HIP graph."""
+    """A serving-style decode step: the rotary embedding of q and of the new key, the cache
+    write of the new key and value, and decode.  Timed as two launches
+    (pa_rope_reshape_and_cache, then pa_decode) and as the one fused launch
+    (pa_decode_step_rope), each eager and as replays of the step captured in a HIP graph."""
     from workloads import rope_tables
     d = upload(torch, b, dev)
     pos = torch.from_numpy(b.context_lens.astype(np.int64) - 1).to(dev)
@@ -387,21 +388,31 @@ def run_graph(pa, torch, b, steps, warmup, dev):
         pa.pa_decode(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, b.scale, b.max_context_len,
                      partition, workspace=ws, seq_order=order)
 
-    side = torch.cuda.Stream(dev)
-    side.wait_stream(torch.cuda.current_stream(dev))
-    with torch.cuda.stream(side):
+    def fused():
+        pa.pa_decode_step_rope(out, d.q, d.key_new, d.value_new, d.slot, pos, cos_d, sin_d,
+                               d.k_cache, d.v_cache, d.tables, d.lens, b.scale, b.max_context_len,
+                               partition, workspace=ws, seq_order=order)
+
+    def eager_and_graph(fn):
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                fn()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize(dev)
+        eager_ms = _timed(torch, fn, steps)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
         for _ in range(warmup):
-            step()
-    torch.cuda.current_stream(dev).wait_stream(side)
-    torch.cuda.synchronize(dev)
-    eager_ms = _timed(torch, step, steps)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
-    for _ in range(warmup):
-        g.replay()
-    graph_ms = _timed(torch, g.replay, steps)
-    return {"eager_ms": eager_ms, "graph_ms": graph_ms, "partition_size": partition}
+            g.replay()
+        return eager_ms, _timed(torch, g.replay, steps)
+
+    eager_ms, graph_ms = eager_and_graph(step)
+    fused_ms, fused_graph_ms = eager_and_graph(fused)
+    return {"eager_ms": eager_ms, "graph_ms": graph_ms, "fused_ms": fused_ms,
+            "fused_graph_ms": fused_graph_ms, "partition_size": partition}
 
 
 def run_prefill(pa, torch, b, steps, warmup, dev):
@@ -447,7 +458,8 @@ def main(argv=None) -> int:
                          "a ':int8' suffix runs the workload over an INT8 KV cache, ':cpN' "
                          "as one device of an N-way context-parallel group, ':rope' times the "
                          "fused rotary embedding + cache write of its new tokens, ':graph' a "
-                         "rotary + decode step eager and as HIP-graph replays")
+                         "rotary + decode step as two launches and as one fused launch, each eager "
+                         "and as HIP-graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-kernel-bytes", type=int, default=0,
@@ -560,12 +572,17 @@ def main(argv=None) -> int:
             r2 = run_graph(pa, torch, b2, max(50, steps2), max(5, args.warmup // 4), dev)
             kv2 = b2.kv_bytes()
             secondary[entry] = {
-                "step": "pa_rope_reshape_and_cache + pa_decode (two launches), eager vs HIP-graph replay",
+                "step": "rotary embedding + cache write + decode: two launches "
+                        "(pa_rope_reshape_and_cache, pa_decode) vs one (pa_decode_step_rope), "
+                        "each eager and as HIP-graph replays",
                 "partition_size": r2["partition_size"], "steps": max(50, steps2),
                 "eager_us_per_step": round(r2["eager_ms"] * 1e3, 2),
                 "graph_us_per_step": round(r2["graph_ms"] * 1e3, 2),
                 "graph_speedup": round(r2["eager_ms"] / r2["graph_ms"], 3),
-                "graph_effective_GBps": round(kv2 / (r2["graph_ms"] * 1e-3) / 1e9, 2)}
+                "fused_eager_us_per_step": round(r2["fused_ms"] * 1e3, 2),
+                "fused_graph_us_per_step": round(r2["fused_graph_ms"] * 1e3, 2),
+                "fused_speedup": round(r2["eager_ms"] / r2["fused_ms"], 3),
+                "fused_effective_GBps": round(kv2 / (r2["fused_ms"] * 1e-3) / 1e9, 2)}
             continue
         if variant == "rope":
             r2 = run_rope(pa, torch, b2, max(20, steps2), max(2, args.warmup // 4), dev)

@@ -16,8 +16,9 @@ def _bits(t):
     return t.view(torch.int16).cpu().numpy()
 
 
-@pytest.mark.parametrize("partition,fused", [(0, False), (128, False), (0, True), (128, True)])
-def test_graph_replays_match_eager(partition, fused):
+@pytest.mark.parametrize("mode", ["rope_then_decode", "step", "step_rope"])
+@pytest.mark.parametrize("partition", [0, 128])
+def test_graph_replays_match_eager(partition, mode):
     b = make_batch(B=12, Hq=16, Hkv=4, D=128, BS=16, dtype="bf16", scale=128 ** -0.5, seed=4242,
                    lens_range=(40, 700))
     d = upload(b)
@@ -35,11 +36,16 @@ def test_graph_replays_match_eager(partition, fused):
     kc, vc = d.k_cache, d.v_cache
 
     def step(q_, k_, v_, kc_, vc_, out_, ws_):
-        if fused:
+        if mode == "step":
             # one launch: store this step's K/V rows and attend
             pa.pa_decode_step(out_, q_, k_, v_, d.slot_mapping, kc_, vc_, d.block_tables,
                               d.context_lens, b.scale, b.max_context_len, partition, workspace=ws_,
                               seq_order=order)
+        elif mode == "step_rope":
+            # one launch: rotate q and the new key, store this step's K/V rows and attend
+            pa.pa_decode_step_rope(out_, q_, k_, v_, d.slot_mapping, pos, cos_d, sin_d, kc_, vc_,
+                                   d.block_tables, d.context_lens, b.scale, b.max_context_len,
+                                   partition, workspace=ws_, seq_order=order)
         else:
             # rotary embedding of q (in place) and K on its way into the cache, then decode
             pa.pa_rope_reshape_and_cache(q_, k_, v_, kc_, vc_, pos, cos_d, sin_d, d.slot_mapping)
@@ -76,4 +82,4 @@ def test_graph_replays_match_eager(partition, fused):
         assert torch.equal(kc.view(torch.int16), kc_e.view(torch.int16)), f"replay {r}: K cache"
         assert torch.equal(vc.view(torch.int16), vc_e.view(torch.int16)), f"replay {r}: V cache"
         assert torch.isfinite(out.float()).all()
-    log(f"graph partition={partition} fused={fused}: 4 replays bit-identical to eager")
+    log(f"graph partition={partition} {mode}: 4 replays bit-identical to eager")
