@@ -6,8 +6,8 @@
 // through the block table (section 2.1) and the softmax statistics kept in
 // fp32 (page "vLLM-Ascend ...", section 3.1, problem 2).
 //
-// Work decomposition.  One workgroup (4 wavefronts) per (sequence, KV head,
-// context partition).  All G = Hq/Hkv query heads that read the KV head are
+// Work decomposition.  One workgroup (NW wavefronts, see DecodeShape) per
+// (sequence, KV head, context partition).  All G = Hq/Hkv query heads that read the KV head are
 // served by the same workgroup, so every K/V byte is fetched once per step.
 //
 // Loads.  A token's row for one KV head is head_dim * 2 bytes (256 B at
@@ -23,7 +23,7 @@
 // over the tokens it sees (fp32 running max m and sum l, in the log2 domain so
 // the exponential is a single v_exp_f32).  Scores are reduced across the LPR
 // lanes with DPP row operations.  At the end the row slots of a wavefront are
-// merged with cross-lane shuffles and the four wavefronts through LDS.
+// merged with cross-lane shuffles and the NW wavefronts through LDS.
 //
 // Partitions.  With partition_size > 0 a long context is cut into partitions
 // of that many tokens.  A partition writes its normalised output o_p and its
@@ -44,17 +44,24 @@
 
 namespace pa {
 
-#ifndef PA_DECODE_PF
-#define PA_DECODE_PF 8    // steps of K and V in flight per lane (group size)
-#endif
-#ifndef PA_DECODE_WPE
-#define PA_DECODE_WPE 2   // minimum resident waves per SIMD the register budget must allow
-#endif
 #ifndef PA_DECODE_AUX
 #define PA_DECODE_AUX kCachePolicyNT
 #endif
 
-constexpr int kDecodeWaves = 4;
+// Launch shape of decode_partition_kernel for G query heads per KV head.
+// G <= 2: eight wavefronts per workgroup and four steps of K and V in flight
+// per lane, within 128 VGPRs, so that a SIMD holds four wavefronts and a
+// compute unit two workgroups (on the Qwen3-shaped batch this measured 3.5%
+// faster than four wavefronts with eight steps each: the same bytes in flight
+// per workgroup, and the same two-round longest-first dispatch).
+// G = 4 or 8 (head_dim 64; at head_dim 128 the matrix-core kernel runs):
+// four wavefronts, four steps, two wavefronts per SIMD.
+template <int G>
+struct DecodeShape {
+  static constexpr int waves = G <= 2 ? 8 : 4;
+  static constexpr int pf = 4;
+  static constexpr int waves_per_eu = G <= 2 ? 4 : 2;
+};
 constexpr int kTableCap = 256;  // block ids staged in LDS per chunk of a partition
 constexpr float kEmptyMax = -1.0e30f;  // finite "no token yet" max: keeps 2^(m - m') finite
 
@@ -69,7 +76,7 @@ template <int D, int G>
 __device__ __forceinline__ void write_empty_rows(const DecodeArgs& a, int seq, int h0) {
   const int64_t row0 = (int64_t)seq * a.num_heads + h0;
   uint16_t* o = static_cast<uint16_t*>(a.out) + row0 * D;
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) o[idx] = 0;
+  for (int idx = threadIdx.x; idx < G * D; idx += (int)blockDim.x) o[idx] = 0;
   if (a.out_ml && (int)threadIdx.x < G)
     reinterpret_cast<float2*>(a.out_ml)[row0 + threadIdx.x] = make_float2(-__builtin_inff(), 0.f);
 }
@@ -84,14 +91,14 @@ __device__ __forceinline__ float2* row_ml_target(const DecodeArgs& a, int nparts
   return nullptr;
 }
 
-template <int DT, int D, int BS, int G, int PF, int WAVES_PER_EU, int LOAD_AUX, bool ROPE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_EU, 8)))
+template <int DT, int D, int BS, int G, int NW, int PF, int WAVES_PER_EU, int LOAD_AUX, bool ROPE>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_PER_EU, 8)))
 void decode_partition_kernel(const DecodeArgs a) {
   constexpr int LPR = D / 8;           // lanes per token row
   constexpr int RPW = 64 / LPR;        // token rows per wavefront load
-  constexpr int NW = kDecodeWaves;
   constexpr int TPS = NW * RPW;        // tokens per workgroup step
   static_assert(BS % RPW == 0, "a wavefront's rows must lie in one block");
+  static_assert(PF >= 1 && PF <= 64, "lane u of a wavefront addresses step u of a group");
 
   __shared__ float s_acc[NW][G][D];
   __shared__ float s_ml[NW][G][2];
@@ -218,7 +225,7 @@ void decode_partition_kernel(const DecodeArgs a) {
     const int c1 = min(t1c, c0 + kChunkTokens);
     const int lb0 = c0 / BS;
     const int nchunk_blk = (c1 - c0 + BS - 1) / BS;
-    static_assert(kTableCap == 256, "one table entry per thread");
+    static_assert(kTableCap <= 64 * NW, "one table entry per thread");
     __syncthreads();  // previous chunk's table reads are done
     if ((int)threadIdx.x < nchunk_blk) {
       const int32_t blk = c0 == t0 ? tbl_first : bt[lb0 + threadIdx.x];
@@ -235,7 +242,7 @@ void decode_partition_kernel(const DecodeArgs a) {
     const uint32_t wave_t0 = (uint32_t)c0 + (uint32_t)wave * RPW;
     struct Group { uint32_t lo, hi, nrec; };
     auto group_where = [&](int sbase) -> Group {
-      const uint32_t tb = wave_t0 + (uint32_t)(sbase + (lane & (PF - 1))) * TPS;
+      const uint32_t tb = wave_t0 + (uint32_t)(sbase + lane % PF) * TPS;
       const uint32_t lb = tb / BS;
       const uint32_t o = tb % BS;                        // first row inside the block
       const int nvr = min(BS, c1 - (int)(lb * BS)) - (int)o;  // valid rows from there
@@ -387,7 +394,7 @@ void decode_partition_kernel(const DecodeArgs a) {
   // Merge the wavefronts and write the partition (or final) result.  A
   // partition's rows of the G heads are contiguous in part_out.
   const int64_t prow = ((int64_t)seq * a.num_parts + part) * a.num_heads + h0;
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
     const int g = idx / D;
     const int d = idx - g * D;
     float M = s_ml[0][g][0];
@@ -523,13 +530,13 @@ constexpr bool decode_uses_mfma() {
 
 template <int DT, int D, int BS, int G, bool ROPE>
 void launch_partitions(const DecodeArgs& a, unsigned grid, hipStream_t s) {
-  constexpr int PF = (G <= 2) ? PA_DECODE_PF : 4;
-  constexpr int WPE = (G <= 4) ? PA_DECODE_WPE : 2;
+  using Shape = DecodeShape<G>;
   if constexpr (decode_uses_mfma<D, G>()) {
     hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, G, ROPE>), dim3(grid), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, PF, WPE, PA_DECODE_AUX, ROPE>),
-                       dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, Shape::waves, Shape::pf,
+                                                Shape::waves_per_eu, PA_DECODE_AUX, ROPE>),
+                       dim3(grid), dim3(64 * Shape::waves), 0, s, a);
   }
 }
 
