@@ -428,15 +428,14 @@ void decode_partition_kernel(const DecodeArgs a) {
 }
 
 // One wavefront per (sequence, query head): merge that row's partitions.
-// Lane p folds the (m, l) of partitions p, p+64, ...; the partial outputs are
-// fetched in batches of 8 partitions, each lane owning D/64 consecutive
-// dimensions, one batch ahead of the sum.  The first batch and all (m, l) are
-// loaded before the context length is known; entries of partitions past the
-// context are never used.
+// Lane p folds the (m, l) of partitions p, p+64, ...; each lane owns D/64
+// consecutive dimensions of the partial outputs.  The outputs of the first 64
+// partitions and all (m, l) are loaded before the context length is known;
+// entries of partitions past the context are never used.
 template <int DT, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
   constexpr int E = D / 64;
-  constexpr int PB = 8;
+  constexpr int PA = 64;
   typedef float floatE __attribute__((ext_vector_type(E)));
   // A lane's E partial-output elements (cache dtype) as one raw word.
   typedef typename std::conditional<E == 2, uint32_t, uint16_t>::type RawE;
@@ -456,10 +455,12 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
   const RawE* po = reinterpret_cast<const RawE*>(a.part_out + base * D + lane * E);
   const int64_t rstride = pstride * (D / E);  // RawE words between partitions
   const float2* pml = reinterpret_cast<const float2*>(a.part_ml) + base;
-  RawE pv[PB];
+  // The first PA partitions' outputs are all requested at once (indices
+  // clamped to the last partition of the grid, always inside the workspace),
+  // so up to PA partitions cost one memory round trip.
+  RawE pv[PA];
 #pragma unroll
-  for (int j = 0; j < PB; ++j)
-    pv[j] = j < P ? po[j * rstride] : RawE(0);
+  for (int j = 0; j < PA; ++j) pv[j] = po[min(j, P - 1) * rstride];
   const float2 ml_own = lane < P ? pml[lane * pstride] : make_float2(0.f, 0.f);
   const float m_own = ml_own.x, l_own = ml_own.y;
 
@@ -484,31 +485,23 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
 
-  // Batches of PB partitions, the next batch's outputs loaded while the
-  // current one is summed.  The loads are unconditional (indices clamped to
-  // the last partition of the grid, always inside the workspace) so that no
-  // wait for them lands at a branch join.
   floatE acc = {};
-  for (int p0 = 0; p0 < n; p0 += PB) {
-    RawE pn[PB];
 #pragma unroll
-    for (int j = 0; j < PB; ++j) pn[j] = po[min(p0 + PB + j, P - 1) * rstride];
-#pragma unroll
-    for (int j = 0; j < PB; ++j) {
-      const int p = p0 + j;
-      if (p < n) {
-        float w;
-        if (n <= 64) {
-          w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_own), p));
-        } else {
-          const float2 mlp = pml[p * pstride];
-          w = mlp.y * fast_exp2(mlp.x - M);
-        }
-        acc += w * widen(pv[j]);
+  for (int j = 0; j < PA; ++j) {
+    if (j < n) {
+      float w;
+      if (n <= 64) {
+        w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_own), j));
+      } else {
+        const float2 mlp = pml[j * pstride];
+        w = mlp.y * fast_exp2(mlp.x - M);
       }
+      acc += w * widen(pv[j]);
     }
-#pragma unroll
-    for (int j = 0; j < PB; ++j) pv[j] = pn[j];
+  }
+  for (int p = PA; p < n; ++p) {  // only with more than PA partitions
+    const float2 mlp = pml[p * pstride];
+    acc += (mlp.y * fast_exp2(mlp.x - M)) * widen(po[p * rstride]);
   }
   uint16_t* out = static_cast<uint16_t*>(a.out) + ((int64_t)seq * a.num_heads + h) * D + lane * E;
   const float inv = 1.0f / den;
