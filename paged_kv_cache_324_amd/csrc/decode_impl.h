@@ -56,6 +56,16 @@ namespace pa {
 // per workgroup, and the same two-round longest-first dispatch).
 // G = 4 or 8 (head_dim 64; at head_dim 128 the matrix-core kernel runs):
 // four wavefronts, four steps, two wavefronts per SIMD.
+// Wavefronts per decode_mfma_kernel workgroup: eight when a workgroup streams
+// at least kMfmaLongSpan tokens (its partition, or the whole context when
+// unsplit), four otherwise.  Eight halve the workgroups a compute unit holds
+// (175 VGPRs: two wavefronts per SIMD) and double each one's loads in flight,
+// which pays when spans are long and uneven (Llama-2-shaped batch, 4k-8k
+// contexts unsplit: 310 -> 293 us) but not for short partitions, whose
+// workgroups are dominated by their prologue and merge (512-token
+// partitions: 165 -> 192 us; 2048: 174 -> 179 us; 4096: equal).
+constexpr int kMfmaLongSpan = 4096;
+
 template <int G>
 struct DecodeShape {
   static constexpr int waves = G <= 2 ? 8 : 4;
@@ -511,7 +521,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
     reinterpret_cast<float2*>(a.out_ml)[(int64_t)seq * a.num_heads + h] = make_float2(M, den);
 }
 
-template <int DT, int BS, int G, bool ROPE>
+template <int DT, int BS, int G, int NW, bool ROPE>
 __global__ void decode_mfma_kernel(const DecodeArgs a);
 
 // Matrix cores take the score/value products once a KV head serves 4 or more
@@ -525,7 +535,11 @@ template <int DT, int D, int BS, int G, bool ROPE>
 void launch_partitions(const DecodeArgs& a, unsigned grid, hipStream_t s) {
   using Shape = DecodeShape<G>;
   if constexpr (decode_uses_mfma<D, G>()) {
-    hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, G, ROPE>), dim3(grid), dim3(256), 0, s, a);
+    if (a.part_tokens >= kMfmaLongSpan) {
+      hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, G, 8, ROPE>), dim3(grid), dim3(512), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, G, 4, ROPE>), dim3(grid), dim3(256), 0, s, a);
+    }
   } else {
     hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, Shape::waves, Shape::pf,
                                                 Shape::waves_per_eu, PA_DECODE_AUX, ROPE>),

@@ -9,7 +9,7 @@
 // instead of fp32 vector ALUs, which keeps GQA-8 decode bound by HBM rather
 // than by VALU issue.
 //
-// One workgroup (4 wavefronts) per (sequence, KV head, context partition).
+// One workgroup (NW wavefronts) per (sequence, KV head, context partition).
 // The partition is cut into 32-key steps taken round-robin by the four
 // wavefronts:
 //   S^T = K Q^T   16x16x32 MFMA, two 16-key groups per step.  A = K rows
@@ -49,16 +49,16 @@ constexpr float kMdLazyRescale = 8.0f;
 // then touch 16 distinct bank groups.
 __device__ __forceinline__ int md_vswz(int r) { return (2 * r) & 15; }
 
-template <int DT, int BS, int G, bool ROPE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int DT, int BS, int G, int NW, bool ROPE>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_mfma_kernel(const DecodeArgs a) {
   constexpr int D = 128;
   static_assert(G >= 1 && G <= 16, "heads of a group fill the 16 MFMA columns");
   static_assert(BS % 16 == 0, "a 16-key group lies in one block");
   // One V buffer per wavefront; at the end the same bytes hold that
   // wavefront's fp32 O^T (16 heads x 128 dims) for the merge.
-  __shared__ __attribute__((aligned(16))) unsigned char s_v[4][kMdStep];  // 32 KB
-  __shared__ float s_ml[4 * 16 * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v[NW][kMdStep];  // 8 KB per wavefront
+  __shared__ float s_ml[NW * 16 * 2];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;   // head (score / output column)
@@ -88,7 +88,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
     return bt[min(lbA + (kMdStepKeys * s + 16 * (lane & 1)) / BS, a.max_blocks - 1)];
   };
   const int32_t ids_first = load_ids(wave);
-  int32_t ids_next = load_ids(wave + 4);
+  int32_t ids_next = load_ids(wave + NW);
 
   // Q^T fragments: column = head col, dims 32 ks + 8 quad .. + 7.  Columns
   // past G repeat head h0 (finite scores in columns of their own, never
@@ -273,7 +273,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
     }
   };
 
-  // Merge the four wavefronts' (m, l, O) and write the partition.
+  // Merge the NW wavefronts' (m, l, O) and write the partition.
   auto merge = [&]() {
     float* s_o = reinterpret_cast<float*>(sv);  // this wavefront's [16][128]
 #pragma unroll
@@ -285,18 +285,18 @@ void decode_mfma_kernel(const DecodeArgs a) {
       s_ml[(wave * 16 + col) * 2 + 1] = lsum;
     }
     __syncthreads();
-    const float* s_all = reinterpret_cast<const float*>(&s_v[0][0]);  // [4][16][128]
+    const float* s_all = reinterpret_cast<const float*>(&s_v[0][0]);  // [NW][16][128]
     // The partition's rows of the G heads are contiguous in part_out.
     const int64_t prow = ((int64_t)seq * a.num_parts + part) * a.num_heads + h0;
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
       const int g = idx / D;
       const int d = idx - g * D;
       float M = s_ml[g * 2];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) M = fmaxf(M, s_ml[(w * 16 + g) * 2]);
+      for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[(w * 16 + g) * 2]);
       float den = 0.f, ov = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float f = fast_exp2(s_ml[(w * 16 + g) * 2] - M);
         den = fmaf(s_ml[(w * 16 + g) * 2 + 1], f, den);
         ov = fmaf(s_all[(w * 16 + g) * D + d], f, ov);
@@ -313,10 +313,10 @@ void decode_mfma_kernel(const DecodeArgs a) {
       const int g = threadIdx.x;
       float M = s_ml[g * 2];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) M = fmaxf(M, s_ml[(w * 16 + g) * 2]);
+      for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[(w * 16 + g) * 2]);
       float den = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
+      for (int w = 0; w < NW; ++w)
         den = fmaf(s_ml[(w * 16 + g) * 2 + 1], fast_exp2(s_ml[(w * 16 + g) * 2] - M), den);
       mlp[g] = make_float2(M, den);
     }
@@ -326,21 +326,21 @@ void decode_mfma_kernel(const DecodeArgs a) {
   int s = wave;
   if (s < nsteps) {
     issue(s, ids_first);
-    for (; s < nsteps; s += 4) {
-      // The ids of step s + 8 go out before the K/V of step s + 4, so waiting
+    for (; s < nsteps; s += NW) {
+      // The ids of step s + 2 NW go out before the K/V of step s + NW, so waiting
       // for ids never waits for K/V; loads past the partition are harmless
       // (clamped ids, size-0 resources), so every step sees the same loads in
       // flight.
-      const int32_t ids_after = load_ids(s + 8);
+      const int32_t ids_after = load_ids(s + 2 * NW);
       store_v();
       f32x4 sc[2];
       scores(sc);
-      issue(s + 4, ids_next);
+      issue(s + NW, ids_next);
       ids_next = ids_after;
       accumulate(sc, t0 + kMdStepKeys * s, t1c);
     }
   }
-  if (new_here && wave == (nsteps & 3)) {
+  if (new_here && wave == nsteps % NW) {
     // The new token, on the wavefront with the fewest steps: row 0 of a
     // step whose buffer resources span just its rows of key_new / value_new,
     // so every other row loads as zeros (and scores -inf).
