@@ -12,7 +12,7 @@
 // 2 KB run (the token-major 16-bit layout would leave 16 runs of 128 bytes).
 //
 // The structure is that of decode_mfma_kernel (decode_mfma_impl.h): one
-// workgroup of 4 wavefronts per (sequence, KV head, partition), 32-key steps
+// workgroup of 4 or 8 wavefronts per (sequence, KV head, partition), 32-key steps
 // taken round-robin, scores S^T = K Q^T on 16x16x32 MFMA and O^T += V^T P^T on
 // 16x16x16 MFMA from a transposed LDS tile, a merge of the wavefronts through
 // LDS.  What differs:
@@ -54,14 +54,14 @@ __device__ __forceinline__ u32x4 i8_to_16(uint32_t w0, uint32_t w1) {
   return u32x4{i8_pair<DT>(w0, 0), i8_pair<DT>(w0, 1), i8_pair<DT>(w1, 0), i8_pair<DT>(w1, 1)};
 }
 
-template <int DT, int BS, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int DT, int BS, int G, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_int8_kernel(const DecodeArgs a) {
   constexpr int D = 128;
   static_assert(G >= 1 && G <= 16, "heads of a group fill the 16 MFMA columns");
   static_assert(BS % 16 == 0, "a 16-key group lies in one block");
-  __shared__ __attribute__((aligned(16))) unsigned char s_v[4][kI8Step];  // 32 KB
-  __shared__ float s_ml[4 * 16 * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v[NW][kI8Step];  // 8 KB per wavefront
+  __shared__ float s_ml[NW * 16 * 2];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;
@@ -83,8 +83,8 @@ void decode_int8_kernel(const DecodeArgs a) {
     return bt[min(lbA + (kI8StepKeys * s + 16 * (lane & 1)) / BS, a.max_blocks - 1)];
   };
   const int32_t ids_first = load_ids(wave);
-  const int32_t ids_second = load_ids(wave + 4);
-  int32_t ids_next = load_ids(wave + 8);
+  const int32_t ids_second = load_ids(wave + NW);
+  int32_t ids_next = load_ids(wave + 2 * NW);
 
   // Q^T fragment for step ks: head col (columns past G repeat head h0), dims
   // 32 quad + 8 ks .. + 7, the order the key codes are loaded in.
@@ -100,7 +100,7 @@ void decode_int8_kernel(const DecodeArgs a) {
   if (L == 0) {
     if (part == 0) {
       uint16_t* o = static_cast<uint16_t*>(a.out) + ((int64_t)seq * a.num_heads + h0) * D;
-      for (int idx = threadIdx.x; idx < G * D; idx += 256) o[idx] = 0;
+      for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) o[idx] = 0;
     }
     return;
   }
@@ -240,35 +240,35 @@ void decode_int8_kernel(const DecodeArgs a) {
     }
   };
 
-  // Step s computes from one register set, which then takes step s + 8; the
-  // other set holds step s + 4.  Block ids run a step ahead of the loads that
+  // Step s computes from one register set, which then takes step s + 2 NW;
+  // the other set holds step s + NW.  Block ids run a step ahead of the loads that
   // use them.  Look-ahead loads are unconditional (clamped ids, size-0
   // resources past the partition), so every step waits for the same loads.
   const int nsteps = (t1 - t0 + kI8StepKeys - 1) / kI8StepKeys;
   auto step = [&](int s, Regs& r) {
-    const int32_t ids_after = load_ids(s + 12);
+    const int32_t ids_after = load_ids(s + 3 * NW);
     store_v(r);
     f32x4 sc[2], kscale[2], vscale[2];
     scores(r, sc, kscale, vscale);
-    issue(s + 8, ids_next, r);
+    issue(s + 2 * NW, ids_next, r);
     ids_next = ids_after;
     accumulate(sc, kscale, vscale, t0 + kI8StepKeys * s, t1);
   };
   int s = wave;
   if (s < nsteps) {
     issue(s, ids_first, ra);
-    issue(s + 4, ids_second, rb);
+    issue(s + NW, ids_second, rb);
     while (true) {
       step(s, ra);
-      s += 4;
+      s += NW;
       if (s >= nsteps) break;
       step(s, rb);
-      s += 4;
+      s += NW;
       if (s >= nsteps) break;
     }
   }
 
-  // Merge the four wavefronts' (m, l, O) and write the partition.
+  // Merge the NW wavefronts' (m, l, O) and write the partition.
   float* s_o = reinterpret_cast<float*>(sv);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
@@ -281,15 +281,15 @@ void decode_int8_kernel(const DecodeArgs a) {
   __syncthreads();
   const float* s_all = reinterpret_cast<const float*>(&s_v[0][0]);
   const int64_t prow = ((int64_t)seq * a.num_parts + part) * a.num_heads + h0;
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
     const int g = idx / D;
     const int d = idx - g * D;
     float M = s_ml[g * 2];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, s_ml[(w * 16 + g) * 2]);
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[(w * 16 + g) * 2]);
     float den = 0.f, ov = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float f = fast_exp2(s_ml[(w * 16 + g) * 2] - M);
       den = fmaf(s_ml[(w * 16 + g) * 2 + 1], f, den);
       ov = fmaf(s_all[(w * 16 + g) * D + d], f, ov);
@@ -305,10 +305,10 @@ void decode_int8_kernel(const DecodeArgs a) {
     const int g = threadIdx.x;
     float M = s_ml[g * 2];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, s_ml[(w * 16 + g) * 2]);
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[(w * 16 + g) * 2]);
     float den = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
+    for (int w = 0; w < NW; ++w)
       den = fmaf(s_ml[(w * 16 + g) * 2 + 1], fast_exp2(s_ml[(w * 16 + g) * 2] - M), den);
     reinterpret_cast<float2*>(a.part_ml)[prow + g] = make_float2(M, den);
   }
@@ -317,7 +317,11 @@ void decode_int8_kernel(const DecodeArgs a) {
 template <int DT, int BS, int G>
 hipError_t launch_int8_t(const DecodeArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_parts);
-  hipLaunchKernelGGL((decode_int8_kernel<DT, BS, G>), dim3(grid), dim3(256), 0, s, a);
+  if (a.part_tokens >= kMfmaLongSpan) {  // as for the 16-bit matrix-core kernel
+    hipLaunchKernelGGL((decode_int8_kernel<DT, BS, G, 8>), dim3(grid), dim3(512), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((decode_int8_kernel<DT, BS, G, 4>), dim3(grid), dim3(256), 0, s, a);
+  }
   if (a.num_parts > 1)
     hipLaunchKernelGGL((decode_merge_kernel<DT, 128>), dim3((unsigned)(a.num_seqs * a.num_heads)),
                        dim3(64), 0, s, a);
