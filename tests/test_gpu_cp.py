@@ -94,6 +94,18 @@ def test_decode_partial_matches_shard_oracle(dt, G, BS, partition):
         check_partial(o[n], ml[n], sh.oracle_partial(n), f"partial {dt} G{G} BS{BS} p{partition} shard {n}")
 
 
+@pytest.mark.parametrize("G,BS,partition", [(8, 16, 0), (4, 256, 0), (8, 32, 4096)])
+def test_decode_partial_long_shards(G, BS, partition):
+    """Shards of 4096+ tokens: the eight-wavefront matrix-core kernel in partial mode."""
+    Hkv = 2
+    b = make_batch(B=3, Hq=Hkv * G, Hkv=Hkv, D=128, BS=BS, dtype="bf16", scale=128 ** -0.5,
+                   seed=9470 + G + BS + partition, lens_range=(9000, 13000))
+    sh = Shards(b, 2, "contiguous")
+    o, ml = sh.partials(partition)
+    for n in range(2):
+        check_partial(o[n], ml[n], sh.oracle_partial(n), f"long partial G{G} BS{BS} p{partition} shard {n}")
+
+
 @pytest.mark.parametrize("D,G", [(64, 2), (64, 8), (128, 2)])
 def test_decode_partial_head_dims(D, G):
     b = make_batch(B=4, Hq=4 * G, Hkv=4, D=D, BS=32, dtype="f16", scale=D ** -0.5,

@@ -322,6 +322,47 @@ def test_decode_step_fused_length_edges(partition):
     assert np.array_equal(to_bits(d.k_cache[d.idx]), kc_ref)
 
 
+@pytest.mark.parametrize("name,partition", [("llama2_70b_decode_bs16", 0), ("long_splitk_decode", 0),
+                                            ("long_splitk_decode", 4096)])
+def test_decode_step_fused_long_spans_sampled(name, partition):
+    """Spans of 4096+ tokens run the eight-wavefront matrix-core kernel, which also takes
+    the new token on its wavefront with the fewest steps."""
+    b = make_config(name)
+    log(f"fused step {name} partition={partition}")
+    d = upload(b)
+    got = to_f64(_fused_step(b, d, partition))
+    rows = sorted(set([0, 1, b.B // 2, b.B - 1]))
+    ref, sel = _oracle_rows(b, rows)
+    mx, rel = check_close(got[sel], ref, f"fused {name} p={partition}")
+    log(f"  rows {rows}: max_abs={mx:.3e} rel_l2={rel:.3e}")
+    assert np.all(np.isfinite(got))
+    kc_ref, vc_ref = host_caches_after_write(b)
+    assert np.array_equal(to_bits(d.k_cache[d.idx]), kc_ref)
+    assert np.array_equal(to_bits(d.v_cache[d.idx]), vc_ref)
+
+
+@pytest.mark.parametrize("lens", [[5000, 4097, 4200, 6001], [4098, 4162, 4258, 4290]])
+def test_decode_step_fused_needle_on_new_token_long(lens):
+    """As below with 8 query heads per KV head and 4096+-token contexts (eight wavefronts;
+    the lengths give ceil((L-1)/32) % 8 = 5, 0, 4, 4 and 1, 3, 6, 7, the wavefront that takes
+    the new token)."""
+    G, Hkv = 8, 2
+    b = make_batch(B=len(lens), Hq=G * Hkv, Hkv=Hkv, D=128, BS=16, dtype="bf16", scale=1.0,
+                   seed=52, lens=lens, NB=2048)
+    one = to_u16(np.ones(1, np.float32), "bf16")[0]
+    hi = to_u16(np.array([100.0], np.float32), "bf16")[0]
+    lo = to_u16(np.array([-100.0], np.float32), "bf16")[0]
+    b.q[:] = 0
+    b.q[:, :, 0] = one
+    b.k_blocks[..., 0] = lo           # every cached key scores -100
+    b.key_new[:] = 0
+    b.key_new[..., 0] = hi            # the new key scores +100
+    got = to_bits(_fused_step(b, upload(b), 0))
+    for i in range(len(lens)):
+        for h in range(G * Hkv):
+            assert np.array_equal(got[i, h], b.value_new[i, h // G])
+
+
 def test_decode_step_fused_needle_on_new_token():
     """The new token is the needle: the output is exactly its value row."""
     lens = [700, 33, 1]
