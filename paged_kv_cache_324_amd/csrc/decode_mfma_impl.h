@@ -10,7 +10,7 @@
 // than by VALU issue.
 //
 // One workgroup (NW wavefronts) per (sequence, KV head, context partition).
-// The partition is cut into 32-key steps taken round-robin by the four
+// The partition is cut into 32-key steps taken round-robin by the NW
 // wavefronts:
 //   S^T = K Q^T   16x16x32 MFMA, two 16-key groups per step.  A = K rows
 //                 (16 keys x 32 dims), loaded straight from the cache into
@@ -29,7 +29,7 @@
 // LDS) the same registers take the loads of the wavefront's next step, whose
 // block ids were loaded a step earlier still; so one step per wavefront is
 // always in flight.
-// At the end the four wavefronts' (m, l, O) are merged through LDS and the
+// At the end the NW wavefronts' (m, l, O) are merged through LDS and the
 // partition writes `out` (unsplit context) or its normalised partial for the
 // merge kernel.
 #pragma once
