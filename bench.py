@@ -45,6 +45,13 @@ KERNEL_SOURCES_INT8 = ["paged_kv_cache_324_amd/csrc/decode_int8.hip",
                        "paged_kv_cache_324_amd/csrc/decode_impl.h",
                        "paged_kv_cache_324_amd/csrc/mfma.h",
                        "paged_kv_cache_324_amd/csrc/pa_device.h"]
+# Sources of the chunked-prefill kernel and of the fused rotary + cache-write kernel.
+KERNEL_SOURCES_PREFILL = ["paged_kv_cache_324_amd/csrc/prefill.hip",
+                          "paged_kv_cache_324_amd/csrc/prefill_impl.h",
+                          "paged_kv_cache_324_amd/csrc/mfma.h",
+                          "paged_kv_cache_324_amd/csrc/pa_device.h"]
+KERNEL_SOURCES_ROPE = ["paged_kv_cache_324_amd/csrc/rope_reshape.hip",
+                       "paged_kv_cache_324_amd/csrc/pa_device.h"]
 
 
 def kernel_source_sha(sources=None) -> str:
@@ -55,19 +62,25 @@ def kernel_source_sha(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str, partition: int, int8: bool = False):
-    """HBM bytes per decode launch from the committed counter summary, if it is current."""
-    tag = "_int8" if int8 else ""
-    path = os.path.join(PROFILES, f"decode_{workload}{tag}_p{partition}_counters.md")
+def traffic_from(summary: str, sources):
+    """HBM bytes per launch recorded in profiles/<summary>, while the hash of `sources`
+    still matches the one recorded with it (else None: the kernel changed since)."""
+    path = os.path.join(PROFILES, summary)
     if not os.path.exists(path):
         return None
     text = open(path).read()
     sha = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", text)
     val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    current = kernel_source_sha(KERNEL_SOURCES_INT8 if int8 else None)
-    if not sha or not val or sha.group(1) != current:
+    if not sha or not val or sha.group(1) != kernel_source_sha(sources):
         return None
     return float(val.group(1))
+
+
+def recorded_traffic(workload: str, partition: int, int8: bool = False):
+    """HBM bytes per decode launch from the committed counter summary, if it is current."""
+    tag = "_int8" if int8 else ""
+    return traffic_from(f"decode_{workload}{tag}_p{partition}_counters.md",
+                        KERNEL_SOURCES_INT8 if int8 else KERNEL_SOURCES)
 
 
 def cpu_baseline(b, budget_s: float = 10.0):
@@ -566,7 +579,9 @@ def main(argv=None) -> int:
                 "merge_GBps": round(achm, 2),
                 "roofline": {"bound": "hbm", "kernel": f"pa_decode_partial ({kern})",
                              "achieved": round(ach2, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                             "frac": round(ach2 / HBM_PEAK_GBPS, 4), "traffic": None}}
+                             "frac": round(ach2 / HBM_PEAK_GBPS, 4),
+                             "traffic": traffic_from(f"decode_{name}_cp{n}_counters.md",
+                                                     KERNEL_SOURCES)}}
             continue
         if variant == "graph":
             r2 = run_graph(pa, torch, b2, max(50, steps2), max(5, args.warmup // 4), dev)
@@ -596,7 +611,9 @@ def main(argv=None) -> int:
                 "plain_reshape_and_cache_us": _stats_us(r2["plain_ms"]),
                 "roofline": {"bound": "hbm", "kernel": "rope_reshape_kernel",
                              "achieved": round(ach2, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                             "frac": round(ach2 / HBM_PEAK_GBPS, 4), "traffic": None}}
+                             "frac": round(ach2 / HBM_PEAK_GBPS, 4),
+                             "traffic": traffic_from(f"rope_reshape_{name}_counters.md",
+                                                     KERNEL_SOURCES_ROPE)}}
             continue
         if variant == "int8":
             p2 = resolve_partition(pa, c2, b2)
@@ -630,7 +647,9 @@ def main(argv=None) -> int:
                 "algorithmic_gflop": round(flops / 1e9, 2),
                 "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tfl, 2),
                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}}
+                             "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "traffic": traffic_from(f"prefill_{name}_counters.md",
+                                                     KERNEL_SOURCES_PREFILL)}}
         else:
             p2 = resolve_partition(pa, c2, b2)
             r2 = run_decode(pa, torch, b2, p2, steps2, max(2, args.warmup // 4), False, dev)
