@@ -204,8 +204,7 @@ void decode_int8_kernel(const DecodeArgs a) {
     }
     float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    mx = max_xor32(max_xor16(mx)) * a.scale_log2;
     if (__builtin_amdgcn_ballot_w64(mx > m + kI8LazyRescale)) {
       const float m_new = fmaxf(m, mx);
       const float alpha = fast_exp2(m - m_new);
@@ -223,8 +222,7 @@ void decode_int8_kernel(const DecodeArgs a) {
         psum += p;
         sc[gr][i] = p * vscale[gr][i];  // the value scale, outside the denominator
       }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
+    psum = sum_xor32(sum_xor16(psum));
     lsum += psum;
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr) {

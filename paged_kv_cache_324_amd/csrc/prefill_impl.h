@@ -265,13 +265,7 @@ void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[sub][j]);
     }
-    {  // max with the partner lane l ^ 32 by a VALU lane swap (no LDS round trip): with both
-       // operands mx, v_permlane32_swap leaves the lower half's value in the first result
-       // and the upper half's in the second, on every lane
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                       false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
-    }
+    mx = max_xor32(mx) * a.scale_log2;  // partner lane l ^ 32, by a lane swap
     if (__builtin_amdgcn_read_exec() & __builtin_amdgcn_ballot_w64(mx > m + kLazyRescale)) {
       const float m_new = fmaxf(m, mx);
       const float alpha = fast_exp2(m - m_new);
