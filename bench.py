@@ -18,6 +18,7 @@ CPU oracle on the host cores.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -556,16 +557,24 @@ def main(argv=None) -> int:
     }
     secondary = {}
     for entry in [x for x in args.secondary.split(",") if x]:
+        # Hand the previous workload's pools (up to ~20 GB) back to the device, so that
+        # each entry's caches are fresh allocations rather than pieces of cached segments.
+        torch.cuda.synchronize(dev)
+        gc.collect()
+        torch.cuda.empty_cache()
         name, _, variant = entry.partition(":")
         c2 = CONFIGS[name]
         t_gen = time.perf_counter()
         b2 = make_config(name)
         print(f"[bench] generated {name} in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
               flush=True)
-        steps2 = max(5, args.steps // 10)
+        # Half the headline's steps and its full warm-up: with a tenth of them (20 steps,
+        # 5 warm-up) the secondary timings read 5-14% slow, the device still ramping up.
+        steps2 = max(5, args.steps // 2)
+        warm2 = max(2, args.warmup)
         if variant.startswith("cp"):
             n = int(variant[2:])
-            r2 = run_decode_cp(pa, torch, b2, n, steps2, max(2, args.warmup // 4), dev)
+            r2 = run_decode_cp(pa, torch, b2, n, steps2, warm2, dev)
             kb = r2["shard_kv_bytes"]
             ach2 = kb / (float(r2["kernel_ms"].mean()) * 1e-3) / 1e9
             achm = r2["merge_bytes"] / (float(r2["merge_ms"].mean()) * 1e-3) / 1e9
@@ -584,7 +593,7 @@ def main(argv=None) -> int:
                                                      KERNEL_SOURCES)}}
             continue
         if variant == "graph":
-            r2 = run_graph(pa, torch, b2, max(50, steps2), max(5, args.warmup // 4), dev)
+            r2 = run_graph(pa, torch, b2, max(50, steps2), max(5, warm2), dev)
             kv2 = b2.kv_bytes()
             secondary[entry] = {
                 "step": "rotary embedding + cache write + decode: two launches "
@@ -600,7 +609,7 @@ def main(argv=None) -> int:
                 "fused_effective_GBps": round(kv2 / (r2["fused_ms"] * 1e-3) / 1e9, 2)}
             continue
         if variant == "rope":
-            r2 = run_rope(pa, torch, b2, max(20, steps2), max(2, args.warmup // 4), dev)
+            r2 = run_rope(pa, torch, b2, max(20, steps2), warm2, dev)
             rb = rope_bytes(b2)
             ach2 = rb / (float(r2["kernel_ms"].mean()) * 1e-3) / 1e9
             secondary[entry] = {
@@ -617,7 +626,7 @@ def main(argv=None) -> int:
             continue
         if variant == "int8":
             p2 = resolve_partition(pa, c2, b2)
-            r2 = run_decode_int8(pa, torch, b2, p2, steps2, max(2, args.warmup // 4), dev)
+            r2 = run_decode_int8(pa, torch, b2, p2, steps2, warm2, dev)
             kb = int8_kv_bytes(b2)
             ach2 = kb / (float(r2["kernel_ms"].mean()) * 1e-3) / 1e9
             secondary[entry] = {
@@ -633,7 +642,7 @@ def main(argv=None) -> int:
                              "traffic": recorded_traffic(name, p2, int8=True)}}
             continue
         if c2["kind"] == "prefill":
-            r2 = run_prefill(pa, torch, b2, steps2, max(2, args.warmup // 4), dev)
+            r2 = run_prefill(pa, torch, b2, steps2, warm2, dev)
             flops = prefill_flops(b2)
             tfl = flops / (float(r2["kernel_ms"].mean()) * 1e-3) / 1e12
             secondary[name] = {
@@ -652,7 +661,7 @@ def main(argv=None) -> int:
                                                      KERNEL_SOURCES_PREFILL)}}
         else:
             p2 = resolve_partition(pa, c2, b2)
-            r2 = run_decode(pa, torch, b2, p2, steps2, max(2, args.warmup // 4), False, dev)
+            r2 = run_decode(pa, torch, b2, p2, steps2, warm2, False, dev)
             kv2 = b2.kv_bytes()
             ach2 = kv2 / (float(r2["kernel_ms"].mean()) * 1e-3) / 1e9
             secondary[name] = {
