@@ -65,6 +65,11 @@ namespace pa {
 // workgroups are dominated by their prologue and merge (512-token
 // partitions: 165 -> 192 us; 2048: 174 -> 179 us; 4096: equal).
 constexpr int kMfmaLongSpan = 4096;
+// Two wavefronts when contexts are cut into partitions of at most this many
+// tokens: each wavefront then takes more of its partition's few steps
+// (context-parallel shard at partition 256: 31.5 -> 30.8 us; long split-K at
+// 512: 165.6 -> 164.3 us).
+constexpr int kMfmaShortPartition = 512;
 
 template <int G>
 struct DecodeShape {
@@ -537,6 +542,8 @@ void launch_partitions(const DecodeArgs& a, unsigned grid, hipStream_t s) {
   if constexpr (decode_uses_mfma<D, G>()) {
     if (a.part_tokens >= kMfmaLongSpan) {
       hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, G, 8, ROPE>), dim3(grid), dim3(512), 0, s, a);
+    } else if (a.num_parts > 1 && a.part_tokens <= kMfmaShortPartition) {
+      hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, G, 2, ROPE>), dim3(grid), dim3(128), 0, s, a);
     } else {
       hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, G, 4, ROPE>), dim3(grid), dim3(256), 0, s, a);
     }

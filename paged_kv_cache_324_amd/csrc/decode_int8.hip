@@ -38,7 +38,6 @@ constexpr int kI8Row = 256;                   // bytes of one converted (16-bit)
 constexpr int kI8StepKeys = 32;
 constexpr int kI8Step = kI8StepKeys * kI8Row;
 constexpr float kI8LazyRescale = 8.0f;
-constexpr int kInt8ShortPartition = 512;  // tokens; see launch_int8_t
 
 __device__ __forceinline__ int i8_vswz(int r) { return (2 * r) & 15; }
 
@@ -318,12 +317,12 @@ hipError_t launch_int8_t(const DecodeArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_parts);
   // Wavefronts per workgroup: eight for spans of kMfmaLongSpan+ tokens (as for the
   // 16-bit matrix-core kernel); two for contexts cut into partitions of at most
-  // kInt8ShortPartition tokens, so that each wavefront takes more steps of its
+  // kMfmaShortPartition tokens, so that each wavefront takes more steps of its
   // short partition (long split-K INT8 decode at 512: 100.3 -> 96.4 us; unsplit
   // contexts of up to 2048 tokens lose with two: 62.1 -> 67.5 us); four otherwise.
   if (a.part_tokens >= kMfmaLongSpan) {
     hipLaunchKernelGGL((decode_int8_kernel<DT, BS, G, 8>), dim3(grid), dim3(512), 0, s, a);
-  } else if (a.num_parts > 1 && a.part_tokens <= kInt8ShortPartition) {
+  } else if (a.num_parts > 1 && a.part_tokens <= kMfmaShortPartition) {
     hipLaunchKernelGGL((decode_int8_kernel<DT, BS, G, 2>), dim3(grid), dim3(128), 0, s, a);
   } else {
     hipLaunchKernelGGL((decode_int8_kernel<DT, BS, G, 4>), dim3(grid), dim3(256), 0, s, a);
