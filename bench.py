@@ -569,7 +569,7 @@ def main(argv=None) -> int:
         print(f"[bench] generated {name} in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
               flush=True)
         # Half the headline's steps and its full warm-up: with a tenth of them (20 steps,
-        # 5 warm-up) the secondary timings read 5-14% slow, the device still ramping up.
+        # 5 warm-up) the secondary timings read 5-14% slower than in longer runs.
         steps2 = max(5, args.steps // 2)
         warm2 = max(2, args.warmup)
         if variant.startswith("cp"):
