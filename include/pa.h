@@ -327,6 +327,31 @@ int pa_decode_int8(void* out, const void* q, const void* k_codes, const void* v_
                    void* workspace, size_t workspace_bytes, int dtype, void* stream);
 
 /*
+ * pa_decode_step_int8: one decode step over an INT8 cache, i.e.
+ * pa_reshape_and_cache_int8 of one new token per sequence followed by
+ * pa_decode_int8, in a single kernel launch.  The new token of sequence i is
+ * logical position context_lens[i] - 1; its 16-bit rows key[i], value[i]
+ * ([num_seqs][num_kv_heads][head_dim], dtype) are quantised per (token, KV
+ * head) exactly as pa_reshape_and_cache_int8 quantises a row, stored at cache
+ * slot slot_mapping[i] (codes in k_codes / v_codes, scales in k_scales /
+ * v_scales; skipped when the slot is negative or outside the pool) and
+ * attended to as that position's dequantised K/V.  Cache positions below
+ * context_lens[i] - 1 are read from the caches.  Codes and scales written equal
+ * pa_reshape_and_cache_int8's bit for bit; the output equals
+ * pa_reshape_and_cache_int8 followed by pa_decode_int8 whenever slot_mapping[i]
+ * is the slot of position context_lens[i] - 1 in sequence i's block table,
+ * within rounding (the summation order differs).  Other arguments, workspace
+ * rules and supported shapes as for pa_decode_int8.
+ */
+int pa_decode_step_int8(void* out, const void* q, const void* key, const void* value,
+                        const int64_t* slot_mapping, void* k_codes, void* v_codes, float* k_scales,
+                        float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
+                        const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads,
+                        int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                        int max_context_len, float scale, int partition_size, void* workspace,
+                        size_t workspace_bytes, int dtype, void* stream);
+
+/*
  * pa_decode_order: host-side helper (HOST pointers, no GPU work).  Writes to
  * order[0..num_seqs) the sequence indices sorted by decreasing
  * context_lens[i], equal lengths in index order -- the longest-first visiting

@@ -92,6 +92,10 @@ def _declare(lib):
     lib.pa_decode_int8.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int,
                                    c_int, c_int, c_int, c_i64, c_int, c_int, c_f, c_int, c_vp, c_sz,
                                    c_int, c_vp]
+    lib.pa_decode_step_int8.restype = c_int
+    lib.pa_decode_step_int8.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                        c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_i64, c_int,
+                                        c_int, c_f, c_int, c_vp, c_sz, c_int, c_vp]
     lib.pa_rope_reshape_and_cache.restype = c_int
     lib.pa_rope_reshape_and_cache.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                               c_i64, c_int, c_int, c_int, c_int, c_i64, c_i64,
@@ -358,6 +362,33 @@ def pa_decode_step_rope(out, q, key, value, slot_mapping, positions, cos, sin, k
         _dev(slot_mapping, "slot_mapping", torch.int64), _dev(positions, "positions", torch.int64),
         _dev(cos, "cos", torch.float32), _dev(sin, "sin", torch.float32), cos.shape[0],
         k_cache.data_ptr(), v_cache.data_ptr(), _dev(block_tables, "block_tables", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32), order_ptr, B, Hq, Hkv, D, BS, NB,
+        block_tables.shape[1], int(max_context_len), float(scale), int(partition_size), ws_ptr,
+        ws_bytes, dt, _stream(q, stream)))
+    return out
+
+
+def pa_decode_step_int8(out, q, key, value, slot_mapping, k_codes, v_codes, k_scales, v_scales,
+                        block_tables, context_lens, scale: float, max_context_len: int,
+                        partition_size: int = 512, workspace=None, seq_order=None,
+                        stream=None) -> torch.Tensor:
+    """One decode step over an INT8 cache: quantise each sequence's new K/V token into its
+    slot and attend, in one launch (see :func:`pa_reshape_and_cache_int8`)."""
+    lib, B, Hq, Hkv, D, BS, NB, dt, ws_ptr, ws_bytes, order_ptr = _decode_common(
+        q, k_codes, v_codes, block_tables, context_lens, seq_order, out, max_context_len,
+        partition_size, workspace, cache_dtype=torch.int8, head_major=True)
+    if key.shape != (B, Hkv, D) or value.shape != key.shape or slot_mapping.shape != (B,):
+        raise ValueError("decode_step_int8: key/value must be [B][Hkv][D], slot_mapping [B]")
+    if k_scales.shape != (NB, Hkv, BS) or v_scales.shape != k_scales.shape:
+        raise ValueError("decode_step_int8: scales must be [num_blocks][num_kv_heads][block_size]")
+    _dev(key, "key", q.dtype)
+    _dev(value, "value", q.dtype)
+    ks = _dev(k_scales, "k_scales", torch.float32)
+    vs = _dev(v_scales, "v_scales", torch.float32)
+    _check(lib.pa_decode_step_int8(
+        out.data_ptr(), q.data_ptr(), key.data_ptr(), value.data_ptr(),
+        _dev(slot_mapping, "slot_mapping", torch.int64), k_codes.data_ptr(), v_codes.data_ptr(),
+        ks, vs, _dev(block_tables, "block_tables", torch.int32),
         _dev(context_lens, "context_lens", torch.int32), order_ptr, B, Hq, Hkv, D, BS, NB,
         block_tables.shape[1], int(max_context_len), float(scale), int(partition_size), ws_ptr,
         ws_bytes, dt, _stream(q, stream)))

@@ -107,6 +107,10 @@ void decode_int8_kernel(const DecodeArgs a) {
   if (t0 >= L) return;
   const int t1 = (int)min((int64_t)L, (int64_t)t0 + a.part_tokens);
   const int nparts_seq = 1 + (L - 1) / a.part_tokens;
+  // Fused step: the partition holding position L-1 reads only the cached
+  // positions before it; the new token is quantised and attended below.
+  const bool new_here = a.key_new != nullptr && t1 == L;
+  const int t1c = new_here ? L - 1 : t1;
 
   const int32_t nb32 = a.num_blocks > INT32_MAX ? INT32_MAX : (int32_t)a.num_blocks;
   const uint32_t row_bytes = (uint32_t)D;  // consecutive keys of one head
@@ -137,7 +141,7 @@ void decode_int8_kernel(const DecodeArgs a) {
       const int g0 = t0 + kI8StepKeys * s + 16 * gr;
       const int lb = g0 / BS;
       const int32_t blk = __builtin_amdgcn_readlane(ids, gr);
-      const int nv = min(16, t1 - g0);
+      const int nv = min(16, t1c - g0);
       const bool ok = nv > 0 && blk >= 0 && blk < nb32;
       const int off_in_blk = g0 - lb * BS;
       const uint64_t off = ok ? (uint64_t)(uint32_t)blk * block_bytes + (uint64_t)off_in_blk * row_bytes : 0ull;
@@ -242,7 +246,7 @@ void decode_int8_kernel(const DecodeArgs a) {
   // the other set holds step s + NW.  Block ids run a step ahead of the loads that
   // use them.  Look-ahead loads are unconditional (clamped ids, size-0
   // resources past the partition), so every step waits for the same loads.
-  const int nsteps = (t1 - t0 + kI8StepKeys - 1) / kI8StepKeys;
+  const int nsteps = (t1c - t0 + kI8StepKeys - 1) / kI8StepKeys;
   auto step = [&](int s, Regs& r) {
     const int32_t ids_after = load_ids(s + 3 * NW);
     store_v(r);
@@ -250,7 +254,7 @@ void decode_int8_kernel(const DecodeArgs a) {
     scores(r, sc, kscale, vscale);
     issue(s + 2 * NW, ids_next, r);
     ids_next = ids_after;
-    accumulate(sc, kscale, vscale, t0 + kI8StepKeys * s, t1);
+    accumulate(sc, kscale, vscale, t0 + kI8StepKeys * s, t1c);
   };
   int s = wave;
   if (s < nsteps) {
@@ -264,6 +268,75 @@ void decode_int8_kernel(const DecodeArgs a) {
       s += NW;
       if (s >= nsteps) break;
     }
+  }
+
+  if (new_here && wave == nsteps % NW) {
+    // The new token (position L-1), on the wavefront with the fewest steps.
+    // Lanes 0..15 quantise its key row and lanes 16..31 its value row, 8
+    // dimensions each, exactly as pa_reshape_and_cache_int8 does (scale = amax
+    // / 127, code = rint(x / scale), IEEE float32); the codes and scales are
+    // stored at the token's slot for later steps and attended from registers
+    // as a one-key step (every other key of the step is zeros and masked).
+    const int64_t nrow = ((int64_t)seq * a.num_kv_heads + kvh) * D;
+    const bool is_v = lane >= 16;
+    const int qsub = lane & 15;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (lane < 32)
+      x = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(is_v ? a.value_new : a.key_new) +
+                                         nrow)[qsub];
+    const float f[8] = {lo_f32<DT>(x.x), hi_f32<DT>(x.x), lo_f32<DT>(x.y), hi_f32<DT>(x.y),
+                        lo_f32<DT>(x.z), hi_f32<DT>(x.z), lo_f32<DT>(x.w), hi_f32<DT>(x.w)};
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
+#pragma unroll
+    for (int o2 = 8; o2 >= 1; o2 >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o2));  // 16-lane row
+    const float qscale = amax / 127.0f;
+    uint32_t pk[2] = {0u, 0u};
+    if (qscale > 0.f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int cq = (int)__builtin_rintf(f[e] / qscale);
+        pk[e >> 2] |= ((uint32_t)cq & 0xFFu) << (8 * (e & 3));
+      }
+    }
+    const int64_t slot = a.slot_mapping[seq];
+    if (lane < 32 && slot >= 0 && slot < a.num_slots) {
+      const int64_t sblk = slot / BS;
+      const int64_t srow = (sblk * a.num_kv_heads + kvh) * BS + (slot - sblk * BS);
+      int8_t* codes = static_cast<int8_t*>(is_v ? a.v_cache_w : a.k_cache_w);
+      *reinterpret_cast<uint2*>(codes + srow * D + 8 * qsub) = make_uint2(pk[0], pk[1]);
+      if (qsub == 0) (is_v ? a.v_scales_w : a.k_scales_w)[srow] = qscale;
+    }
+    // Registers of the one-key step, laid out as issue() loads a cached step:
+    // key 0 of group 0 is the new token.  Its key codes, dims 32 quad .. + 31,
+    // go to the lanes with col 0 (from quantising lanes 4 quad .. 4 quad + 3);
+    // its value codes, dims 16 (lane & 7) .. + 15, to lanes 0..7 (from lanes
+    // 16 + 2 (lane & 7) and the next); its scales to the quad-0 lanes.
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    Regs rn;
+    uint32_t kw[8], vw[4];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) kw[k] = (uint32_t)__shfl((int)pk[k & 1], 4 * quad + (k >> 1));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) vw[k] = (uint32_t)__shfl((int)pk[k & 1], 16 + 2 * (lane & 7) + (k >> 1));
+    const float ksn = __shfl(qscale, 0), vsn = __shfl(qscale, 16);
+    rn.kr[0][0] = col == 0 ? u32x4{kw[0], kw[1], kw[2], kw[3]} : zero4;
+    rn.kr[0][1] = col == 0 ? u32x4{kw[4], kw[5], kw[6], kw[7]} : zero4;
+    rn.kr[1][0] = zero4;
+    rn.kr[1][1] = zero4;
+    rn.vr[0][0] = lane < 8 ? u32x4{vw[0], vw[1], vw[2], vw[3]} : zero4;
+    rn.vr[0][1] = zero4;
+    rn.vr[1][0] = zero4;
+    rn.vr[1][1] = zero4;
+    rn.ksc[0] = quad == 0 ? u32x4{__float_as_uint(ksn), 0u, 0u, 0u} : zero4;
+    rn.vsc[0] = quad == 0 ? u32x4{__float_as_uint(vsn), 0u, 0u, 0u} : zero4;
+    rn.ksc[1] = zero4;
+    rn.vsc[1] = zero4;
+    store_v(rn);
+    f32x4 sc[2], kscale[2], vscale[2];
+    scores(rn, sc, kscale, vscale);
+    accumulate(sc, kscale, vscale, L - 1, L);
   }
 
   // Merge the NW wavefronts' (m, l, O) and write the partition.

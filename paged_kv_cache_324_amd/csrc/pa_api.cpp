@@ -222,6 +222,9 @@ struct NewTokens {
   const float* cos_table = nullptr;
   const float* sin_table = nullptr;
   int64_t max_position = 0;
+  // INT8 caches (pa_decode_step_int8): where the new rows' scales are stored.
+  float* k_scales = nullptr;
+  float* v_scales = nullptr;
 };
 
 // Per-row scales of an INT8 cache (pa_decode_int8); null for 16-bit caches.
@@ -252,6 +255,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (nt && (!nt->key || !nt->value || !nt->slot_mapping || !nt->k_cache || !nt->v_cache))
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (nt && i8 && (!nt->k_scales || !nt->v_scales))
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (i8 && (!i8->k || !i8->v)) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (out_ml && reinterpret_cast<uintptr_t>(out_ml) % 8 != 0)
@@ -290,6 +295,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.v_cache_w = nt ? nt->v_cache : nullptr;
   a.k_scales = i8 ? i8->k : nullptr;
   a.v_scales = i8 ? i8->v : nullptr;
+  a.k_scales_w = nt ? nt->k_scales : nullptr;
+  a.v_scales_w = nt ? nt->v_scales : nullptr;
   a.positions = nt ? nt->positions : nullptr;
   a.rope_cos = nt ? nt->cos_table : nullptr;
   a.rope_sin = nt ? nt->sin_table : nullptr;
@@ -496,6 +503,24 @@ int pa_decode_int8(void* out, const void* q, const void* k_codes, const void* v_
   if (head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "INT8 decode supports head_dim 128 only");
   const Int8Scales i8{k_scales, v_scales};
   return decode_impl(out, q, k_codes, v_codes, block_tables, context_lens, seq_order, nullptr, &i8, nullptr,
+                     num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
+                     workspace_bytes, dtype, stream);
+}
+
+int pa_decode_step_int8(void* out, const void* q, const void* key, const void* value,
+                        const int64_t* slot_mapping, void* k_codes, void* v_codes, float* k_scales,
+                        float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
+                        const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads,
+                        int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                        int max_context_len, float scale, int partition_size, void* workspace,
+                        size_t workspace_bytes, int dtype, void* stream) {
+  if (head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "INT8 decode supports head_dim 128 only");
+  NewTokens nt{key, value, slot_mapping, k_codes, v_codes};
+  nt.k_scales = k_scales;
+  nt.v_scales = v_scales;
+  const Int8Scales i8{k_scales, v_scales};
+  return decode_impl(out, q, k_codes, v_codes, block_tables, context_lens, seq_order, &nt, &i8, nullptr,
                      num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
                      workspace_bytes, dtype, stream);

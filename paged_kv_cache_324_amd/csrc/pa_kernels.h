@@ -82,6 +82,9 @@ struct DecodeArgs {
   void* v_cache_w;
   const float* k_scales;  // INT8 caches only: [num_blocks][num_kv_heads][block_size]
   const float* v_scales;
+  // INT8 fused step only (null otherwise): where the new token's scales are stored.
+  float* k_scales_w;
+  float* v_scales_w;
   // Fused rotary embedding (fused step only; null otherwise): the query and the
   // new key of sequence i are rotated by row positions[i] of the float32
   // tables [max_position][head_dim / 2] before use (rows outside the table:

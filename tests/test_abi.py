@@ -159,6 +159,30 @@ def test_decode_step_rejects_bad_arguments(lib):
     assert f(*bad) == -3
 
 
+def test_decode_step_int8_rejects_bad_arguments(lib):
+    f = lib.pa_decode_step_int8
+    # out, q, key, value, slot_mapping, k_codes, v_codes, k_scales, v_scales, tables, lens,
+    # seq_order, B, Hq, Hkv, D, BS, NB, max_blocks, max_len, scale, partition, ws, ws_bytes,
+    # dtype, stream
+    base = [P, P, P, P, P, P, P, P, P, P, P, None, 2, 16, 8, 128, 16, 100, 10, 160, 0.1, 0, None,
+            0, pa.PA_BF16, None]
+    bad = list(base)
+    bad[7] = None                          # k_scales
+    assert f(*bad) == -1 and "null" in lib.pa_last_error().decode()
+    bad = list(base)
+    bad[4] = None                          # slot_mapping
+    assert f(*bad) == -1 and "null" in lib.pa_last_error().decode()
+    bad = list(base)
+    bad[15] = 64                           # head_dim: INT8 decode takes 128 only
+    assert f(*bad) == -2
+    bad = list(base)
+    bad[21] = 32                           # needs a workspace
+    assert f(*bad) == -3
+    bad = list(base)
+    bad[12] = 0                            # no sequences: nothing to do
+    assert f(*bad) == 0
+
+
 def test_decode_order_is_longest_first_and_stable():
     import numpy as np
     lens = np.array([5, 9, 5, 0, 12, 9, 1], dtype=np.int32)
@@ -183,7 +207,7 @@ def test_bench_refuses_several_gpus():
 def test_new_entry_points_have_bindings():
     for name in ("pa_decode_partial", "pa_merge_partials", "pa_rope_reshape_and_cache",
                  "pa_decode_int8", "pa_reshape_and_cache_int8", "pa_copy_blocks",
-                 "pa_decode_partition_hint"):
+                 "pa_decode_partition_hint", "pa_decode_step_int8"):
         assert callable(getattr(pa, name)), name
 
 

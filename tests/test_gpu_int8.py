@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from oracle import int8_kv
-from paged_kv_cache_324_amd import pa_decode_int8, pa_reshape_and_cache_int8
+from paged_kv_cache_324_amd import pa_decode_int8, pa_decode_step_int8, pa_reshape_and_cache_int8
 from workloads import make_batch, make_config, to_u16
 
 from _gpu import bits_to_device, check_close, log, to_f64
@@ -34,7 +34,7 @@ def cached_rows(b):
 class Int8Batch:
     """Device and host INT8 caches holding the batch's cached tokens and this step's new ones."""
 
-    def __init__(self, b):
+    def __init__(self, b, write_new=True):
         self.b = b
         dt = torch.bfloat16 if b.dtype == "bf16" else torch.float16
         kr, vr, comp, phys = cached_rows(b)
@@ -43,7 +43,8 @@ class Int8Batch:
         self.vc = torch.zeros_like(self.kc)
         self.ks = torch.zeros((NB, Hkv, BS), dtype=torch.float32, device="cuda")
         self.vs = torch.zeros_like(self.ks)
-        for k, v, s in ((kr, vr, phys), (b.key_new, b.value_new, b.slot_mapping)):
+        pairs = ((kr, vr, phys), (b.key_new, b.value_new, b.slot_mapping))
+        for k, v, s in pairs if write_new else pairs[:1]:
             if len(s):
                 pa_reshape_and_cache_int8(bits_to_device(k, dt), bits_to_device(v, dt), self.kc,
                                           self.vc, self.ks, self.vs,
@@ -168,3 +169,68 @@ def test_int8_keeps_attention_close_to_16bit():
     rel = float(np.linalg.norm(got - ref16) / np.linalg.norm(ref16))
     log(f"int8 vs 16-bit attention: relative L2 {rel:.3e}")
     assert rel < 3e-2
+
+
+# ------------------------------------------------------------------ fused step
+def _step_int8(ib, partition):
+    """pa_decode_step_int8 on a cache that holds only the already-cached tokens."""
+    b = ib.b
+    dt = torch.bfloat16 if b.dtype == "bf16" else torch.float16
+    out = torch.empty_like(ib.q)
+    pa_decode_step_int8(out, ib.q, bits_to_device(b.key_new, dt), bits_to_device(b.value_new, dt),
+                        torch.from_numpy(b.slot_mapping).cuda(), ib.kc, ib.vc, ib.ks, ib.vs,
+                        ib.tables, ib.lens, b.scale, b.max_context_len, partition)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_new_slots(ib):
+    """The new tokens' codes and scales at their slots equal the oracle's quantisation."""
+    b = ib.b
+    phys = b.slot_mapping.astype(np.int64)
+    comp = b.slot_mapping_compact.astype(np.int64)
+    for dev, host in ((ib.kc, ib.hk), (ib.vc, ib.hv)):
+        got = dev[torch.from_numpy(phys // b.BS).cuda(), :, torch.from_numpy(phys % b.BS).cuda()]
+        assert np.array_equal(got.cpu().numpy(), host[comp // b.BS, :, comp % b.BS])
+    for dev, host in ((ib.ks, ib.hks), (ib.vs, ib.hvs)):
+        got = dev[torch.from_numpy(phys // b.BS).cuda(), :, torch.from_numpy(phys % b.BS).cuda()]
+        assert np.array_equal(got.cpu().numpy().view(np.uint32),
+                              host[comp // b.BS, :, comp % b.BS].view(np.uint32))
+
+
+STEP = [(dt, BS, G, p) for dt in ("bf16", "f16") for BS in (16, 256) for G in (1, 2, 4, 8)
+        for p in (0, 256)]
+
+
+@pytest.mark.parametrize("dt,BS,G,partition", STEP)
+def test_decode_step_int8_matches_oracle(dt, BS, G, partition):
+    Hkv = 2
+    b = make_batch(B=6, Hq=Hkv * G, Hkv=Hkv, D=128, BS=BS, dtype=dt, scale=128 ** -0.5,
+                   seed=9600 + STEP.index((dt, BS, G, partition)), lens_range=(1, 700))
+    ib = Int8Batch(b, write_new=False)
+    got = to_f64(_step_int8(ib, partition))
+    check_close(got, ib.oracle(), f"int8 step {dt} BS{BS} G{G} p{partition}")
+    _check_new_slots(ib)
+
+
+@pytest.mark.parametrize("partition", [0, 512, 32])
+def test_decode_step_int8_length_edges(partition):
+    """Lengths 1 (only the new token), block and partition edges, and 4096+ tokens (the
+    eight-wavefront kernel when unsplit, two wavefronts at partitions up to 512)."""
+    lens = [1, 2, 16, 17, 33, 512, 513, 4097, 5000]
+    b = make_batch(B=len(lens), Hq=8, Hkv=2, D=128, BS=16, dtype="bf16", scale=128 ** -0.5,
+                   seed=9650 + partition, lens=lens)
+    ib = Int8Batch(b, write_new=False)
+    got = to_f64(_step_int8(ib, partition))
+    check_close(got, ib.oracle(), f"int8 step edges p{partition}")
+    _check_new_slots(ib)
+
+
+def test_decode_step_int8_qwen3_shaped_sampled():
+    b = make_config("qwen3_0p6b_decode")
+    ib = Int8Batch(b, write_new=False)
+    got = to_f64(_step_int8(ib, 0))
+    rows = [0, 1, 63, 64, 127]
+    mx, rel = check_close(got[rows], ib.oracle(rows), "int8 step qwen3-shaped")
+    log(f"  rows {rows}: max_abs={mx:.3e} rel_l2={rel:.3e}")
+    _check_new_slots(ib)
