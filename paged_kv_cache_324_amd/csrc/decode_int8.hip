@@ -247,6 +247,14 @@ void decode_int8_kernel(const DecodeArgs a) {
   // use them.  Look-ahead loads are unconditional (clamped ids, size-0
   // resources past the partition), so every step waits for the same loads.
   const int nsteps = (t1c - t0 + kI8StepKeys - 1) / kI8StepKeys;
+  // The new token's 16-bit rows (lanes 0..15 key, 16..31 value, 16 bytes each)
+  // are fetched before the cached steps, on the wavefront that attends to it.
+  u32x4 new_x = {0u, 0u, 0u, 0u};
+  if (new_here && wave == nsteps % NW && lane < 32) {
+    const int64_t nrow = ((int64_t)seq * a.num_kv_heads + kvh) * D;
+    new_x = reinterpret_cast<const u32x4*>(
+        static_cast<const uint16_t*>(lane >= 16 ? a.value_new : a.key_new) + nrow)[lane & 15];
+  }
   auto step = [&](int s, Regs& r) {
     const int32_t ids_after = load_ids(s + 3 * NW);
     store_v(r);
@@ -277,13 +285,9 @@ void decode_int8_kernel(const DecodeArgs a) {
     // / 127, code = rint(x / scale), IEEE float32); the codes and scales are
     // stored at the token's slot for later steps and attended from registers
     // as a one-key step (every other key of the step is zeros and masked).
-    const int64_t nrow = ((int64_t)seq * a.num_kv_heads + kvh) * D;
     const bool is_v = lane >= 16;
     const int qsub = lane & 15;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (lane < 32)
-      x = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(is_v ? a.value_new : a.key_new) +
-                                         nrow)[qsub];
+    const u32x4 x = new_x;
     const float f[8] = {lo_f32<DT>(x.x), hi_f32<DT>(x.x), lo_f32<DT>(x.y), hi_f32<DT>(x.y),
                         lo_f32<DT>(x.z), hi_f32<DT>(x.z), lo_f32<DT>(x.w), hi_f32<DT>(x.w)};
     float amax = 0.f;
