@@ -2,18 +2,25 @@
 """Benchmark of the paged-attention decode step on one MI355X.
 
 A step is one pass of the decode hot path over one synthetic batch already
-resident in HBM: ``pa_reshape_and_cache`` writes each sequence's new K/V token
-into its cache slot, then ``pa_decode`` (partition kernel + partition merge
-kernel) attends every query head over its paged context.  The default workload is the
-Qwen3-0.6B-shaped decode batch (128 sequences, 16 query / 8 KV heads, head_dim
-128, 16-token blocks shuffled over a 300k-block pool, context lengths uniform
-in [200, 2048], bf16).
+resident in HBM: each sequence's new K/V token is stored into its cache slot and
+every query head attends over its paged context (``pa_decode_step``, one
+launch; with ``--unfused``, ``pa_reshape_and_cache`` then ``pa_decode``).  The
+default workload is the Qwen3-0.6B-shaped decode batch (128 sequences, 16 query
+/ 8 KV heads, head_dim 128, 16-token blocks shuffled over a 300k-block pool,
+context lengths uniform in [200, 2048], bf16).
 
-Prints one JSON line.  ``value`` is effective KV GB/s: the logical K+V bytes
-the batch attends over (every context token of every sequence, once) divided
-by the step time.  The ``roofline`` object reports the decode kernels alone,
-timed with HIP events on the stream they run on; ``cpu_baseline`` times the
-CPU oracle on the host cores.
+Protocol: ``--warmup`` untimed steps, then exactly ``--steps`` timed steps, each
+preceded by a flush read of ``--flush-mb`` MiB (so no K/V byte comes from the
+Infinity Cache or an L2) and bracketed by HIP events on the stream it runs on.
+``value`` is effective KV GB/s over the median step: the logical K+V bytes the
+batch attends over (every context token of every sequence, once) divided by the
+step time; ``roofline.achieved`` is the same bytes over the mean of the same
+durations.  Warm back-to-back steps, a streaming-read ceiling and (for split
+contexts) the partition and merge kernels timed on their own are reported as
+labelled extras; ``cpu_baseline`` times the CPU oracle on the host cores, and
+``parity`` compares the step's output with the oracle's.
+
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -84,8 +91,9 @@ def recorded_traffic(workload: str, partition: int, int8: bool = False):
                         KERNEL_SOURCES_INT8 if int8 else KERNEL_SOURCES)
 
 
-def cpu_baseline(b, budget_s: float = 10.0):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+def cpu_baseline(b, budget_s: float = 10.0, gpu_out_bits=None):
+    """The oracle, as it stands, on a bounded sample of the same workload.  With the GPU
+    step's output given, the first pass's oracle output also yields the headline parity."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -94,11 +102,17 @@ def cpu_baseline(b, budget_s: float = 10.0):
         blas_threads = 1
     kc, vc = b.k_blocks.copy(), b.v_blocks.copy()
     reps, kv, seqs = 0, 0, 0
+    parity = None
     wall0, cpu0 = time.perf_counter(), time.process_time()
     # One pass over the whole batch, then more passes while the budget lasts.
     while True:
         oracle.reshape_and_cache(b.key_new, b.value_new, kc, vc, b.slot_mapping_compact)
-        oracle.paged_decode(b.q, kc, vc, b.block_tables_compact, b.context_lens, b.scale, b.dtype)
+        ref = oracle.paged_decode(b.q, kc, vc, b.block_tables_compact, b.context_lens, b.scale,
+                                  b.dtype)
+        if parity is None and gpu_out_bits is not None:
+            t_par = time.perf_counter()
+            parity = parity_stats(gpu_out_bits, ref, b.dtype)
+            wall0 += time.perf_counter() - t_par          # not part of the oracle's time
         reps += 1
         kv += b.kv_bytes()
         seqs += b.B
@@ -111,12 +125,31 @@ def cpu_baseline(b, budget_s: float = 10.0):
             "sample": f"{reps} full pass(es) of the {b.B}-sequence batch (reshape_and_cache + "
                       f"float64 decode), {wall:.1f} s wall, {cpu:.1f} s CPU",
             "seqs_per_s": round(seqs / wall, 2),
-            "host_cpus_visible": len(os.sched_getaffinity(0))}
+            "host_cpus_visible": len(os.sched_getaffinity(0))}, parity
 
 
 def _stats_us(ms):
-    return {"mean": round(float(np.mean(ms)) * 1e3, 2), "p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
-            "p50": round(float(np.median(ms)) * 1e3, 2), "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)}
+    ms = np.asarray(ms, dtype=np.float64)
+    return {"n": int(ms.size), "mean": round(float(np.mean(ms)) * 1e3, 2),
+            "p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
+            "p50": round(float(np.median(ms)) * 1e3, 2),
+            "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)}
+
+
+def parity_stats(got_bits, ref, dtype):
+    """Headline parity, computed in the CPU-baseline leg from the oracle output it has just
+    produced: max-abs and relative L2 of the GPU output against the float64 oracle, the
+    count of |o_ref| >= 4, and the largest error in excess of rounding o_ref to 16 bits."""
+    import oracle
+    from workloads import to_u16
+    got = oracle.decode_u16(got_bits, dtype)
+    err = np.abs(got - ref)
+    rounded = oracle.decode_u16(to_u16(ref.astype(np.float32), dtype), dtype)
+    return {"what": "headline step output vs the float64 oracle, every element",
+            "max_abs": float(err.max()), "rel_l2": float(np.linalg.norm(got - ref) / np.linalg.norm(ref)),
+            "n_ref_abs_ge_4": int((np.abs(ref) >= 4).sum()),
+            "max_excess_over_16bit_rounding": float((err - np.abs(rounded - ref)).max()),
+            "bar": {"max_abs": 1.5e-2, "rel_l2": 5e-3}}
 
 
 def prefill_flops(b) -> float:
@@ -149,26 +182,80 @@ def upload(torch, b, dev):
         qsl=torch.from_numpy(b.query_start_loc).to(dev))
 
 
-def _timed(torch, fn, steps):
-    """Wall time of `steps` back-to-back calls, nothing else on the stream."""
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        fn()
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps * 1e3
+class Timer:
+    """The timing protocol.  A timed call is preceded by a flush: a read of a buffer of
+    `flush_mb` MiB (default 1 GiB, four times the 256 MB Infinity Cache), so no operand
+    is served from the MALL or an L2, and, being a read, it leaves no dirty line to be
+    written back during the call.  HIP events recorded on the stream the call is enqueued
+    on bracket the call alone."""
+
+    def __init__(self, torch, dev, flush_mb: int):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream(dev)
+        self.flush_bytes = max(1, int(flush_mb)) << 20
+        self.flush_buf = torch.ones(self.flush_bytes // 4, dtype=torch.int32, device=dev)
+
+    def flush(self):
+        self.flush_buf.sum()
+
+    def _bracket(self, fn, n, flush):
+        torch = self.torch
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        torch.cuda.synchronize()
+        for s, e in ev:
+            if flush:
+                self.flush()
+            s.record(self.stream)
+            fn()
+            e.record(self.stream)
+        torch.cuda.synchronize()
+        return np.array([s.elapsed_time(e) for s, e in ev])
+
+    def cold(self, fn, n):
+        """Durations (ms) of n calls, each after a flush."""
+        return self._bracket(fn, n, True)
+
+    def warm(self, fn, n):
+        """Durations (ms) of n event-bracketed calls issued back to back."""
+        return self._bracket(fn, n, False)
+
+    def back_to_back(self, fn, n):
+        """Wall time per call (ms) of n calls issued back to back, nothing else on the stream."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n * 1e3
+
+    def warmup(self, fn, calls: int, min_ms: float = 0.0):
+        """At least `calls` calls, and more until at least `min_ms` of them have run."""
+        torch = self.torch
+        t0 = time.perf_counter()
+        done = 0
+        while done < calls or (time.perf_counter() - t0) * 1e3 < min_ms:
+            for _ in range(max(1, calls if done < calls else 16)):
+                fn()
+                done += 1
+            torch.cuda.synchronize()
+
+    def stream_read_ceiling(self):
+        """A streaming read of the flush buffer (torch's int32 sum), as a reference rate
+        for what a read-only kernel reaches on this device; never used as a denominator."""
+        for _ in range(3):
+            self.flush()
+        ms = self.warm(self.flush, 10)
+        return {"kernel": f"torch.sum over {self.flush_bytes >> 20} MiB of int32 (a streaming read)",
+                "GBps": round(self.flush_bytes / (float(np.median(ms)) * 1e-3) / 1e9, 1),
+                "us_p50": round(float(np.median(ms)) * 1e3, 2)}
 
 
-def _events(torch, fn, steps, stream):
-    """Per-call durations (ms) of fn, each bracketed by HIP events on `stream`."""
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for s, e in ev:
-        s.record(stream)
-        fn()
-        e.record(stream)
-    torch.cuda.synchronize()
-    return np.array([s.elapsed_time(e) for s, e in ev])
+# Secondary workloads run a fixed number of cold steps after a time-based warm-up,
+# independent of --steps, so a short driver run reports them as a long one does.
+SECONDARY_STEPS = 50
+SECONDARY_WARMUP_MS = 100.0
 
 
 def resolve_partition(pa, cfg, b):
@@ -178,11 +265,15 @@ def resolve_partition(pa, cfg, b):
     return pa.pa_decode_partition_hint(b.B, b.Hkv, b.max_context_len, b.BS)
 
 
-def run_decode(pa, torch, b, partition, steps, warmup, unfused, dev, cold_iters=0):
+def run_decode(pa, torch, b, partition, steps, warmup, unfused, dev, timer, warmup_ms=0.0):
+    """Decode steps on the batch: `warmup` untimed steps, then exactly `steps` cold steps
+    (the timed region), then the labelled extras: warm back-to-back steps and, for a split
+    decode, its two phases (pa_decode_partitions cold, pa_decode_merge over the partials
+    it left) timed on their own."""
     d = upload(torch, b, dev)
     out = torch.empty_like(d.q)
     workspace = pa.decode_workspace(b.B, b.Hq, b.D, b.max_context_len, partition, dev)
-    stream = torch.cuda.current_stream(dev)
+    stream = timer.stream
     # Longest-first visiting order of the sequences, computed on the host from
     # the lengths the caller knows (the library's pa_decode_order).
     order = torch.from_numpy(pa.pa_decode_order(b.context_lens)).to(dev)
@@ -201,28 +292,36 @@ def run_decode(pa, torch, b, partition, steps, warmup, unfused, dev, cold_iters=
                               d.tables, d.lens, b.scale, b.max_context_len, partition,
                               workspace=workspace, seq_order=order, stream=stream)
 
-    for _ in range(warmup):
-        step()
-    ms = _timed(torch, step, steps)                       # the timed region
-    kernel_ms = _events(torch, decode if unfused else step, steps, stream)
-    # Cold calls: a 1 GiB read (four times the 256 MB Infinity Cache) before
-    # each one, so no K/V byte is served from the MALL or an L2, and no dirty
-    # line is left to be written back during the call; only the call is timed.
-    cold = []
-    if cold_iters > 0:
-        flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
-        for _ in range(cold_iters):
-            flush.sum()
-            cold.append(float(_events(torch, decode if unfused else step, 1, stream)[0]))
-        del flush
+    timer.warmup(step, warmup, warmup_ms)
+    step_ms = timer.cold(step, steps)                     # the timed region
+    out_bits = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    warm_ms = timer.back_to_back(step, steps)
+    split = bool(partition) and b.max_context_len > partition
+    phases = None
+    if split:
+        def partitions():
+            pa.pa_decode_partitions(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, b.scale,
+                                    b.max_context_len, partition, workspace=workspace,
+                                    seq_order=order, stream=stream)
+
+        def merge():
+            pa.pa_decode_merge(out, d.lens, b.max_context_len, partition, workspace,
+                               seq_order=order, stream=stream)
+
+        k2 = timer.cold(partitions, steps)
+        partitions()
+        phases = {"k2_partitions_us": _stats_us(k2),
+                  "k3_merge_us": _stats_us(timer.warm(merge, steps)),
+                  "note": "k2: pa_decode_partitions alone, cold (no new-token store); k3: "
+                          "pa_decode_merge alone over the partials k2 left, back to back "
+                          "(the partials resident, as after k2 in a step)"}
     # The library runs the matrix-core kernel for 4+ query heads per KV head at
     # head_dim 128, the vector kernel otherwise.
     kern = "decode_mfma_kernel" if (b.G >= 4 and b.D == 128) else "decode_partition_kernel"
     name = ("pa_decode" if unfused else "pa_decode_step") + (
-        f" ({kern} + merge kernel)" if partition and b.max_context_len > partition else
-        f" (one {kern} launch)")
-    return {"ms_per_step": ms, "kernel_ms": kernel_ms, "kernel_name": name,
-            "cold_ms": np.array(cold)}
+        f" ({kern} + merge kernel)" if split else f" (one {kern} launch)")
+    return {"step_ms": step_ms, "warm_ms": warm_ms, "kernel_name": name, "phases": phases,
+            "out_bits": out_bits}
 
 
 def int8_kv_bytes(b) -> int:
@@ -231,7 +330,7 @@ def int8_kv_bytes(b) -> int:
     return int(b.context_lens.astype(np.int64).sum()) * b.Hkv * (b.D + 4) * 2
 
 
-def run_decode_int8(pa, torch, b, partition, steps, warmup, dev):
+def run_decode_int8(pa, torch, b, partition, steps, dev, timer):
     """Decode over an INT8 cache: each step quantises the new tokens into their slots and
     attends, in one launch (pa_decode_step_int8); the same step as two launches
     (pa_reshape_and_cache_int8, pa_decode_int8) is timed beside it.  The cache is filled
@@ -262,7 +361,7 @@ def run_decode_int8(pa, torch, b, partition, steps, warmup, dev):
     lens = torch.from_numpy(b.context_lens).to(dev)
     out = torch.empty_like(q)
     workspace = pa.decode_workspace(b.B, b.Hq, b.D, b.max_context_len, partition, dev)
-    stream = torch.cuda.current_stream(dev)
+    stream = timer.stream
     order = torch.from_numpy(pa.pa_decode_order(b.context_lens)).to(dev)
     torch.cuda.synchronize(dev)
 
@@ -279,20 +378,20 @@ def run_decode_int8(pa, torch, b, partition, steps, warmup, dev):
                                b.max_context_len, partition, workspace=workspace,
                                seq_order=order, stream=stream)
 
-    # Two rounds of (fused, two launches), each after its warm-up; the second round is
-    # reported, so neither variant is timed first on a freshly filled cache.
-    for _ in range(2):
-        for _ in range(warmup):
-            step()
-        ms = _timed(torch, step, steps)
-        for _ in range(warmup):
-            two_launches()
-        ms_two = _timed(torch, two_launches, steps)
-    kernel_ms = _events(torch, step, steps, stream)
+    timer.warmup(step, 5, SECONDARY_WARMUP_MS)
+    step_ms = timer.cold(step, steps)
+    timer.warmup(two_launches, 5, SECONDARY_WARMUP_MS)
+    two_ms = timer.cold(two_launches, steps)
+    split = bool(partition) and b.max_context_len > partition
+    merge_ms = None
+    if split:
+        step()
+        merge_ms = timer.warm(lambda: pa.pa_decode_merge(out, lens, b.max_context_len, partition,
+                                                         workspace, seq_order=order,
+                                                         stream=stream), steps)
     name = "pa_decode_step_int8 (decode_int8_kernel" + (
-        " + merge kernel)" if partition and b.max_context_len > partition else ", one launch)")
-    return {"ms_per_step": ms, "kernel_ms": kernel_ms, "kernel_name": name,
-            "two_launch_ms_per_step": ms_two}
+        " + merge kernel)" if split else ", one launch)")
+    return {"step_ms": step_ms, "two_launch_ms": two_ms, "kernel_name": name, "merge_ms": merge_ms}
 
 
 def contiguous_shard(b, nshards, s):
@@ -311,7 +410,7 @@ def contiguous_shard(b, nshards, s):
     return tables, lens
 
 
-def run_decode_cp(pa, torch, b, nshards, steps, warmup, dev):
+def run_decode_cp(pa, torch, b, nshards, steps, dev, timer):
     """Context-parallel decode as one device of an nshards-way group sees it: the partial
     decode of its shard (the first, which holds the most tokens) at its real shape, then
     the merge of all nshards partial rows.  All shards' partials are computed once
@@ -333,7 +432,7 @@ def run_decode_cp(pa, torch, b, nshards, steps, warmup, dev):
                              b.scale, mx, part, workspace=ws, seq_order=shards[-1][5])
     tables, lens_d, mx, part, ws, order, lens = shards[0]
     out = torch.empty_like(d.q)
-    stream = torch.cuda.current_stream(dev)
+    stream = timer.stream
     torch.cuda.synchronize(dev)
 
     def partial():
@@ -347,13 +446,12 @@ def run_decode_cp(pa, torch, b, nshards, steps, warmup, dev):
         partial()
         merge()
 
-    for _ in range(warmup):
-        step()
-    ms = _timed(torch, step, steps)
+    timer.warmup(step, 5, SECONDARY_WARMUP_MS)
+    step_ms = timer.cold(step, steps)
     shard_bytes = int(lens.astype(np.int64).sum()) * b.Hkv * b.D * 2 * 2
     merge_bytes = b.B * b.Hq * (nshards * (b.D * 2 + 8) + b.D * 2)
-    return {"ms_per_step": ms, "kernel_ms": _events(torch, partial, steps, stream),
-            "merge_ms": _events(torch, merge, steps, stream), "partition_size": part,
+    return {"step_ms": step_ms, "partial_ms": timer.cold(partial, steps),
+            "merge_ms": timer.warm(merge, steps), "partition_size": part,
             "shard_kv_bytes": shard_bytes, "merge_bytes": merge_bytes,
             "shard_tokens": [int(lens.min()), int(lens.max())]}
 
@@ -366,7 +464,7 @@ def rope_bytes(b) -> int:
     return T * (b.Hq * b.D * 2 * 2 + b.Hkv * b.D * 2 * 4 + b.D // 2 * 4 * 2)
 
 
-def run_rope(pa, torch, b, steps, warmup, dev):
+def run_rope(pa, torch, b, steps, dev, timer):
     """pa_rope_reshape_and_cache over the workload's new tokens at their positions (queries
     rotated in place), beside the plain pa_reshape_and_cache of the same tokens."""
     from workloads import rope_tables
@@ -378,7 +476,7 @@ def run_rope(pa, torch, b, steps, warmup, dev):
     cos_d, sin_d = torch.from_numpy(cos).to(dev), torch.from_numpy(sin).to(dev)
     pos_d = torch.from_numpy(pos).to(dev)
     q = d.q if d.q.shape[0] == T else torch.zeros((T, b.Hq, b.D), dtype=d.q.dtype, device=dev)
-    stream = torch.cuda.current_stream(dev)
+    stream = timer.stream
 
     def fused():
         pa.pa_rope_reshape_and_cache(q, d.key_new, d.value_new, d.k_cache, d.v_cache, pos_d, cos_d,
@@ -387,14 +485,13 @@ def run_rope(pa, torch, b, steps, warmup, dev):
     def plain():
         pa.pa_reshape_and_cache(d.key_new, d.value_new, d.k_cache, d.v_cache, d.slot, stream=stream)
 
-    for _ in range(warmup):
-        fused()
-    ms = _timed(torch, fused, steps)
-    return {"ms_per_step": ms, "kernel_ms": _events(torch, fused, steps, stream),
-            "plain_ms": _events(torch, plain, steps, stream), "tokens": T}
+    timer.warmup(fused, 5, SECONDARY_WARMUP_MS)
+    fused_ms = timer.cold(fused, steps)
+    timer.warmup(plain, 5, SECONDARY_WARMUP_MS)
+    return {"step_ms": fused_ms, "plain_ms": timer.cold(plain, steps), "tokens": T}
 
 
-def run_graph(pa, torch, b, steps, warmup, dev):
+def run_graph(pa, torch, b, steps, warmup, dev, timer):
     """A serving-style decode step: the rotary embedding of q and of the new key, the cache
     write of the new key and value, and decode.  Timed as two launches
     (pa_rope_reshape_and_cache, then pa_decode) and as the one fused launch
@@ -428,13 +525,13 @@ def run_graph(pa, torch, b, steps, warmup, dev):
                 fn()
         torch.cuda.current_stream(dev).wait_stream(side)
         torch.cuda.synchronize(dev)
-        eager_ms = _timed(torch, fn, steps)
+        eager_ms = timer.back_to_back(fn, steps)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             fn()
         for _ in range(warmup):
             g.replay()
-        return eager_ms, _timed(torch, g.replay, steps)
+        return eager_ms, timer.back_to_back(g.replay, steps)
 
     eager_ms, graph_ms = eager_and_graph(step)
     fused_ms, fused_graph_ms = eager_and_graph(fused)
@@ -442,10 +539,10 @@ def run_graph(pa, torch, b, steps, warmup, dev):
             "fused_graph_ms": fused_graph_ms, "partition_size": partition}
 
 
-def run_prefill(pa, torch, b, steps, warmup, dev):
+def run_prefill(pa, torch, b, steps, dev, timer):
     d = upload(torch, b, dev)
     out = torch.empty_like(d.q)
-    stream = torch.cuda.current_stream(dev)
+    stream = timer.stream
     order = torch.from_numpy(pa.pa_decode_order(b.context_lens)).to(dev)
 
     def reshape():
@@ -459,19 +556,141 @@ def run_prefill(pa, torch, b, steps, warmup, dev):
         reshape()
         prefill()
 
-    for _ in range(warmup):
-        step()
-    ms = _timed(torch, step, steps)
-    return {"ms_per_step": ms, "kernel_ms": _events(torch, prefill, steps, stream),
-            "reshape_ms": _events(torch, reshape, steps, stream)}
+    timer.warmup(step, 5, SECONDARY_WARMUP_MS)
+    step_ms = timer.cold(step, steps)
+    return {"step_ms": step_ms, "prefill_ms": timer.cold(prefill, steps),
+            "reshape_ms": timer.cold(reshape, steps)}
+
+
+def _p50(ms) -> float:
+    return float(np.median(ms))
+
+
+def _hbm_roofline(kernel, nbytes, ms, traffic):
+    """Algorithmic bytes over the mean duration of the same timed calls."""
+    achieved = nbytes / (float(np.mean(ms)) * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic}
+
+
+def secondary_entry(pa, torch, entry, dev, timer):
+    """One entry of the secondary report, measured by the same cold protocol with a fixed
+    number of steps and a time-based warm-up."""
+    from workloads import CONFIGS, make_config
+    name, _, variant = entry.partition(":")
+    c2 = CONFIGS[name]
+    t_gen = time.perf_counter()
+    b2 = make_config(name)
+    print(f"[bench] generated {name} in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
+          flush=True)
+    n = SECONDARY_STEPS
+    if variant.startswith("cp"):
+        ns = int(variant[2:])
+        r2 = run_decode_cp(pa, torch, b2, ns, n, dev, timer)
+        kb = r2["shard_kv_bytes"]
+        kern = "decode_mfma_kernel" if (b2.G >= 4 and b2.D == 128) else "decode_partition_kernel"
+        return {
+            "step": f"pa_decode_partial (shard 0 of {ns}) + pa_merge_partials ({ns} shards)",
+            "partition_size": r2["partition_size"], "steps": n,
+            "ms_per_step": round(_p50(r2["step_ms"]), 5), "step_us": _stats_us(r2["step_ms"]),
+            "shard_tokens": r2["shard_tokens"], "shard_kv_bytes": kb,
+            "merge_bytes": r2["merge_bytes"], "partial_us": _stats_us(r2["partial_ms"]),
+            "merge_us": _stats_us(r2["merge_ms"]),
+            "merge_GBps": round(r2["merge_bytes"] / (float(np.mean(r2["merge_ms"])) * 1e-3) / 1e9, 2),
+            "roofline": _hbm_roofline(f"pa_decode_partial ({kern})", kb, r2["partial_ms"],
+                                      traffic_from(f"decode_{name}_cp{ns}_counters.md",
+                                                   KERNEL_SOURCES))}
+    if variant == "graph":
+        r2 = run_graph(pa, torch, b2, n, 10, dev, timer)
+        kv2 = b2.kv_bytes()
+        return {
+            "step": "rotary embedding + cache write + decode: two launches "
+                    "(pa_rope_reshape_and_cache, pa_decode) vs one (pa_decode_step_rope), "
+                    "each eager and as HIP-graph replays, warm back to back",
+            "partition_size": r2["partition_size"], "steps": n,
+            "eager_us_per_step": round(r2["eager_ms"] * 1e3, 2),
+            "graph_us_per_step": round(r2["graph_ms"] * 1e3, 2),
+            "graph_speedup": round(r2["eager_ms"] / r2["graph_ms"], 3),
+            "fused_eager_us_per_step": round(r2["fused_ms"] * 1e3, 2),
+            "fused_graph_us_per_step": round(r2["fused_graph_ms"] * 1e3, 2),
+            "fused_speedup": round(r2["eager_ms"] / r2["fused_ms"], 3),
+            "fused_effective_GBps": round(kv2 / (r2["fused_ms"] * 1e-3) / 1e9, 2)}
+    if variant == "rope":
+        r2 = run_rope(pa, torch, b2, n, dev, timer)
+        rb = rope_bytes(b2)
+        plain_bytes = 2 * 2 * r2["tokens"] * b2.Hkv * b2.D * 2
+        return {
+            "step": "pa_rope_reshape_and_cache (queries rotated in place, keys rotated into "
+                    "the cache, values copied)", "tokens": r2["tokens"], "steps": n,
+            "ms_per_step": round(_p50(r2["step_ms"]), 5), "algorithmic_bytes": rb,
+            "rope_us": _stats_us(r2["step_ms"]),
+            "plain_reshape_and_cache_us": _stats_us(r2["plain_ms"]),
+            "plain_reshape_and_cache_GBps": round(plain_bytes / (_p50(r2["plain_ms"]) * 1e-3) / 1e9, 1),
+            "roofline": _hbm_roofline("rope_reshape_kernel", rb, r2["step_ms"],
+                                      traffic_from(f"rope_reshape_{name}_counters.md",
+                                                   KERNEL_SOURCES_ROPE))}
+    if variant == "int8":
+        p2 = resolve_partition(pa, c2, b2)
+        r2 = run_decode_int8(pa, torch, b2, p2, n, dev, timer)
+        kb = int8_kv_bytes(b2)
+        t = _p50(r2["step_ms"]) * 1e-3
+        e = {"step": "pa_decode_step_int8 (quantising store + decode, one launch)",
+             "partition_size": p2, "steps": n, "ms_per_step": round(t * 1e3, 5),
+             "step_us": _stats_us(r2["step_ms"]),
+             "two_launch_us": _stats_us(r2["two_launch_ms"]),
+             "int8_kv_bytes": kb, "effective_GBps": round(kb / t / 1e9, 2),
+             "note": "effective_GBps counts the INT8 codes and scales read; the same step over a "
+                     "16-bit cache would read kv_bytes_16bit",
+             "kv_bytes_16bit": b2.kv_bytes(),
+             "seqs_per_s": round(b2.B / t, 1),
+             "roofline": _hbm_roofline(r2["kernel_name"], kb, r2["step_ms"],
+                                       recorded_traffic(name, p2, int8=True))}
+        if r2["merge_ms"] is not None:
+            e["k3_merge_us"] = _stats_us(r2["merge_ms"])
+        return e
+    if c2["kind"] == "prefill":
+        r2 = run_prefill(pa, torch, b2, n, dev, timer)
+        flops = prefill_flops(b2)
+        tfl = flops / (float(np.mean(r2["prefill_ms"])) * 1e-3) / 1e12
+        return {
+            "step": "pa_reshape_and_cache (all new tokens) + pa_prefill_chunk", "steps": n,
+            "ms_per_step": round(_p50(r2["step_ms"]), 5), "step_us": _stats_us(r2["step_ms"]),
+            "prefill_us": _stats_us(r2["prefill_ms"]),
+            "reshape_and_cache_us": _stats_us(r2["reshape_ms"]),
+            "reshape_and_cache_GBps": round(
+                2 * 2 * len(b2.slot_mapping) * b2.Hkv * b2.D * 2 / (_p50(r2["reshape_ms"]) * 1e-3)
+                / 1e9, 1),
+            "algorithmic_gflop": round(flops / 1e9, 2),
+            "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tfl, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": traffic_from(f"prefill_{name}_counters.md",
+                                                 KERNEL_SOURCES_PREFILL)}}
+    p2 = resolve_partition(pa, c2, b2)
+    r2 = run_decode(pa, torch, b2, p2, n, 5, False, dev, timer, warmup_ms=SECONDARY_WARMUP_MS)
+    kv2 = b2.kv_bytes()
+    t = _p50(r2["step_ms"]) * 1e-3
+    e = {"step": "pa_decode_step", "partition_size": p2, "steps": n, "ms_per_step": round(t * 1e3, 5),
+         "step_us": _stats_us(r2["step_ms"]), "effective_GBps": round(kv2 / t / 1e9, 2),
+         "unique_kv_bytes": b2.unique_kv_bytes(), "kv_bytes": kv2,
+         "warm_back_to_back_us": round(r2["warm_ms"] * 1e3, 2),
+         "roofline": _hbm_roofline(r2["kernel_name"], kv2, r2["step_ms"],
+                                   recorded_traffic(name, p2))}
+    if r2["phases"]:
+        e["phases"] = r2["phases"]
+    return e
 
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qwen3_0p6b_decode")
+    ap.add_argument("--seed", type=int, default=None,
+                    help="seed of the headline workload's inputs (default: the workload's own)")
+    ap.add_argument("--flush-mb", type=int, default=1024,
+                    help="MiB read before every timed call to evict the Infinity Cache and L2s")
     ap.add_argument("--partition", type=int, default=None, help="tokens per context partition")
     ap.add_argument("--unfused", action="store_true",
                     help="step = pa_reshape_and_cache + pa_decode (two launches) instead of the "
@@ -526,17 +745,19 @@ def main(argv=None) -> int:
         print("bench.py: the headline workload is a decode batch", file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
+    timer = Timer(torch, dev, args.flush_mb)
 
     t_gen = time.perf_counter()
-    b = make_config(args.workload)
+    seed = cfg["seed"] if args.seed is None else args.seed
+    b = make_config(args.workload, seed=seed)
     print(f"[bench] generated {args.workload} in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
           flush=True)
     partition = resolve_partition(pa, cfg, b) if args.partition is None else args.partition
-    r = run_decode(pa, torch, b, partition, args.steps, args.warmup, args.unfused, dev,
-                   cold_iters=20)
+    r = run_decode(pa, torch, b, partition, args.steps, args.warmup, args.unfused, dev, timer)
+    print("[bench] headline timed", file=sys.stderr, flush=True)
     kv = b.kv_bytes()
-    value = kv / (r["ms_per_step"] * 1e-3) / 1e9
-    achieved = kv / (float(r["kernel_ms"].mean()) * 1e-3) / 1e9
+    t = _p50(r["step_ms"]) * 1e-3
+    value = kv / t / 1e9
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -544,7 +765,7 @@ def main(argv=None) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(r["ms_per_step"], 5),
+        "ms_per_step": round(t * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -553,20 +774,26 @@ def main(argv=None) -> int:
         "config": {"workload": args.workload, "num_seqs": b.B, "num_heads": b.Hq,
                    "num_kv_heads": b.Hkv, "head_dim": b.D, "block_size": b.BS,
                    "pool_blocks": b.NB, "context_lens": "uniform[%d,%d]" % tuple(cfg["lens"]),
-                   "seed": cfg["seed"], "partition_size": partition,
+                   "seed": seed, "partition_size": partition,
                    "step": "pa_reshape_and_cache + pa_decode" if args.unfused else
                            "pa_decode_step (new-token store + decode, one launch)",
                    "seq_order": "longest context first (pa_decode_order on the host)",
                    "kv_bytes_per_step": kv},
+        "protocol": (f"{args.warmup} warm-up steps, then {args.steps} timed steps, each after a "
+                     f"{args.flush_mb} MiB flush read and bracketed by HIP events on its stream; "
+                     "value and ms_per_step from the median, roofline.achieved from the mean of "
+                     "the same durations"),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "seqs_per_s": round(b.B / (r["ms_per_step"] * 1e-3), 1),
-        "decode_us": _stats_us(r["kernel_ms"]),
-        "decode_cold_us": _stats_us(r["cold_ms"]),
-        "cold_GBps_p50": round(kv / (float(np.median(r["cold_ms"])) * 1e-3) / 1e9, 2),
-        "roofline": {"bound": "hbm", "kernel": r["kernel_name"],
-                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": recorded_traffic(args.workload, partition)},
+        "seqs_per_s": round(b.B / t, 1),
+        "step_us": _stats_us(r["step_ms"]),
+        "warm_back_to_back": {"us_per_step": round(r["warm_ms"] * 1e3, 2),
+                              "GBps": round(kv / (r["warm_ms"] * 1e-3) / 1e9, 2),
+                              "note": "labelled extra: the same step issued back to back "
+                                      "without flushes, wall time per step"},
+        "kernels": r["phases"] or {"k2": r["kernel_name"], "k3": "none (no context split)"},
+        "stream_read_ceiling": timer.stream_read_ceiling(),
+        "roofline": _hbm_roofline(r["kernel_name"], kv, r["step_ms"],
+                                  recorded_traffic(args.workload, partition)),
     }
     secondary = {}
     for entry in [x for x in args.secondary.split(",") if x]:
@@ -575,125 +802,12 @@ def main(argv=None) -> int:
         torch.cuda.synchronize(dev)
         gc.collect()
         torch.cuda.empty_cache()
-        name, _, variant = entry.partition(":")
-        c2 = CONFIGS[name]
-        t_gen = time.perf_counter()
-        b2 = make_config(name)
-        print(f"[bench] generated {name} in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
-              flush=True)
-        # Half the headline's steps and its full warm-up: with a tenth of them (20 steps,
-        # 5 warm-up) the secondary timings read 5-14% slower than in longer runs.
-        steps2 = max(5, args.steps // 2)
-        warm2 = max(2, args.warmup)
-        if variant.startswith("cp"):
-            n = int(variant[2:])
-            r2 = run_decode_cp(pa, torch, b2, n, steps2, warm2, dev)
-            kb = r2["shard_kv_bytes"]
-            ach2 = kb / (float(r2["kernel_ms"].mean()) * 1e-3) / 1e9
-            achm = r2["merge_bytes"] / (float(r2["merge_ms"].mean()) * 1e-3) / 1e9
-            kern = "decode_mfma_kernel" if (b2.G >= 4 and b2.D == 128) else "decode_partition_kernel"
-            secondary[entry] = {
-                "step": f"pa_decode_partial (shard 0 of {n}) + pa_merge_partials ({n} shards)",
-                "partition_size": r2["partition_size"], "steps": steps2,
-                "ms_per_step": round(r2["ms_per_step"], 5), "shard_tokens": r2["shard_tokens"],
-                "shard_kv_bytes": kb, "merge_bytes": r2["merge_bytes"],
-                "partial_us": _stats_us(r2["kernel_ms"]), "merge_us": _stats_us(r2["merge_ms"]),
-                "merge_GBps": round(achm, 2),
-                "roofline": {"bound": "hbm", "kernel": f"pa_decode_partial ({kern})",
-                             "achieved": round(ach2, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                             "frac": round(ach2 / HBM_PEAK_GBPS, 4),
-                             "traffic": traffic_from(f"decode_{name}_cp{n}_counters.md",
-                                                     KERNEL_SOURCES)}}
-            continue
-        if variant == "graph":
-            r2 = run_graph(pa, torch, b2, max(50, steps2), max(5, warm2), dev)
-            kv2 = b2.kv_bytes()
-            secondary[entry] = {
-                "step": "rotary embedding + cache write + decode: two launches "
-                        "(pa_rope_reshape_and_cache, pa_decode) vs one (pa_decode_step_rope), "
-                        "each eager and as HIP-graph replays",
-                "partition_size": r2["partition_size"], "steps": max(50, steps2),
-                "eager_us_per_step": round(r2["eager_ms"] * 1e3, 2),
-                "graph_us_per_step": round(r2["graph_ms"] * 1e3, 2),
-                "graph_speedup": round(r2["eager_ms"] / r2["graph_ms"], 3),
-                "fused_eager_us_per_step": round(r2["fused_ms"] * 1e3, 2),
-                "fused_graph_us_per_step": round(r2["fused_graph_ms"] * 1e3, 2),
-                "fused_speedup": round(r2["eager_ms"] / r2["fused_ms"], 3),
-                "fused_effective_GBps": round(kv2 / (r2["fused_ms"] * 1e-3) / 1e9, 2)}
-            continue
-        if variant == "rope":
-            r2 = run_rope(pa, torch, b2, max(20, steps2), warm2, dev)
-            rb = rope_bytes(b2)
-            ach2 = rb / (float(r2["kernel_ms"].mean()) * 1e-3) / 1e9
-            secondary[entry] = {
-                "step": "pa_rope_reshape_and_cache (queries rotated in place, keys rotated into "
-                        "the cache, values copied)", "tokens": r2["tokens"],
-                "ms_per_step": round(r2["ms_per_step"], 5), "algorithmic_bytes": rb,
-                "rope_us": _stats_us(r2["kernel_ms"]),
-                "plain_reshape_and_cache_us": _stats_us(r2["plain_ms"]),
-                "roofline": {"bound": "hbm", "kernel": "rope_reshape_kernel",
-                             "achieved": round(ach2, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                             "frac": round(ach2 / HBM_PEAK_GBPS, 4),
-                             "traffic": traffic_from(f"rope_reshape_{name}_counters.md",
-                                                     KERNEL_SOURCES_ROPE)}}
-            continue
-        if variant == "int8":
-            p2 = resolve_partition(pa, c2, b2)
-            r2 = run_decode_int8(pa, torch, b2, p2, steps2, warm2, dev)
-            kb = int8_kv_bytes(b2)
-            ach2 = kb / (float(r2["kernel_ms"].mean()) * 1e-3) / 1e9
-            secondary[entry] = {
-                "step": "pa_decode_step_int8 (quantising store + decode, one launch)",
-                "partition_size": p2, "steps": steps2, "ms_per_step": round(r2["ms_per_step"], 5),
-                "two_launch_ms_per_step": round(r2["two_launch_ms_per_step"], 5),
-                "int8_kv_bytes": kb, "effective_GBps": round(kb / (r2["ms_per_step"] * 1e-3) / 1e9, 2),
-                "bf16_equivalent_GBps": round(b2.kv_bytes() / (r2["ms_per_step"] * 1e-3) / 1e9, 2),
-                "seqs_per_s": round(b2.B / (r2["ms_per_step"] * 1e-3), 1),
-                "decode_us": _stats_us(r2["kernel_ms"]),
-                "roofline": {"bound": "hbm", "kernel": r2["kernel_name"], "achieved": round(ach2, 2),
-                             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                             "frac": round(ach2 / HBM_PEAK_GBPS, 4),
-                             "traffic": recorded_traffic(name, p2, int8=True)}}
-            continue
-        if c2["kind"] == "prefill":
-            r2 = run_prefill(pa, torch, b2, steps2, warm2, dev)
-            flops = prefill_flops(b2)
-            tfl = flops / (float(r2["kernel_ms"].mean()) * 1e-3) / 1e12
-            secondary[name] = {
-                "step": "pa_reshape_and_cache (all new tokens) + pa_prefill_chunk",
-                "steps": steps2, "ms_per_step": round(r2["ms_per_step"], 5),
-                "prefill_us": _stats_us(r2["kernel_ms"]),
-                "reshape_and_cache_us": _stats_us(r2["reshape_ms"]),
-                "reshape_and_cache_GBps": round(
-                    2 * 2 * len(b2.slot_mapping) * b2.Hkv * b2.D * 2
-                    / (float(np.median(r2["reshape_ms"])) * 1e-3) / 1e9, 1),
-                "algorithmic_gflop": round(flops / 1e9, 2),
-                "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tfl, 2),
-                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
-                             "traffic": traffic_from(f"prefill_{name}_counters.md",
-                                                     KERNEL_SOURCES_PREFILL)}}
-        else:
-            p2 = resolve_partition(pa, c2, b2)
-            r2 = run_decode(pa, torch, b2, p2, steps2, warm2, False, dev)
-            kv2 = b2.kv_bytes()
-            ach2 = kv2 / (float(r2["kernel_ms"].mean()) * 1e-3) / 1e9
-            secondary[name] = {
-                "step": "pa_decode_step", "partition_size": p2, "steps": steps2,
-                "ms_per_step": round(r2["ms_per_step"], 5),
-                "effective_GBps": round(kv2 / (r2["ms_per_step"] * 1e-3) / 1e9, 2),
-                "unique_kv_bytes": b2.unique_kv_bytes(), "kv_bytes": kv2,
-                "decode_us": _stats_us(r2["kernel_ms"]),
-                "roofline": {"bound": "hbm", "kernel": r2["kernel_name"],
-                             "achieved": round(ach2, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                             "frac": round(ach2 / HBM_PEAK_GBPS, 4),
-                             "traffic": recorded_traffic(name, p2)}}
-        del b2
+        secondary[entry] = secondary_entry(pa, torch, entry, dev, timer)
     if secondary:
         result["secondary"] = secondary
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(b, args.cpu_budget)
+        result["cpu_baseline"], result["parity"] = cpu_baseline(b, args.cpu_budget, r["out_bits"])
     print(json.dumps(result), flush=True)
     return 0
 

@@ -183,7 +183,9 @@ int pa_decode_partition_hint(int num_seqs, int num_kv_heads, int max_context_len
  * call's kernels finish on `stream`).
  *
  * Supported: num_heads / num_kv_heads in {1, 2, 4, 8}; head_dim in {64, 128};
- * block_size in {16, 32, 256}; dtype PA_F16 or PA_BF16; finite scale.
+ * block_size in {16, 32, 256}; dtype PA_F16 or PA_BF16; scale finite and > 0
+ * (PA_ERR_INVALID_ARG otherwise: the softmax temperature, 1/sqrt(head_dim) in the
+ * pages' attention).
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
@@ -191,6 +193,42 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int64_t num_blocks, int max_blocks_per_seq, int max_context_len, float scale,
               int partition_size, void* workspace, size_t workspace_bytes, int dtype,
               void* stream);
+
+/*
+ * The two phases of a split decode as calls of their own.  pa_decode with
+ * partition_size > 0 enqueues the partition kernel (each partition's fp32 max,
+ * sum and normalised output into the workspace; sequences that fit one
+ * partition are written to `out` directly) and then, when some context spans
+ * several partitions, the merge of those partitions (the reduction after a
+ * split of the context across cores, page "vLLM-Ascend ...", section 3.1).
+ *
+ * pa_decode_partitions: the first phase alone.  Arguments, rules and
+ * supported shapes exactly as for pa_decode; rows of sequences whose context
+ * spans several partitions are left unwritten until pa_decode_merge runs.
+ *
+ * pa_decode_merge: the second phase alone, over the workspace that a
+ * preceding split decode on `stream` filled (pa_decode_partitions, or any of
+ * pa_decode, pa_decode_step, pa_decode_step_rope, pa_decode_int8,
+ * pa_decode_step_int8, which already merge; a repeated merge rewrites the
+ * same rows).  num_seqs, num_heads, head_dim, max_context_len,
+ * partition_size, context_lens, seq_order, workspace and dtype must be those
+ * of that call.  Writes out[i][h] for every sequence i whose context spans
+ * more than one partition (and that seq_order lists), nothing else.  A no-op
+ * when partition_size == 0 or max_context_len <= partition_size.  Returns
+ * PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED (head_dim not 64/128, dtype) or
+ * PA_ERR_WORKSPACE (missing, short, not 16-byte aligned) before any HIP call.
+ */
+int pa_decode_partitions(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads,
+                         int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                         int max_context_len, float scale, int partition_size, void* workspace,
+                         size_t workspace_bytes, int dtype, void* stream);
+
+int pa_decode_merge(void* out, const int32_t* context_lens, const int32_t* seq_order,
+                    int num_seqs, int num_heads, int head_dim, int max_context_len,
+                    int partition_size, void* workspace, size_t workspace_bytes, int dtype,
+                    void* stream);
 
 /*
  * pa_decode_step: one decode step, i.e. pa_reshape_and_cache of one new token
@@ -380,7 +418,8 @@ int pa_decode_order(const int32_t* context_lens, int num_seqs, int32_t* order);
  * QK^T and PV run as 32x32x16 matrix-core (MFMA) tiles with fp32 accumulation;
  * the softmax is fp32 and the probabilities are rounded to the input dtype
  * before the PV product.  Supported: head_dim 128; block_size 16, 32, 256;
- * num_heads / num_kv_heads in {1, 2, 4, 8}; dtype PA_F16 or PA_BF16.
+ * num_heads / num_kv_heads in {1, 2, 4, 8}; dtype PA_F16 or PA_BF16; scale finite and
+ * > 0 (PA_ERR_INVALID_ARG otherwise).
  */
 int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_tables, const int32_t* context_lens,

@@ -14,9 +14,11 @@ from ._binding import (  # noqa: F401
     pa_copy_blocks,
     pa_decode,
     pa_decode_int8,
+    pa_decode_merge,
     pa_decode_order,
     pa_decode_partial,
     pa_decode_partition_hint,
+    pa_decode_partitions,
     pa_decode_step,
     pa_decode_step_int8,
     pa_decode_step_rope,

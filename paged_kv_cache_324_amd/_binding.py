@@ -51,6 +51,11 @@ def _declare(lib):
     lib.pa_decode.restype = c_int
     lib.pa_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
                               c_int, c_i64, c_int, c_int, c_f, c_int, c_vp, c_sz, c_int, c_vp]
+    lib.pa_decode_partitions.restype = c_int
+    lib.pa_decode_partitions.argtypes = lib.pa_decode.argtypes
+    lib.pa_decode_merge.restype = c_int
+    lib.pa_decode_merge.argtypes = [c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_vp, c_sz,
+                                    c_int, c_vp]
     lib.pa_decode_step.restype = c_int
     lib.pa_decode_step.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                    c_int, c_int, c_int, c_int, c_int, c_i64, c_int, c_int, c_f,
@@ -280,6 +285,44 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
                          B, Hq, Hkv, D, BS, NB, block_tables.shape[1], int(max_context_len),
                          float(scale), int(partition_size), ws_ptr, ws_bytes, dt,
                          _stream(q, stream)))
+    return out
+
+
+def pa_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                         max_context_len: int, partition_size: int = 512, workspace=None,
+                         seq_order=None, stream=None) -> torch.Tensor:
+    """The partition phase of pa_decode alone: rows of contexts that span several
+    partitions stay in ``workspace`` (which must then be given) until pa_decode_merge."""
+    lib, B, Hq, Hkv, D, BS, NB, dt, ws_ptr, ws_bytes, order_ptr = _decode_common(
+        q, k_cache, v_cache, block_tables, context_lens, seq_order, out, max_context_len,
+        partition_size, workspace)
+    if ws_ptr is not None and workspace is None:
+        raise ValueError("decode partitions: pass the workspace the merge will read")
+    _check(lib.pa_decode_partitions(_dev(out, "out"), _dev(q, "q"), k_cache.data_ptr(),
+                                    v_cache.data_ptr(),
+                                    _dev(block_tables, "block_tables", torch.int32),
+                                    _dev(context_lens, "context_lens", torch.int32), order_ptr,
+                                    B, Hq, Hkv, D, BS, NB, block_tables.shape[1],
+                                    int(max_context_len), float(scale), int(partition_size),
+                                    ws_ptr, ws_bytes, dt, _stream(q, stream)))
+    return out
+
+
+def pa_decode_merge(out, context_lens, max_context_len: int, partition_size: int, workspace,
+                    seq_order=None, stream=None) -> torch.Tensor:
+    """The merge phase of a split decode alone, over the partials a preceding split decode
+    left in ``workspace``; ``out`` is ``[num_seqs][num_heads][head_dim]``."""
+    lib = load_library()
+    B, Hq, D = out.shape
+    if context_lens.shape != (B,) or (seq_order is not None and seq_order.shape != (B,)):
+        raise ValueError("decode merge: context_lens and seq_order must be [num_seqs]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    order_ptr = None if seq_order is None else _dev(seq_order, "seq_order", torch.int32)
+    _check(lib.pa_decode_merge(_dev(out, "out"), _dev(context_lens, "context_lens", torch.int32),
+                               order_ptr, B, Hq, D, int(max_context_len), int(partition_size),
+                               ws_ptr, ws_bytes, _dtype_code(out), _stream(out, stream)))
     return out
 
 

@@ -3,7 +3,7 @@
 
 namespace pa {
 hipError_t launch_decode_bf16(const DecodeArgs& a, int head_dim, int block_size, int group,
-                              hipStream_t s) {
-  return launch_decode_dt<DT_BF16>(a, head_dim, block_size, group, s);
+                              int phases, hipStream_t s) {
+  return launch_decode_dt<DT_BF16>(a, head_dim, block_size, group, phases, s);
 }
 }  // namespace pa

@@ -3,7 +3,7 @@
 
 namespace pa {
 hipError_t launch_decode_f16(const DecodeArgs& a, int head_dim, int block_size, int group,
-                             hipStream_t s) {
-  return launch_decode_dt<DT_F16>(a, head_dim, block_size, group, s);
+                             int phases, hipStream_t s) {
+  return launch_decode_dt<DT_F16>(a, head_dim, block_size, group, phases, s);
 }
 }  // namespace pa

@@ -443,6 +443,8 @@ void decode_partition_kernel(const DecodeArgs a) {
 }
 
 // One wavefront per (sequence, query head): merge that row's partitions.
+// Rows are visited through `seq_order` like the partition kernel's workgroups,
+// so a sequence the order leaves out is neither read nor written.
 // Lane p folds the (m, l) of partitions p, p+64, ...; each lane owns D/64
 // consecutive dimensions of the partial outputs.  The outputs of the first 64
 // partitions and all (m, l) are loaded before the context length is known;
@@ -462,7 +464,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
   };
   const int lane = threadIdx.x;
   const int h = blockIdx.x % a.num_heads;
-  const int seq = blockIdx.x / a.num_heads;
+  const int rank = blockIdx.x / a.num_heads;
+  const int seq = a.seq_order ? a.seq_order[rank] : rank;
+  if (seq < 0 || seq >= a.num_seqs) return;
   const int P = a.num_parts;
   // Partition p of this row is entry (seq * P + p) * num_heads + h.
   const int64_t base = (int64_t)seq * P * a.num_heads + h;
@@ -554,48 +558,62 @@ void launch_partitions(const DecodeArgs& a, unsigned grid, hipStream_t s) {
   }
 }
 
-template <int DT, int D, int BS, int G>
-hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
-  const unsigned grid = (unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_parts);
-  if (a.rope_cos) {
-    launch_partitions<DT, D, BS, G, true>(a, grid, s);
-  } else {
-    launch_partitions<DT, D, BS, G, false>(a, grid, s);
-  }
+// The partition merge (a6) of a split decode, when some context spans several
+// partitions.
+template <int DT, int D>
+void launch_merge(const DecodeArgs& a, hipStream_t s) {
   if (a.num_parts > 1) {
     hipLaunchKernelGGL((decode_merge_kernel<DT, D>), dim3((unsigned)(a.num_seqs * a.num_heads)),
                        dim3(64), 0, s, a);
   }
+}
+
+template <int DT, int D, int BS, int G>
+hipError_t launch_decode_t(const DecodeArgs& a, int phases, hipStream_t s) {
+  const unsigned grid = (unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_parts);
+  if (phases & kPhasePartitions) {
+    if (a.rope_cos) {
+      launch_partitions<DT, D, BS, G, true>(a, grid, s);
+    } else {
+      launch_partitions<DT, D, BS, G, false>(a, grid, s);
+    }
+  }
+  if (phases & kPhaseMerge) launch_merge<DT, D>(a, s);
   return hipGetLastError();
 }
 
 template <int DT, int D, int BS>
-hipError_t launch_decode_g(const DecodeArgs& a, int group, hipStream_t s) {
+hipError_t launch_decode_g(const DecodeArgs& a, int group, int phases, hipStream_t s) {
   switch (group) {
-    case 1: return launch_decode_t<DT, D, BS, 1>(a, s);
-    case 2: return launch_decode_t<DT, D, BS, 2>(a, s);
-    case 4: return launch_decode_t<DT, D, BS, 4>(a, s);
-    case 8: return launch_decode_t<DT, D, BS, 8>(a, s);
+    case 1: return launch_decode_t<DT, D, BS, 1>(a, phases, s);
+    case 2: return launch_decode_t<DT, D, BS, 2>(a, phases, s);
+    case 4: return launch_decode_t<DT, D, BS, 4>(a, phases, s);
+    case 8: return launch_decode_t<DT, D, BS, 8>(a, phases, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int DT, int D>
-hipError_t launch_decode_bs(const DecodeArgs& a, int block_size, int group, hipStream_t s) {
+hipError_t launch_decode_bs(const DecodeArgs& a, int block_size, int group, int phases,
+                            hipStream_t s) {
+  if (phases == kPhaseMerge) {  // the merge alone does not depend on the cache's shape
+    launch_merge<DT, D>(a, s);
+    return hipGetLastError();
+  }
   switch (block_size) {
-    case 16: return launch_decode_g<DT, D, 16>(a, group, s);
-    case 32: return launch_decode_g<DT, D, 32>(a, group, s);
-    case 256: return launch_decode_g<DT, D, 256>(a, group, s);
+    case 16: return launch_decode_g<DT, D, 16>(a, group, phases, s);
+    case 32: return launch_decode_g<DT, D, 32>(a, group, phases, s);
+    case 256: return launch_decode_g<DT, D, 256>(a, group, phases, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int DT>
 hipError_t launch_decode_dt(const DecodeArgs& a, int head_dim, int block_size, int group,
-                            hipStream_t s) {
+                            int phases, hipStream_t s) {
   switch (head_dim) {
-    case 64: return launch_decode_bs<DT, 64>(a, block_size, group, s);
-    case 128: return launch_decode_bs<DT, 128>(a, block_size, group, s);
+    case 64: return launch_decode_bs<DT, 64>(a, block_size, group, phases, s);
+    case 128: return launch_decode_bs<DT, 128>(a, block_size, group, phases, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -20,13 +20,17 @@
 //     bytes of dims 32 quad .. 32 quad + 31 and MFMA step ks takes dims
 //     32 quad + 8 ks .. + 7; the query fragments follow the same dim order (a
 //     dot product does not depend on the order of its terms);
-//   * codes are exact in fp16 and bf16 (|code| <= 127), so each is converted in
-//     registers to the query's 16-bit type; the key scale multiplies the
-//     fp32 score, the value scale multiplies p after the softmax sum (so the
-//     denominator is unchanged) before p is rounded for the value product;
+//   * key codes are exact in fp16 and bf16 (|code| <= 127), so each is
+//     converted in registers to the query's 16-bit type and the key scale
+//     multiplies the fp32 score;
 //   * V rows arrive as 16-byte chunks of 16 codes and are written to LDS as
 //     two 16-byte chunks of 16-bit values, in the swizzled layout the
-//     transposed reads expect;
+//     transposed reads expect: each value dequantised, code x scale rounded to
+//     fp32 and then once to the query's 16-bit type (the operand type of the
+//     value product);
+//   * p is rounded to the 16-bit type for the value product, and the row sum
+//     is a ones MFMA over the same rounded p (as in the 16-bit matrix-core
+//     kernel), so numerator and denominator weigh every key alike;
 //   * a step carries half the bytes, so each wavefront keeps two steps in
 //     flight (two register sets) instead of one.
 #include "decode_impl.h"
@@ -52,6 +56,22 @@ __device__ __forceinline__ uint32_t i8_pair(uint32_t w, int k) {
 template <int DT>
 __device__ __forceinline__ u32x4 i8_to_16(uint32_t w0, uint32_t w1) {
   return u32x4{i8_pair<DT>(w0, 0), i8_pair<DT>(w0, 1), i8_pair<DT>(w1, 0), i8_pair<DT>(w1, 1)};
+}
+
+// The four codes of a dword dequantised with row scale s, as two packed 16-bit
+// pairs: code x s rounded once to fp32, then to the 16-bit type (nearest
+// even).  Each code is read as the unsigned byte code + 128 of w ^ 0x80808080
+// (one byte-to-float conversion) and the product formed as
+// fma(code + 128, s, nb) with nb = -128 s (exact), which equals code x s up to
+// that single rounding.
+template <int DT>
+__device__ __forceinline__ u32x2 i8x4_dequant(uint32_t w, float s, float nb) {
+  const uint32_t u = w ^ 0x80808080u;
+  const float f0 = fmaf((float)(u & 0xFFu), s, nb);
+  const float f1 = fmaf((float)((u >> 8) & 0xFFu), s, nb);
+  const float f2 = fmaf((float)((u >> 16) & 0xFFu), s, nb);
+  const float f3 = fmaf((float)(u >> 24), s, nb);
+  return u32x2{pack2<DT>(f0, f1), pack2<DT>(f2, f3)};
 }
 
 template <int DT, int BS, int G, int NW>
@@ -121,15 +141,21 @@ void decode_int8_kernel(const DecodeArgs a) {
   const char* vsbase = reinterpret_cast<const char*>(a.v_scales) + (size_t)kvh * BS * 4;
   const uint64_t sblock_bytes = (uint64_t)a.num_kv_heads * BS * 4;
 
-  float m = kEmptyMax, lsum = 0.f;
+  float m = kEmptyMax;
   f32x4 o[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{};
+  f32x4 lacc = f32x4{};  // row sums of the rounded P (every row holds its column's sum)
+  const uint32_t one2 = pack2<DT>(1.f, 1.f);
+  const u32x2 ones = {one2, one2};
   unsigned char* const sv = s_v[wave];
   // Two register sets of codes and scales: the steps s + 4 and s + 8 of a
-  // wavefront are in flight while step s computes.
+  // wavefront are in flight while step s computes.  ksc: the key scales of
+  // keys 4 quad .. + 3 of each group (the keys whose scores this lane holds);
+  // vrs: the value scale of the V row this lane stages (see store_v).
   struct Regs {
-    u32x4 kr[2][2], vr[2][2], ksc[2], vsc[2];
+    u32x4 kr[2][2], vr[2][2], ksc[2];
+    float vrs[2][2];
   };
   Regs ra, rb;
 
@@ -160,12 +186,15 @@ void decode_int8_kernel(const DecodeArgs a) {
         r.vr[gr][j] = buffer_load16<kCachePolicyNT>(
             rv, (uint32_t)(8 * j + (lane >> 3)) * row_bytes + (uint32_t)((lane & 7) * 16));
       r.ksc[gr] = buffer_load16<kCachePolicyNT>(rks, (uint32_t)(16 * quad));
-      r.vsc[gr] = buffer_load16<kCachePolicyNT>(rvs, (uint32_t)(16 * quad));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        r.vrs[gr][j] = buffer_load4f<kCachePolicyNT>(rvs, (uint32_t)(4 * (8 * j + (lane >> 3))));
     }
   };
 
-  // V codes -> 16-bit rows of this wavefront's LDS tile (row 16 gr + 8 j +
-  // lane / 8 of the step, dims 16 (lane % 8) .. + 15 = chunks 2 (lane % 8), +1).
+  // V codes -> dequantised 16-bit rows of this wavefront's LDS tile (row 16 gr +
+  // 8 j + lane / 8 of the step, dims 16 (lane % 8) .. + 15 = chunks 2 (lane % 8),
+  // +1), each code times its row's scale.
   auto store_v = [&](const Regs& r) {
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr)
@@ -175,12 +204,16 @@ void decode_int8_kernel(const DecodeArgs a) {
         const int c = 2 * (lane & 7);
         unsigned char* rowp = sv + row * kI8Row;
         const u32x4 w = r.vr[gr][j];
-        *reinterpret_cast<u32x4*>(rowp + ((c ^ i8_vswz(row)) * 16)) = i8_to_16<DT>(w.x, w.y);
-        *reinterpret_cast<u32x4*>(rowp + (((c + 1) ^ i8_vswz(row)) * 16)) = i8_to_16<DT>(w.z, w.w);
+        const float vs = r.vrs[gr][j], nb = -128.f * vs;
+        const u32x2 d0 = i8x4_dequant<DT>(w.x, vs, nb), d1 = i8x4_dequant<DT>(w.y, vs, nb);
+        const u32x2 d2 = i8x4_dequant<DT>(w.z, vs, nb), d3 = i8x4_dequant<DT>(w.w, vs, nb);
+        *reinterpret_cast<u32x4*>(rowp + ((c ^ i8_vswz(row)) * 16)) = u32x4{d0.x, d0.y, d1.x, d1.y};
+        *reinterpret_cast<u32x4*>(rowp + (((c + 1) ^ i8_vswz(row)) * 16)) =
+            u32x4{d2.x, d2.y, d3.x, d3.y};
       }
   };
 
-  auto scores = [&](const Regs& r, f32x4 (&sc)[2], f32x4 (&kscale)[2], f32x4 (&vscale)[2]) {
+  auto scores = [&](const Regs& r, f32x4 (&sc)[2], f32x4 (&kscale)[2]) {
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr) {
       sc[gr] = f32x4{};
@@ -191,12 +224,10 @@ void decode_int8_kernel(const DecodeArgs a) {
         sc[gr] = mfma16x16x32<DT>(kf, qf[ks], sc[gr]);
       }
       kscale[gr] = __builtin_bit_cast(f32x4, r.ksc[gr]);
-      vscale[gr] = __builtin_bit_cast(f32x4, r.vsc[gr]);
     }
   };
 
-  auto accumulate = [&](f32x4 (&sc)[2], const f32x4 (&kscale)[2], const f32x4 (&vscale)[2], int kb,
-                        int kend) {
+  auto accumulate = [&](f32x4 (&sc)[2], const f32x4 (&kscale)[2], int kb, int kend) {
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr) sc[gr] *= kscale[gr];  // key j's score x sK[j]
     if (kb + kI8StepKeys > kend) {
@@ -213,24 +244,18 @@ void decode_int8_kernel(const DecodeArgs a) {
       const float m_new = fmaxf(m, mx);
       const float alpha = fast_exp2(m - m_new);
       m = m_new;
-      lsum *= alpha;
+      lacc *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
     }
-    float psum = 0.f;
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(fmaf(sc[gr][i], a.scale_log2, -m));
-        psum += p;
-        sc[gr][i] = p * vscale[gr][i];  // the value scale, outside the denominator
-      }
-    psum = sum_xor32(sum_xor16(psum));
-    lsum += psum;
+      for (int i = 0; i < 4; ++i) sc[gr][i] = fast_exp2(fmaf(sc[gr][i], a.scale_log2, -m));
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr) {
       const u32x2 pf = {pack2<DT>(sc[gr][0], sc[gr][1]), pack2<DT>(sc[gr][2], sc[gr][3])};
+      lacc = mfma16x16x16<DT>(ones, pf, lacc);
       const int rr = 16 * gr + 4 * quad + (col >> 2);
       const unsigned char* rowp = sv + rr * kI8Row + 8 * (col & 1);
 #pragma unroll
@@ -258,11 +283,11 @@ void decode_int8_kernel(const DecodeArgs a) {
   auto step = [&](int s, Regs& r) {
     const int32_t ids_after = load_ids(s + 3 * NW);
     store_v(r);
-    f32x4 sc[2], kscale[2], vscale[2];
-    scores(r, sc, kscale, vscale);
+    f32x4 sc[2], kscale[2];
+    scores(r, sc, kscale);
     issue(s + 2 * NW, ids_next, r);
     ids_next = ids_after;
-    accumulate(sc, kscale, vscale, t0 + kI8StepKeys * s, t1c);
+    accumulate(sc, kscale, t0 + kI8StepKeys * s, t1c);
   };
   int s = wave;
   if (s < nsteps) {
@@ -315,8 +340,9 @@ void decode_int8_kernel(const DecodeArgs a) {
     // Registers of the one-key step, laid out as issue() loads a cached step:
     // key 0 of group 0 is the new token.  Its key codes, dims 32 quad .. + 31,
     // go to the lanes with col 0 (from quantising lanes 4 quad .. 4 quad + 3);
-    // its value codes, dims 16 (lane & 7) .. + 15, to lanes 0..7 (from lanes
-    // 16 + 2 (lane & 7) and the next); its scales to the quad-0 lanes.
+    // its value codes, dims 16 (lane & 7) .. + 15, and its value scale to lanes
+    // 0..7 (from lanes 16 + 2 (lane & 7) and the next); its key scale to the
+    // quad-0 lanes.
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
     Regs rn;
     uint32_t kw[8], vw[4];
@@ -334,13 +360,15 @@ void decode_int8_kernel(const DecodeArgs a) {
     rn.vr[1][0] = zero4;
     rn.vr[1][1] = zero4;
     rn.ksc[0] = quad == 0 ? u32x4{__float_as_uint(ksn), 0u, 0u, 0u} : zero4;
-    rn.vsc[0] = quad == 0 ? u32x4{__float_as_uint(vsn), 0u, 0u, 0u} : zero4;
     rn.ksc[1] = zero4;
-    rn.vsc[1] = zero4;
+    rn.vrs[0][0] = lane < 8 ? vsn : 0.f;
+    rn.vrs[0][1] = 0.f;
+    rn.vrs[1][0] = 0.f;
+    rn.vrs[1][1] = 0.f;
     store_v(rn);
-    f32x4 sc[2], kscale[2], vscale[2];
-    scores(rn, sc, kscale, vscale);
-    accumulate(sc, kscale, vscale, L - 1, L);
+    f32x4 sc[2], kscale[2];
+    scores(rn, sc, kscale);
+    accumulate(sc, kscale, L - 1, L);
   }
 
   // Merge the NW wavefronts' (m, l, O) and write the partition.
@@ -351,7 +379,7 @@ void decode_int8_kernel(const DecodeArgs a) {
     for (int i = 0; i < 4; ++i) s_o[col * D + 16 * dt + 4 * quad + i] = o[dt][i];
   if (quad == 0) {
     s_ml[(wave * 16 + col) * 2] = m;
-    s_ml[(wave * 16 + col) * 2 + 1] = lsum;
+    s_ml[(wave * 16 + col) * 2 + 1] = lacc[0];
   }
   __syncthreads();
   const float* s_all = reinterpret_cast<const float*>(&s_v[0][0]);
@@ -390,8 +418,12 @@ void decode_int8_kernel(const DecodeArgs a) {
 }
 
 template <int DT, int BS, int G>
-hipError_t launch_int8_t(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_int8_t(const DecodeArgs& a, int phases, hipStream_t s) {
   const unsigned grid = (unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_parts);
+  if (phases & kPhaseMerge && !(phases & kPhasePartitions)) {
+    launch_merge<DT, 128>(a, s);
+    return hipGetLastError();
+  }
   // Wavefronts per workgroup: eight for spans of kMfmaLongSpan+ tokens (as for the
   // 16-bit matrix-core kernel); two for contexts cut into partitions of at most
   // kMfmaShortPartition tokens, so that each wavefront takes more steps of its
@@ -404,37 +436,36 @@ hipError_t launch_int8_t(const DecodeArgs& a, hipStream_t s) {
   } else {
     hipLaunchKernelGGL((decode_int8_kernel<DT, BS, G, 4>), dim3(grid), dim3(256), 0, s, a);
   }
-  if (a.num_parts > 1)
-    hipLaunchKernelGGL((decode_merge_kernel<DT, 128>), dim3((unsigned)(a.num_seqs * a.num_heads)),
-                       dim3(64), 0, s, a);
+  if (phases & kPhaseMerge) launch_merge<DT, 128>(a, s);
   return hipGetLastError();
 }
 
 template <int DT, int BS>
-hipError_t launch_int8_g(const DecodeArgs& a, int group, hipStream_t s) {
+hipError_t launch_int8_g(const DecodeArgs& a, int group, int phases, hipStream_t s) {
   switch (group) {
-    case 1: return launch_int8_t<DT, BS, 1>(a, s);
-    case 2: return launch_int8_t<DT, BS, 2>(a, s);
-    case 4: return launch_int8_t<DT, BS, 4>(a, s);
-    case 8: return launch_int8_t<DT, BS, 8>(a, s);
+    case 1: return launch_int8_t<DT, BS, 1>(a, phases, s);
+    case 2: return launch_int8_t<DT, BS, 2>(a, phases, s);
+    case 4: return launch_int8_t<DT, BS, 4>(a, phases, s);
+    case 8: return launch_int8_t<DT, BS, 8>(a, phases, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int DT>
-hipError_t launch_int8_dt(const DecodeArgs& a, int block_size, int group, hipStream_t s) {
+hipError_t launch_int8_dt(const DecodeArgs& a, int block_size, int group, int phases,
+                          hipStream_t s) {
   switch (block_size) {
-    case 16: return launch_int8_g<DT, 16>(a, group, s);
-    case 32: return launch_int8_g<DT, 32>(a, group, s);
-    case 256: return launch_int8_g<DT, 256>(a, group, s);
+    case 16: return launch_int8_g<DT, 16>(a, group, phases, s);
+    case 32: return launch_int8_g<DT, 32>(a, group, phases, s);
+    case 256: return launch_int8_g<DT, 256>(a, group, phases, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_decode_int8(const DecodeArgs& a, int dtype, int block_size, int group,
-                              hipStream_t s) {
-  return dtype == DT_BF16 ? launch_int8_dt<DT_BF16>(a, block_size, group, s)
-                          : launch_int8_dt<DT_F16>(a, block_size, group, s);
+                              int phases, hipStream_t s) {
+  return dtype == DT_BF16 ? launch_int8_dt<DT_BF16>(a, block_size, group, phases, s)
+                          : launch_int8_dt<DT_F16>(a, block_size, group, phases, s);
 }
 
 }  // namespace pa

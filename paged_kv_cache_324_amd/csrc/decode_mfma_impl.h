@@ -18,13 +18,16 @@
 //                 through a buffer resource based at the group's block (16
 //                 keys never straddle a block) whose size ends at the last
 //                 valid key.  B = Q^T, the G heads in columns 0..G-1.
-//   softmax       lane l owns head l % 16 and 4 keys of each group; max and
-//                 sum add two lane exchanges (l ^ 16, l ^ 32).  Rescaling of
-//                 O is lazy (only when a maximum grows by more than 2^8).
+//   softmax       lane l owns head l % 16 and 4 keys of each group; the max
+//                 adds two lane exchanges (l ^ 16, l ^ 32).  Rescaling of O is
+//                 lazy (only when a maximum grows by more than 2^8).
 //   O^T += V^T P^T  16x16x16 MFMA over each group's 16 keys.  V rows are
 //                 loaded into registers with K, stored to this wavefront's LDS
 //                 buffer and read back transposed (ds_read_b64_tr_b16); P^T is
-//                 the softmax registers.
+//                 the softmax registers rounded to the input dtype.
+//   row sum       one more 16x16x16 MFMA per group, ones P^T: the sum, in
+//                 fp32, of exactly the rounded p the value product consumes,
+//                 so numerator and denominator weigh every key alike.
 // As soon as a step's K and V have left their registers (scores issued, V in
 // LDS) the same registers take the loads of the wavefront's next step, whose
 // block ids were loaded a step earlier still; so one step per wavefront is
@@ -169,10 +172,14 @@ void decode_mfma_kernel(const DecodeArgs a) {
   const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)kvh * D * 2;
   const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)kvh * D * 2;
 
-  float m = kEmptyMax, lsum = 0.f;
+  float m = kEmptyMax;
   f32x4 o[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{};
+  // Row sums of the rounded P: every accumulator row holds its column's sum.
+  f32x4 lacc = f32x4{};
+  const uint32_t one2 = pack2<DT>(1.f, 1.f);
+  const u32x2 ones = {one2, one2};
   unsigned char* const sv = s_v[wave];
   u32x4 kf[2][4], vr[2][4];
 
@@ -241,25 +248,20 @@ void decode_mfma_kernel(const DecodeArgs a) {
       const float m_new = fmaxf(m, mx);
       const float alpha = fast_exp2(m - m_new);
       m = m_new;
-      lsum *= alpha;
+      lacc *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
     }
-    float psum = 0.f;
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(fmaf(sc[gr][i], a.scale_log2, -m));
-        sc[gr][i] = p;
-        psum += p;
-      }
-    psum = sum_xor32(sum_xor16(psum));
-    lsum += psum;
-    // O^T[d][head] += V^T[d][key] P^T[key][head], 16 dims x 16 keys per MFMA.
+      for (int i = 0; i < 4; ++i) sc[gr][i] = fast_exp2(fmaf(sc[gr][i], a.scale_log2, -m));
+    // O^T[d][head] += V^T[d][key] P^T[key][head], 16 dims x 16 keys per MFMA;
+    // the row sum takes the same rounded P^T.
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr) {
       const u32x2 pf = {pack2<DT>(sc[gr][0], sc[gr][1]), pack2<DT>(sc[gr][2], sc[gr][3])};
+      lacc = mfma16x16x16<DT>(ones, pf, lacc);
       const int rr = 16 * gr + 4 * quad + (col >> 2);
       const unsigned char* rowp = sv + rr * kMdRow + 8 * (col & 1);
 #pragma unroll
@@ -280,7 +282,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
       for (int i = 0; i < 4; ++i) s_o[col * D + 16 * dt + 4 * quad + i] = o[dt][i];
     if (quad == 0) {
       s_ml[(wave * 16 + col) * 2] = m;
-      s_ml[(wave * 16 + col) * 2 + 1] = lsum;
+      s_ml[(wave * 16 + col) * 2 + 1] = lacc[0];
     }
     __syncthreads();
     const float* s_all = reinterpret_cast<const float*>(&s_v[0][0]);  // [NW][16][128]

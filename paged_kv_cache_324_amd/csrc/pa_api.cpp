@@ -68,6 +68,11 @@ bool supported_head_dim(int d) { return d == 64 || d == 128; }
 bool supported_block_size(int b) { return b == 16 || b == 32 || b == 256; }
 bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 bool supported_dtype(int t) { return t == PA_F16 || t == PA_BF16; }
+// The softmax scale is a positive temperature (1/sqrt(head_dim) in the pages'
+// attention).  The matrix-core kernels take each row's maximum over the raw
+// scores and fold the scale into the exponent, which orders scores correctly
+// only for a positive scale.
+bool valid_scale(float s) { return std::isfinite(s) && s > 0.f; }
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -239,7 +244,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                 float* out_ml, int num_seqs, int num_heads,
                 int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
                 int max_blocks_per_seq, int max_context_len, float scale, int partition_size,
-                void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+                void* workspace, size_t workspace_bytes, int dtype, void* stream,
+                int phases = pa::kPhaseAll) {
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0");
   int st = check_cache(num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                        max_blocks_per_seq, dtype);
@@ -247,7 +253,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
     return fail(PA_ERR_INVALID_ARG, "max_context_len %d outside [0, max_blocks_per_seq*block_size]",
                 max_context_len);
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  if (!valid_scale(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0))
     return fail(PA_ERR_INVALID_ARG, "partition_size %d must be 0 or a positive multiple of %d",
                 partition_size, block_size);
@@ -314,9 +320,9 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   const int group = num_heads / num_kv_heads;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // PA_F16 / PA_BF16 are the kernels' dtype codes.
-  hipError_t e = i8 ? pa::launch_decode_int8(a, dtype, block_size, group, s)
-                 : dtype == PA_BF16 ? pa::launch_decode_bf16(a, head_dim, block_size, group, s)
-                                    : pa::launch_decode_f16(a, head_dim, block_size, group, s);
+  hipError_t e = i8 ? pa::launch_decode_int8(a, dtype, block_size, group, phases, s)
+                 : dtype == PA_BF16 ? pa::launch_decode_bf16(a, head_dim, block_size, group, phases, s)
+                                    : pa::launch_decode_f16(a, head_dim, block_size, group, phases, s);
   return hip_status(e, "decode launch");
 }
 
@@ -334,6 +340,61 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
                      num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
                      workspace_bytes, dtype, stream);
+}
+
+int pa_decode_partitions(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads,
+                         int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                         int max_context_len, float scale, int partition_size, void* workspace,
+                         size_t workspace_bytes, int dtype, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, seq_order, nullptr, nullptr,
+                     nullptr, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
+                     workspace_bytes, dtype, stream, pa::kPhasePartitions);
+}
+
+int pa_decode_merge(void* out, const int32_t* context_lens, const int32_t* seq_order,
+                    int num_seqs, int num_heads, int head_dim, int max_context_len,
+                    int partition_size, void* workspace, size_t workspace_bytes, int dtype,
+                    void* stream) {
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0");
+  if (num_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_heads must be >= 1");
+  if (!supported_head_dim(head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not in {64,128}", head_dim);
+  if (!supported_dtype(dtype)) return fail(PA_ERR_UNSUPPORTED, "dtype %d not PA_F16/PA_BF16", dtype);
+  if (max_context_len < 0) return fail(PA_ERR_INVALID_ARG, "max_context_len must be >= 0");
+  if (partition_size < 0) return fail(PA_ERR_INVALID_ARG, "partition_size must be >= 0");
+  const int64_t parts = num_partitions(max_context_len, partition_size);
+  if (num_seqs == 0 || parts <= 1) return ok();  // no context spans two partitions
+  if (!out || !context_lens) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if ((int64_t)num_seqs * num_heads > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "launch grid too large");
+  const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, parts);
+  if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+  if (workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(PA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  pa::DecodeArgs a{};
+  const size_t rows = (size_t)num_seqs * num_heads * (size_t)parts;
+  a.out = out;
+  a.context_lens = context_lens;
+  a.seq_order = seq_order;
+  a.part_out = static_cast<uint16_t*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       align_up(rows * head_dim * sizeof(uint16_t)));
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = 1;
+  a.max_context_len = max_context_len;
+  a.num_parts = (int)parts;
+  a.part_tokens = partition_size;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // The merge alone depends on neither the block size nor the head grouping.
+  const hipError_t e = dtype == PA_BF16
+                           ? pa::launch_decode_bf16(a, head_dim, 16, 1, pa::kPhaseMerge, s)
+                           : pa::launch_decode_f16(a, head_dim, 16, 1, pa::kPhaseMerge, s);
+  return hip_status(e, "decode merge launch");
 }
 
 int pa_decode_step(void* out, const void* q, const void* key, const void* value,
@@ -552,7 +613,7 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
   if (st != PA_OK) return st;
   if (head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "prefill supports head_dim 128 only");
   if (max_query_len < 0) return fail(PA_ERR_INVALID_ARG, "max_query_len must be >= 0");
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  if (!valid_scale(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");

@@ -31,6 +31,11 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voffset, 0, AUX);
 }
 
+template <int AUX = 0>
+__device__ __forceinline__ float buffer_load4f(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)voffset, 0, AUX));
+}
+
 // ---- 16-bit float pairs packed in a dword ------------------------------------
 template <int DT>
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c);

@@ -129,16 +129,20 @@ hipError_t launch_reshape_and_cache(const ReshapeArgs& a, hipStream_t s);
 hipError_t launch_rope_reshape(const RopeReshapeArgs& a, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 hipError_t launch_reshape_int8(const ReshapeInt8Args& a, int dtype, int head_dim, hipStream_t s);
+// Which launches of a decode to enqueue: the partition kernel (a2-a5), the
+// partition merge (a6, only when a context spans several partitions), or both.
+enum : int { kPhasePartitions = 1, kPhaseMerge = 2, kPhaseAll = 3 };
+
 // INT8 decode: DecodeArgs with k_cache / v_cache pointing at the int8 codes and
 // the per-row scales in k_scales / v_scales.
 hipError_t launch_decode_int8(const DecodeArgs& a, int dtype, int block_size, int group,
-                              hipStream_t s);
+                              int phases, hipStream_t s);
 
 // dtype DT_F16 / DT_BF16; head_dim 64/128; block_size 16/32/256; group 1/2/4/8.
 hipError_t launch_decode_f16(const DecodeArgs& a, int head_dim, int block_size, int group,
-                             hipStream_t s);
+                             int phases, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, int head_dim, int block_size, int group,
-                              hipStream_t s);
+                              int phases, hipStream_t s);
 
 // Merge of partials computed over disjoint key sets (context-parallel shards).
 struct MergePartialsArgs {

@@ -69,6 +69,9 @@ def _decode(lib, **kw):
     (dict(maxL=161), -1, "max_context_len"),
     (dict(scale=float("inf")), -1, "scale"),
     (dict(scale=float("nan")), -1, "scale"),
+    (dict(scale=0.0), -1, "scale"),
+    (dict(scale=-0.088), -1, "scale"),
+    (dict(scale=-0.0), -1, "scale"),
     (dict(part=24), -1, "partition_size"),
     (dict(part=-16), -1, "partition_size"),
     (dict(part=32), -3, "workspace"),
@@ -127,9 +130,11 @@ def test_prefill_rejects_bad_arguments(lib):
     bad = list(args)
     bad[10] = 6     # 32 heads over 6 KV heads
     assert f(*bad) == -1
-    bad = list(args)
-    bad[17] = float("nan")
-    assert f(*bad) == -1
+    for sc in (float("nan"), float("-inf"), 0.0, -0.0, -0.1):
+        bad = list(args)
+        bad[17] = sc
+        assert f(*bad) == -1
+        assert "scale" in lib.pa_last_error().decode()
     bad = list(args)
     bad[16] = -1
     assert f(*bad) == -1
@@ -277,3 +282,38 @@ def test_rope_without_tokens_or_queries(lib):
              pa.PA_F16, None) == 0
     # no queries: num_heads is ignored, a bad key still rejected
     assert f(None, None, P, P, P, P, P, P, P, 4, 0, 8, 128, 16, 100, 10, pa.PA_F16, None) == -1
+
+
+@pytest.mark.parametrize("scale", [0.0, -1.0, float("nan")])
+def test_int8_decode_and_steps_reject_non_positive_scale(lib, scale):
+    """A non-positive or non-finite scale is rejected by every attention entry point."""
+    int8 = [P, P, P, P, P, P, P, P, None, 2, 16, 8, 128, 16, 100, 10, 160, scale, 0, None, 0,
+            pa.PA_BF16, None]
+    assert lib.pa_decode_int8(*int8) == -1
+    assert "scale" in lib.pa_last_error().decode()
+    step = [P, P, P, P, P, P, P, P, P, None, 2, 16, 8, 128, 16, 100, 10, 160, scale, 0, None, 0,
+            pa.PA_BF16, None]
+    assert lib.pa_decode_step(*step) == -1
+    assert "scale" in lib.pa_last_error().decode()
+
+
+def test_decode_merge_rejects_bad_arguments(lib):
+    f = lib.pa_decode_merge
+    # out, lens, seq_order, B, Hq, D, max_len, partition, ws, ws_bytes, dtype, stream
+    args = [P, P, None, 4, 16, 128, 2048, 512, P, 1 << 20, pa.PA_BF16, None]
+    for i, v, code in [(0, None, -1), (1, None, -1), (3, -1, -1), (4, 0, -1), (5, 96, -2),
+                       (10, 9, -2), (6, -1, -1), (7, -16, -1), (8, None, -3), (9, 100, -3)]:
+        bad = list(args)
+        bad[i] = v
+        assert f(*bad) == code, (i, v)
+    # nothing to merge: no partition split, or no sequence
+    assert f(None, None, None, 4, 16, 128, 2048, 0, None, 0, pa.PA_BF16, None) == 0
+    assert f(None, None, None, 4, 16, 128, 512, 512, None, 0, pa.PA_BF16, None) == 0
+    assert f(None, None, None, 0, 16, 128, 2048, 512, None, 0, pa.PA_BF16, None) == 0
+
+
+def test_decode_partitions_validates_like_decode(lib):
+    a = [P, P, P, P, P, P, None, 2, 16, 8, 128, 16, 100, 10, 160, 0.1, 32, None, 0, pa.PA_BF16, None]
+    assert lib.pa_decode_partitions(*a) == -3          # split without a workspace
+    a[15] = -1.0
+    assert lib.pa_decode_partitions(*a) == -1

@@ -9,7 +9,8 @@ from oracle import context_parallel as cp
 from paged_kv_cache_324_amd import pa_decode_partial, pa_merge_partials, pa_reshape_and_cache
 from workloads import make_batch, make_config, to_u16
 
-from _gpu import bits_to_device, check_close, host_caches_after_write, log, to_f64, upload
+from _gpu import (bits_to_device, check_close, check_full, config_batch, config_decode_ref,
+                  host_caches_after_write, log, to_f64, upload)
 from _shards import split_context
 
 pytestmark = pytest.mark.gpu
@@ -227,19 +228,18 @@ def test_merge_without_out_ml_and_empty_batch():
 
 
 # ------------------------------------------------------------------ full size
-def test_long_context_eight_shards_sampled():
+def test_long_context_eight_shards_full():
     """The long-context batch split over eight shards (one per device of a context-parallel
-    group): every shard's partial at its real shape, merged, sampled against the oracle."""
-    b = make_config("long_splitk_decode")
+    group): every shard's partial rows at their real shape and the merged rows, all of them,
+    against the oracle."""
+    b = config_batch("long_splitk_decode")
     log(f"cp8 long_splitk_decode: B={b.B} lens {b.context_lens.min()}..{b.context_lens.max()}")
     sh = Shards(b, 8, "contiguous")
     o, ml = sh.partials(512)
     out = torch.empty_like(sh.dev.q)
     pa_merge_partials(out, o, ml)
     torch.cuda.synchronize()
-    rows = [0, b.B // 2, b.B - 1]
-    got = to_f64(out)[rows]
-    mx, rel = check_close(got, sh.oracle_full(rows), "cp8 long_splitk_decode")
-    log(f"  rows {rows}: max_abs={mx:.3e} rel_l2={rel:.3e}")
-    ref = sh.oracle_partial(3, rows)
-    check_partial(o[3][rows], ml[3][rows], ref, "cp8 shard 3")
+    check_full(to_f64(out), config_decode_ref("long_splitk_decode"), "cp8 long_splitk_decode merged",
+               b.dtype)
+    for n in range(8):
+        check_partial(o[n], ml[n], sh.oracle_partial(n), f"cp8 shard {n}")

@@ -12,7 +12,8 @@ import oracle
 from paged_kv_cache_324_amd import pa_decode, pa_decode_partition_hint, pa_reshape_and_cache
 from workloads import make_batch, make_config, to_u16
 
-from _gpu import (check_close, host_caches_after_write, log, to_bits, to_f64, upload)
+from _gpu import (check_close, check_full, config_batch, config_decode_ref,
+                  host_caches_after_write, log, to_bits, to_f64, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -81,46 +82,40 @@ def test_reshape_empty_is_noop():
 # ------------------------------------------------------------------ decode parity
 @pytest.mark.parametrize("partition", [0, 16, 64])
 def test_decode_tiny_config(partition):
-    b = make_config("tiny_decode")
+    b = config_batch("tiny_decode")
     log(f"decode tiny partition={partition} lens={b.context_lens.tolist()}")
     got = to_f64(_step(b, upload(b), partition))
-    ref, _ = _oracle_rows(b)
-    check_close(got, ref, f"tiny p={partition}")
+    check_full(got, config_decode_ref("tiny_decode"), f"tiny_decode p={partition}", b.dtype)
 
 
 @pytest.mark.parametrize("partition", [512, 0, 256])
 def test_decode_qwen3_shaped_full_size(partition):
-    b = make_config("qwen3_0p6b_decode")
+    b = config_batch("qwen3_0p6b_decode")
     log(f"decode qwen3-shaped B={b.B} NB={b.NB} partition={partition}")
     got = to_f64(_step(b, upload(b), partition))
-    ref, _ = _oracle_rows(b)
-    mx, rel = check_close(got, ref, f"qwen3 p={partition}")
-    log(f"  max_abs={mx:.3e} rel_l2={rel:.3e}")
+    check_full(got, config_decode_ref("qwen3_0p6b_decode"), f"qwen3_0p6b_decode p={partition}",
+               b.dtype)
 
 
 @pytest.mark.parametrize("partition", [512, 0])
 def test_decode_long_context_split_k(partition):
-    b = make_config("long_splitk_decode")
+    b = config_batch("long_splitk_decode")
     log(f"decode long split-K B={b.B} BS={b.BS} maxL={b.max_context_len} partition={partition}")
     got = to_f64(_step(b, upload(b), partition))
-    ref, _ = _oracle_rows(b)
-    mx, rel = check_close(got, ref, f"long p={partition}")
-    log(f"  max_abs={mx:.3e} rel_l2={rel:.3e}")
+    check_full(got, config_decode_ref("long_splitk_decode"), f"long_splitk_decode p={partition}",
+               b.dtype)
 
 
 @pytest.mark.parametrize("name", ["llama2_70b_decode_bs16", "llama2_70b_decode_bs32"])
 @pytest.mark.parametrize("split", ["hint", 512])
-def test_decode_llama2_shaped_prefix_sharing_sampled(name, split):
-    b = make_config(name)
+def test_decode_llama2_shaped_prefix_sharing_full(name, split):
+    """Every output row of the Llama-2-shaped batch (pairs (2k, 2k+1) share prefix blocks)."""
+    b = config_batch(name)
     partition = (pa_decode_partition_hint(b.B, b.Hkv, b.max_context_len, b.BS)
                  if split == "hint" else split)
     log(f"decode {name} B={b.B} G={b.G} shared blocks={b.shared_pairs} partition={partition}")
     got = to_f64(_step(b, upload(b), partition))
-    rows = [0, 1, 2, 3, 30, 31, 62, 63]      # pairs (2k, 2k+1) share prefix blocks
-    ref, sel = _oracle_rows(b, rows)
-    mx, rel = check_close(got[sel], ref, name)
-    log(f"  max_abs={mx:.3e} rel_l2={rel:.3e}")
-    assert np.all(np.isfinite(got))
+    check_full(got, config_decode_ref(name), f"{name} p={partition}", b.dtype)
 
 
 LENS = [1, 15, 16, 17, 255, 256, 257, 511, 512, 513, 1000, 0]
@@ -297,13 +292,11 @@ def _fused_step(b, d, partition, ordered=True):
                                             ("qwen3_0p6b_decode", 0), ("qwen3_0p6b_decode", 512),
                                             ("long_splitk_decode", 512)])
 def test_decode_step_fused_parity(name, partition):
-    b = make_config(name)
+    b = config_batch(name)
     log(f"fused step {name} partition={partition}")
     d = upload(b)
     got = to_f64(_fused_step(b, d, partition))
-    ref, _ = _oracle_rows(b)
-    mx, rel = check_close(got, ref, f"fused {name} p={partition}")
-    log(f"  max_abs={mx:.3e} rel_l2={rel:.3e}")
+    check_full(got, config_decode_ref(name), f"fused step {name} p={partition}", b.dtype)
     kc_ref, vc_ref = host_caches_after_write(b)
     assert np.array_equal(to_bits(d.k_cache[d.idx]), kc_ref)
     assert np.array_equal(to_bits(d.v_cache[d.idx]), vc_ref)
@@ -324,18 +317,14 @@ def test_decode_step_fused_length_edges(partition):
 
 @pytest.mark.parametrize("name,partition", [("llama2_70b_decode_bs16", 0), ("long_splitk_decode", 0),
                                             ("long_splitk_decode", 4096)])
-def test_decode_step_fused_long_spans_sampled(name, partition):
+def test_decode_step_fused_long_spans_full(name, partition):
     """Spans of 4096+ tokens run the eight-wavefront matrix-core kernel, which also takes
-    the new token on its wavefront with the fewest steps."""
-    b = make_config(name)
+    the new token on its wavefront with the fewest steps.  Every output row is checked."""
+    b = config_batch(name)
     log(f"fused step {name} partition={partition}")
     d = upload(b)
     got = to_f64(_fused_step(b, d, partition))
-    rows = sorted(set([0, 1, b.B // 2, b.B - 1]))
-    ref, sel = _oracle_rows(b, rows)
-    mx, rel = check_close(got[sel], ref, f"fused {name} p={partition}")
-    log(f"  rows {rows}: max_abs={mx:.3e} rel_l2={rel:.3e}")
-    assert np.all(np.isfinite(got))
+    check_full(got, config_decode_ref(name), f"fused step {name} p={partition}", b.dtype)
     kc_ref, vc_ref = host_caches_after_write(b)
     assert np.array_equal(to_bits(d.k_cache[d.idx]), kc_ref)
     assert np.array_equal(to_bits(d.v_cache[d.idx]), vc_ref)
@@ -381,3 +370,69 @@ def test_decode_step_fused_needle_on_new_token():
     for i in range(3):
         for h in range(4):
             assert np.array_equal(got[i, h], b.value_new[i, h // 2])
+
+
+# ------------------------------------------------------------------ the two phases as calls
+@pytest.mark.parametrize("dt,G,partition", [("bf16", 2, 64), ("f16", 8, 128), ("bf16", 4, 512),
+                                            ("bf16", 8, 0)])
+def test_partitions_then_merge_equal_decode_bits(dt, G, partition):
+    """pa_decode_partitions followed by pa_decode_merge is pa_decode, bit for bit; a second
+    merge over the same workspace rewrites the same rows."""
+    from paged_kv_cache_324_amd import decode_workspace, pa_decode_merge, pa_decode_partitions
+    b = make_batch(B=9, Hq=2 * G, Hkv=2, D=128, BS=16, dtype=dt, scale=0.088, seed=53,
+                   lens=[1, 15, 64, 65, 200, 511, 512, 513, 1500], NB=512)
+    d = upload(b)
+    want = to_bits(_step(b, d, partition))
+    ws = decode_workspace(b.B, b.Hq, b.D, b.max_context_len, partition, "cuda")
+    out = torch.empty_like(d.q)
+    pa_decode_partitions(out, d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, b.scale,
+                         b.max_context_len, partition, workspace=ws)
+    pa_decode_merge(out, d.context_lens, b.max_context_len, partition, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(out), want)
+    pa_decode_merge(out, d.context_lens, b.max_context_len, partition, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(out), want)
+
+
+def test_merge_alone_after_int8_decode():
+    """The merge reads the same workspace format after an INT8 split decode."""
+    from paged_kv_cache_324_amd import decode_workspace, pa_decode_int8, pa_decode_merge
+    from test_gpu_int8 import Int8Batch
+    b = make_batch(B=5, Hq=8, Hkv=2, D=128, BS=16, dtype="bf16", scale=0.088, seed=54,
+                   lens=[3, 300, 513, 1024, 777], NB=256)
+    ib = Int8Batch(b)
+    ws = decode_workspace(b.B, b.Hq, b.D, b.max_context_len, 256, "cuda")
+    out = torch.empty_like(ib.q)
+    pa_decode_int8(out, ib.q, ib.kc, ib.vc, ib.ks, ib.vs, ib.tables, ib.lens, b.scale,
+                   b.max_context_len, 256, workspace=ws)
+    torch.cuda.synchronize()
+    want = to_bits(out)
+    out2 = torch.zeros_like(out)
+    pa_decode_merge(out2, ib.lens, b.max_context_len, 256, ws)
+    torch.cuda.synchronize()
+    split = (b.context_lens > 256)
+    assert np.array_equal(to_bits(out2)[split], want[split])
+    assert np.all(to_bits(out2)[~split] == 0)          # single-partition rows: not the merge's
+
+
+@pytest.mark.parametrize("G,partition", [(2, 0), (2, 64), (8, 0), (8, 128)])
+def test_seq_order_subset_leaves_other_rows_unwritten(G, partition):
+    """seq_order entries outside [0, num_seqs) are skipped: the sequences it does not list
+    are neither computed nor merged, and their output rows keep their contents, also
+    when their contexts are split (the merge visits rows through seq_order too)."""
+    b = make_batch(B=8, Hq=2 * G, Hkv=2, D=128, BS=16, dtype="bf16", scale=0.088, seed=55,
+                   lens_range=(100, 900), NB=512)
+    d = upload(b)
+    pa_reshape_and_cache(d.key_new, d.value_new, d.k_cache, d.v_cache, d.slot_mapping)
+    order = np.array([5, -1, 2, 8, 0, 7, 1 << 20, -7], np.int32)
+    listed = np.array([0, 2, 5, 7])
+    out = torch.full(tuple(d.q.shape), 0x1234, dtype=torch.int16, device="cuda").view(d.q.dtype)
+    pa_decode(out, d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, b.scale,
+              b.max_context_len, partition, seq_order=torch.from_numpy(order).cuda())
+    torch.cuda.synchronize()
+    got = to_bits(out)
+    unlisted = np.setdiff1d(np.arange(b.B), listed)
+    assert np.all(got[unlisted] == 0x1234)
+    ref, _ = _oracle_rows(b, listed)
+    check_close(to_f64(out)[listed], ref, f"subset G{G} p{partition}")

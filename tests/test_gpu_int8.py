@@ -8,9 +8,9 @@ import torch
 import oracle
 from oracle import int8_kv
 from paged_kv_cache_324_amd import pa_decode_int8, pa_decode_step_int8, pa_reshape_and_cache_int8
-from workloads import make_batch, make_config, to_u16
+from workloads import make_batch, to_u16
 
-from _gpu import bits_to_device, check_close, log, to_f64
+from _gpu import bits_to_device, check_close, check_full, config_batch, log, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -31,6 +31,12 @@ def cached_rows(b):
     return kr, vr, comp, phys
 
 
+# Fill of every cache slot no call has written: codes 90 and scale -7.0, so a stray read or
+# write of a wrong slot shows in the output or in the cache compare.
+SENT_CODE = 90
+SENT_SCALE = -7.0
+
+
 class Int8Batch:
     """Device and host INT8 caches holding the batch's cached tokens and this step's new ones."""
 
@@ -39,10 +45,10 @@ class Int8Batch:
         dt = torch.bfloat16 if b.dtype == "bf16" else torch.float16
         kr, vr, comp, phys = cached_rows(b)
         NB, BS, Hkv, D = b.NB, b.BS, b.Hkv, b.D
-        self.kc = torch.zeros((NB, Hkv, BS, D), dtype=torch.int8, device="cuda")
-        self.vc = torch.zeros_like(self.kc)
-        self.ks = torch.zeros((NB, Hkv, BS), dtype=torch.float32, device="cuda")
-        self.vs = torch.zeros_like(self.ks)
+        self.kc = torch.full((NB, Hkv, BS, D), SENT_CODE, dtype=torch.int8, device="cuda")
+        self.vc = torch.full_like(self.kc, SENT_CODE)
+        self.ks = torch.full((NB, Hkv, BS), SENT_SCALE, dtype=torch.float32, device="cuda")
+        self.vs = torch.full_like(self.ks, SENT_SCALE)
         pairs = ((kr, vr, phys), (b.key_new, b.value_new, b.slot_mapping))
         for k, v, s in pairs if write_new else pairs[:1]:
             if len(s):
@@ -50,8 +56,8 @@ class Int8Batch:
                                           self.vc, self.ks, self.vs,
                                           torch.from_numpy(np.ascontiguousarray(s)).cuda())
         n = b.k_blocks.shape[0]
-        self.hk = np.zeros((n, Hkv, BS, D), np.int8); self.hv = self.hk.copy()
-        self.hks = np.zeros((n, Hkv, BS), np.float32); self.hvs = self.hks.copy()
+        self.hk = np.full((n, Hkv, BS, D), SENT_CODE, np.int8); self.hv = self.hk.copy()
+        self.hks = np.full((n, Hkv, BS), SENT_SCALE, np.float32); self.hvs = self.hks.copy()
         int8_kv.reshape_and_cache_int8(kr, vr, self.hk, self.hv, self.hks, self.hvs, comp, b.dtype)
         int8_kv.reshape_and_cache_int8(b.key_new, b.value_new, self.hk, self.hv, self.hks, self.hvs,
                                        b.slot_mapping_compact, b.dtype)
@@ -74,6 +80,21 @@ class Int8Batch:
         return int8_kv.paged_decode_int8(b.q[sel], self.hk, self.hv, self.hks, self.hvs,
                                          b.block_tables_compact[sel], b.context_lens[sel], b.scale,
                                          b.dtype)
+
+    def check_caches(self, expect=None):
+        """Every slot of the four device arrays, bit for bit: the batch's blocks equal the
+        host caches (`expect`, default this object's), every other block still holds the
+        fill.  Compared on the device."""
+        hk, hv, hks, hvs = expect if expect is not None else (self.hk, self.hv, self.hks, self.hvs)
+        others = torch.ones(self.b.NB, dtype=torch.bool, device="cuda")
+        others[self.idx] = False
+        for dev, host in ((self.kc, hk), (self.vc, hv)):
+            assert torch.equal(dev[self.idx], torch.from_numpy(host).cuda())
+            assert bool((dev[others] == SENT_CODE).all())
+        for dev, host in ((self.ks, hks), (self.vs, hvs)):
+            assert torch.equal(dev[self.idx].view(torch.int32),
+                               torch.from_numpy(host.view(np.int32)).cuda())
+            assert bool((dev[others] == SENT_SCALE).all())
 
 
 # ------------------------------------------------------------------ quantising reshape
@@ -143,17 +164,26 @@ def test_decode_int8_length_edges(partition):
     assert np.all(got[lens.index(0)] == 0)
 
 
-@pytest.mark.parametrize("name,partition", [("qwen3_0p6b_decode", 0), ("long_splitk_decode", 512),
-                                            ("llama2_70b_decode_bs16", 0)])
-def test_decode_int8_full_size_sampled(name, partition):
-    b = make_config(name)
-    log(f"int8 decode {name}: B={b.B} G={b.G} partition={partition}")
+INT8_FULL = [("qwen3_0p6b_decode", 0), ("long_splitk_decode", 512), ("llama2_70b_decode_bs16", 0),
+             ("llama2_70b_decode_bs32", 0)]
+
+
+@pytest.mark.parametrize("name,partition", INT8_FULL)
+def test_int8_full_size(name, partition):
+    """The full-size decode batches over an INT8 cache: pa_decode_int8 on the cache holding
+    every token, then the fused pa_decode_step_int8 on a cache holding only the cached
+    tokens.  Every output row against the float64 oracle, and every slot of the caches
+    (the new tokens' codes and scales written by the step, nothing else touched)."""
+    b = config_batch(name)
+    log(f"int8 {name}: B={b.B} G={b.G} partition={partition}")
     ib = Int8Batch(b)
-    got = to_f64(ib.decode(partition))
-    rows = sorted(set([0, 1, b.B // 2, b.B - 1] + list(np.random.default_rng(3).integers(0, b.B, 4))))
-    mx, rel = check_close(got[rows], ib.oracle(rows), f"int8 {name}")
-    log(f"  rows {rows}: max_abs={mx:.3e} rel_l2={rel:.3e}")
-    assert np.all(np.isfinite(got))
+    ref = ib.oracle()
+    check_full(to_f64(ib.decode(partition)), ref, f"int8 decode {name} p={partition}", b.dtype)
+    ib.check_caches()
+    del ib
+    ib = Int8Batch(b, write_new=False)
+    check_full(to_f64(_step_int8(ib, partition)), ref, f"int8 step {name} p={partition}", b.dtype)
+    ib.check_caches()
 
 
 def test_int8_keeps_attention_close_to_16bit():
@@ -184,20 +214,6 @@ def _step_int8(ib, partition):
     return out
 
 
-def _check_new_slots(ib):
-    """The new tokens' codes and scales at their slots equal the oracle's quantisation."""
-    b = ib.b
-    phys = b.slot_mapping.astype(np.int64)
-    comp = b.slot_mapping_compact.astype(np.int64)
-    for dev, host in ((ib.kc, ib.hk), (ib.vc, ib.hv)):
-        got = dev[torch.from_numpy(phys // b.BS).cuda(), :, torch.from_numpy(phys % b.BS).cuda()]
-        assert np.array_equal(got.cpu().numpy(), host[comp // b.BS, :, comp % b.BS])
-    for dev, host in ((ib.ks, ib.hks), (ib.vs, ib.hvs)):
-        got = dev[torch.from_numpy(phys // b.BS).cuda(), :, torch.from_numpy(phys % b.BS).cuda()]
-        assert np.array_equal(got.cpu().numpy().view(np.uint32),
-                              host[comp // b.BS, :, comp % b.BS].view(np.uint32))
-
-
 STEP = [(dt, BS, G, p) for dt in ("bf16", "f16") for BS in (16, 256) for G in (1, 2, 4, 8)
         for p in (0, 256)]
 
@@ -210,7 +226,7 @@ def test_decode_step_int8_matches_oracle(dt, BS, G, partition):
     ib = Int8Batch(b, write_new=False)
     got = to_f64(_step_int8(ib, partition))
     check_close(got, ib.oracle(), f"int8 step {dt} BS{BS} G{G} p{partition}")
-    _check_new_slots(ib)
+    ib.check_caches()
 
 
 @pytest.mark.parametrize("partition", [0, 512, 32])
@@ -223,14 +239,35 @@ def test_decode_step_int8_length_edges(partition):
     ib = Int8Batch(b, write_new=False)
     got = to_f64(_step_int8(ib, partition))
     check_close(got, ib.oracle(), f"int8 step edges p{partition}")
-    _check_new_slots(ib)
+    ib.check_caches()
 
 
-def test_decode_step_int8_qwen3_shaped_sampled():
-    b = make_config("qwen3_0p6b_decode")
+@pytest.mark.parametrize("partition", [0, 64])
+def test_decode_step_int8_padding_and_out_of_pool_slots(partition):
+    """A padding slot (-1) and slots past the pool store nothing; those sequences still
+    attend to their new token, taken from the step's key and value rows."""
+    b = make_batch(B=6, Hq=8, Hkv=2, D=128, BS=16, dtype="bf16", scale=128 ** -0.5, seed=9700,
+                   lens=[40, 1, 300, 17, 129, 64], NB=256)
     ib = Int8Batch(b, write_new=False)
-    got = to_f64(_step_int8(ib, 0))
-    rows = [0, 1, 63, 64, 127]
-    mx, rel = check_close(got[rows], ib.oracle(rows), "int8 step qwen3-shaped")
-    log(f"  rows {rows}: max_abs={mx:.3e} rel_l2={rel:.3e}")
-    _check_new_slots(ib)
+    skip = [1, 3, 4]
+    slots = b.slot_mapping.copy()
+    slots[1] = -1
+    slots[3] = b.NB * b.BS            # one past the pool
+    slots[4] = (1 << 40)
+    dt = torch.bfloat16
+    out = torch.empty_like(ib.q)
+    pa_decode_step_int8(out, ib.q, bits_to_device(b.key_new, dt), bits_to_device(b.value_new, dt),
+                        torch.from_numpy(slots).cuda(), ib.kc, ib.vc, ib.ks, ib.vs, ib.tables,
+                        ib.lens, b.scale, b.max_context_len, partition)
+    torch.cuda.synchronize()
+    check_close(to_f64(out), ib.oracle(), f"int8 step skipped slots p{partition}")
+    # Expected caches: the cached tokens and the new tokens of the other sequences only.
+    kr, vr, comp, _ = cached_rows(b)
+    n = b.k_blocks.shape[0]
+    hk = np.full((n, b.Hkv, b.BS, b.D), SENT_CODE, np.int8); hv = hk.copy()
+    hks = np.full((n, b.Hkv, b.BS), SENT_SCALE, np.float32); hvs = hks.copy()
+    int8_kv.reshape_and_cache_int8(kr, vr, hk, hv, hks, hvs, comp, b.dtype)
+    sc = b.slot_mapping_compact.copy()
+    sc[skip] = -1
+    int8_kv.reshape_and_cache_int8(b.key_new, b.value_new, hk, hv, hks, hvs, sc, b.dtype)
+    ib.check_caches((hk, hv, hks, hvs))

@@ -1,6 +1,6 @@
 """Decode at the extremes of its supported sizes: a 128k-token context on one sequence, a
 batch of thousands of short sequences, and the INT8 and context-parallel paths at the long
-end, against the CPU oracle on sampled rows, through the C ABI."""
+end, against the CPU oracle on every output row, through the C ABI."""
 import numpy as np
 import pytest
 import torch
@@ -49,12 +49,9 @@ def test_thousands_of_sequences(G):
     b = make_batch(B=4096, Hq=2 * G, Hkv=2, D=128, BS=16, dtype="f16", scale=128 ** -0.5,
                    seed=9960 + G, lens_range=(1, 64))
     got = _decode(b, upload(b), 0)
-    rows = np.sort(np.random.default_rng(G).choice(b.B, 96, replace=False))
     kc, vc = host_caches_after_write(b)
-    ref = oracle.paged_decode(b.q[rows], kc, vc, b.block_tables_compact[rows], b.context_lens[rows],
-                              b.scale, b.dtype)
-    check_close(got[rows], ref, f"4096 sequences G{G}")
-    assert np.all(np.isfinite(got))
+    ref = oracle.paged_decode(b.q, kc, vc, b.block_tables_compact, b.context_lens, b.scale, b.dtype)
+    check_close(got, ref, f"4096 sequences G{G}")
 
 
 def test_context_parallel_128k_over_16_shards():
