@@ -252,6 +252,28 @@ int pa_decode_step(void* out, const void* q, const void* key, const void* value,
                    size_t workspace_bytes, int dtype, void* stream);
 
 /*
+ * pa_decode_step_scratch: pa_decode_step for callers that cannot allocate
+ * device memory (code under HIP-graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and rules as pa_decode_step
+ * with partition_size honoured, except that there is no workspace argument:
+ * the partial results of split contexts go to a static scratch array of
+ * 16 MiB that the library keeps on each device it runs on until the process
+ * ends.  The call allocates and frees nothing.  A split whose workspace would
+ * exceed 16 MiB (pa_decode_workspace_size) is rejected with PA_ERR_WORKSPACE
+ * before any HIP call.  Nothing in the scratch needs clearing (each call
+ * writes every byte it later reads), but all calls on one device share it:
+ * calls whose kernels overlap on one device (for example on two streams) race
+ * and give undefined results; calls ordered on one stream are safe.
+ */
+int pa_decode_step_scratch(void* out, const void* q, const void* key, const void* value,
+                           const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads,
+                           int head_dim, int block_size, int64_t num_blocks,
+                           int max_blocks_per_seq, int max_context_len, float scale,
+                           int partition_size, int dtype, void* stream);
+
+/*
  * Context parallelism.  A long sequence's context can be split across devices
  * (page "vllm-ascend architecture", sections 1.1 and 3.1): each device holds
  * some of the sequence's tokens in its own pool, attends over them, and the

@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     pa_decode_step,
     pa_decode_step_int8,
     pa_decode_step_rope,
+    pa_decode_step_scratch,
     pa_decode_workspace_size,
     pa_merge_partials,
     pa_prefill_chunk,

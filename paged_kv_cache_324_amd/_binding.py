@@ -60,6 +60,10 @@ def _declare(lib):
     lib.pa_decode_step.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                    c_int, c_int, c_int, c_int, c_int, c_i64, c_int, c_int, c_f,
                                    c_int, c_vp, c_sz, c_int, c_vp]
+    lib.pa_decode_step_scratch.restype = c_int
+    lib.pa_decode_step_scratch.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                           c_vp, c_int, c_int, c_int, c_int, c_int, c_i64, c_int,
+                                           c_int, c_f, c_int, c_int, c_vp]
     lib.pa_decode_order.restype = c_int
     lib.pa_decode_order.argtypes = [c_vp, c_int, c_vp]
     lib.pa_prefill_chunk.restype = c_int
@@ -345,6 +349,29 @@ def pa_decode_step(out, q, key, value, slot_mapping, k_cache, v_cache, block_tab
                               B, Hq, Hkv, D, BS, NB, block_tables.shape[1], int(max_context_len),
                               float(scale), int(partition_size), ws_ptr, ws_bytes, dt,
                               _stream(q, stream)))
+    return out
+
+
+def pa_decode_step_scratch(out, q, key, value, slot_mapping, k_cache, v_cache, block_tables,
+                           context_lens, scale: float, max_context_len: int,
+                           partition_size: int = 512, seq_order=None, stream=None) -> torch.Tensor:
+    """pa_decode_step without a workspace: split-K partials go to the library's static
+    scratch on the device (nothing is allocated by the call)."""
+    lib, B, Hq, Hkv, D, BS, NB, dt, _, _, order_ptr = _decode_common(
+        q, k_cache, v_cache, block_tables, context_lens, seq_order, out, max_context_len, 0, None)
+    if key.shape != (B, Hkv, D) or value.shape != key.shape or slot_mapping.shape != (B,):
+        raise ValueError("decode step: key/value must be [B][Hkv][D], slot_mapping [B]")
+    _dev(key, "key", q.dtype)
+    _dev(value, "value", q.dtype)
+    _check(lib.pa_decode_step_scratch(_dev(out, "out"), _dev(q, "q"), key.data_ptr(),
+                                      value.data_ptr(),
+                                      _dev(slot_mapping, "slot_mapping", torch.int64),
+                                      k_cache.data_ptr(), v_cache.data_ptr(),
+                                      _dev(block_tables, "block_tables", torch.int32),
+                                      _dev(context_lens, "context_lens", torch.int32), order_ptr,
+                                      B, Hq, Hkv, D, BS, NB, block_tables.shape[1],
+                                      int(max_context_len), float(scale), int(partition_size), dt,
+                                      _stream(q, stream)))
     return out
 
 

@@ -12,6 +12,7 @@
 #include <cstring>
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "pa.h"
 #include "pa_blocks.h"
@@ -76,6 +77,57 @@ bool valid_scale(float s) { return std::isfinite(s) && s > 0.f; }
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Scratch of pa_decode_step_scratch, the entry point for callers that cannot
+// allocate: the split-K partial results (normalised outputs and fp32 max/sum)
+// that pa_decode_step keeps in the caller's workspace.  Every device the
+// library runs on holds its own copy until the process ends; each call
+// rewrites every byte it later reads, so nothing in it needs clearing.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on the device that runs `stream` (the current
+// device for the null stream).  Host code never uses the array's name as an
+// address: it is looked up with hipGetSymbolAddress once per device, with that
+// device current, and kept.
+int scratch_address(hipStream_t stream, void** addr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* cached[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e;
+  if (stream) {
+    hipDevice_t d = -1;
+    e = hipStreamGetDevice(stream, &d);
+    dev = (int)d;
+  } else {
+    e = hipGetDevice(&dev);
+  }
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PA_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cached[dev]) {
+    int current = -1;
+    e = hipGetDevice(&current);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (current != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(PA_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (current != dev) {
+      const hipError_t e2 = hipSetDevice(current);
+      if (e2 != hipSuccess) return fail(PA_ERR_HIP, "hipSetDevice(%d): %s", current, hipGetErrorString(e2));
+    }
+    if (e != hipSuccess || !p)
+      return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    cached[dev] = p;
+  }
+  *addr = cached[dev];
+  return PA_OK;
+}
 
 int64_t num_partitions(int max_context_len, int partition_size) {
   if (partition_size <= 0 || max_context_len <= partition_size) return 1;
@@ -245,7 +297,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                 int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
                 int max_blocks_per_seq, int max_context_len, float scale, int partition_size,
                 void* workspace, size_t workspace_bytes, int dtype, void* stream,
-                int phases = pa::kPhaseAll) {
+                int phases = pa::kPhaseAll, bool use_scratch = false) {
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0");
   int st = check_cache(num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                        max_blocks_per_seq, dtype);
@@ -272,7 +324,16 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (grid > INT32_MAX || (int64_t)num_seqs * num_heads > INT32_MAX)
     return fail(PA_ERR_INVALID_ARG, "launch grid too large");
   const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, parts);
-  if (need > 0) {
+  if (need > 0 && use_scratch) {
+    if (need > kScratchBytes)
+      return fail(PA_ERR_WORKSPACE,
+                  "the split needs %zu bytes of workspace; the static scratch holds %zu (use a "
+                  "larger partition_size, or pa_decode_step with a workspace)", need, kScratchBytes);
+    // Every host check has passed: the scratch address is the first HIP call.
+    workspace_bytes = kScratchBytes;
+    const int st2 = scratch_address(static_cast<hipStream_t>(stream), &workspace);
+    if (st2 != PA_OK) return st2;
+  } else if (need > 0) {
     if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes required", need);
     if (workspace_bytes < need)
       return fail(PA_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, need);
@@ -409,6 +470,20 @@ int pa_decode_step(void* out, const void* q, const void* key, const void* value,
                      num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
                      workspace_bytes, dtype, stream);
+}
+
+int pa_decode_step_scratch(void* out, const void* q, const void* key, const void* value,
+                           const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads,
+                           int head_dim, int block_size, int64_t num_blocks,
+                           int max_blocks_per_seq, int max_context_len, float scale,
+                           int partition_size, int dtype, void* stream) {
+  NewTokens nt{key, value, slot_mapping, k_cache, v_cache};
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, seq_order, &nt, nullptr,
+                     nullptr, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, partition_size, nullptr, 0, dtype,
+                     stream, pa::kPhaseAll, /*use_scratch=*/true);
 }
 
 int pa_rope_reshape_and_cache(void* q, const void* key, const void* value, void* k_cache,

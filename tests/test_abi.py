@@ -317,3 +317,18 @@ def test_decode_partitions_validates_like_decode(lib):
     assert lib.pa_decode_partitions(*a) == -3          # split without a workspace
     a[15] = -1.0
     assert lib.pa_decode_partitions(*a) == -1
+
+
+def test_decode_step_scratch_rejects_a_split_beyond_the_scratch(lib):
+    """The no-allocation step refuses, before any HIP call, a split whose partials would not
+    fit its 16 MiB static scratch, and validates the rest like pa_decode_step."""
+    # out, q, key, value, slot, kc, vc, tables, lens, order, B, Hq, Hkv, D, BS, NB, maxb, maxL,
+    # scale, partition, dtype, stream
+    a = [P, P, P, P, P, P, P, P, P, None, 64, 64, 8, 128, 16, 100000, 512, 8192, 0.088, 16,
+         pa.PA_BF16, None]
+    assert lib.pa_decode_step_scratch(*a) == -3
+    assert "static scratch" in lib.pa_last_error().decode()
+    a[18] = 0.0
+    assert lib.pa_decode_step_scratch(*a) == -1
+    a[18], a[0] = 0.088, None
+    assert lib.pa_decode_step_scratch(*a) == -1
