@@ -38,10 +38,15 @@
  * Errors.  Every entry point returns a pa_status.  Host arguments are checked
  * before any HIP call; a failed check returns PA_ERR_INVALID_ARG or
  * PA_ERR_UNSUPPORTED and enqueues nothing; pa_last_error() then gives a
- * thread-local message.  A kernel launch failure returns PA_ERR_HIP.  Device
- * contents are the caller's contract: block ids outside [0, num_blocks) and
- * slots outside [0, num_blocks * block_size) are skipped by the kernels (never
- * dereferenced) and leave the affected output undefined.
+ * thread-local message.  A kernel launch failure returns PA_ERR_HIP, and so
+ * does every call that launches kernels when the library's parts were built
+ * from different versions of its sources (a check made once, at load).
+ * Device contents are the caller's contract: block ids outside [0,
+ * num_blocks), slots at or past num_blocks * block_size and context lengths
+ * above max_context_len are skipped or clamped by the kernels (never
+ * dereferenced) and leave the affected output undefined.  The checking build
+ * of the library (libpa_check.so, compiled with PA_CHECK_INDICES) also records
+ * each such case on the device; pa_take_index_errors reports them.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -59,7 +64,8 @@ typedef enum pa_status {
   PA_ERR_UNSUPPORTED = -2,  /* head_dim / block_size / group / dtype not built  */
   PA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required      */
   PA_ERR_HIP = -4,          /* a HIP launch reported an error                   */
-  PA_ERR_NO_BLOCKS = -5     /* block manager: too few free blocks (pa_blocks.h)  */
+  PA_ERR_NO_BLOCKS = -5,    /* block manager: too few free blocks (pa_blocks.h)  */
+  PA_ERR_BAD_INDEX = -6     /* checking build: kernels met out-of-range indices  */
 } pa_status;
 
 typedef enum pa_dtype { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
@@ -72,6 +78,43 @@ const char* pa_status_string(int status);
 
 /* Detail of the last failed call on the calling thread ("" if none). */
 const char* pa_last_error(void);
+
+/*
+ * Index checks (a debugging aid for the caller's block tables and slot
+ * mappings; the pages diagnose leaked or corrupted blocks from the block
+ * table's reference counts, page "Nano-vLLM-Ascend", section 4.2, problem 3).
+ * The library built with PA_CHECK_INDICES (libpa_check.so; same entry points,
+ * same results) makes its kernels record, in a per-device error record, every
+ * index they would otherwise skip or clamp:
+ *   PA_INDEX_ERR_BLOCK_ID     a block id that a context needs (or a copy source
+ *                             or destination) outside [0, num_blocks)
+ *   PA_INDEX_ERR_SLOT         a slot at or past num_blocks * block_size
+ *                             (negative slots are padding, not errors)
+ *   PA_INDEX_ERR_CONTEXT_LEN  a context length < 0 or above max_context_len
+ *                             (prefill: shorter than its chunk, or past the table)
+ *   PA_INDEX_ERR_QUERY_LOC    query_start_loc outside [0, num_tokens], or a chunk
+ *                             longer than max_query_len
+ * The offending access is still skipped, so nothing faults.
+ *
+ * pa_check_indices_enabled: 1 in the checking build, 0 otherwise.
+ *
+ * pa_take_index_errors: waits for `stream` (HOST pointers for the results),
+ * returns the kinds recorded on the stream's device since the previous call
+ * (an OR of the bits above), the kind and value of the first one, and clears
+ * the record.  Returns PA_OK when there were none, PA_ERR_BAD_INDEX when there
+ * were; PA_ERR_UNSUPPORTED in a library built without PA_CHECK_INDICES.
+ */
+enum {
+  PA_INDEX_ERR_BLOCK_ID = 1,
+  PA_INDEX_ERR_SLOT = 2,
+  PA_INDEX_ERR_CONTEXT_LEN = 4,
+  PA_INDEX_ERR_QUERY_LOC = 8
+};
+
+int pa_check_indices_enabled(void);
+
+int pa_take_index_errors(void* stream, uint32_t* kinds, uint32_t* first_kind,
+                         int64_t* first_value);
 
 /*
  * reshape_and_cache: write this step's new keys and values into their cache

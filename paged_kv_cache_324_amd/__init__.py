@@ -4,11 +4,13 @@ A thin Python face of ``libpa.so``: the functions here carry the names of the
 library's C entry points and only marshal torch device tensors into them.
 """
 from ._binding import (  # noqa: F401
+    CHECK_LIB_PATH,
     LIB_PATH,
     BlockManager,
     PA_BF16,
     PA_F16,
     PAError,
+    checked_indices,
     decode_workspace,
     load_library,
     pa_copy_blocks,
@@ -29,5 +31,6 @@ from ._binding import (  # noqa: F401
     pa_reshape_and_cache,
     pa_reshape_and_cache_int8,
     pa_rope_reshape_and_cache,
+    pa_take_index_errors,
     pa_version,
 )

@@ -8,6 +8,7 @@ there is no fallback path.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -18,11 +19,17 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
+# The same entry points built with PA_CHECK_INDICES: kernels record out-of-range
+# indices on the device (pa_take_index_errors) instead of skipping them silently.
+CHECK_LIB_PATH = os.path.join(_HERE, "libpa_check.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4
+PA_ERR_NO_BLOCKS, PA_ERR_BAD_INDEX = -5, -6
+PA_INDEX_ERR_BLOCK_ID, PA_INDEX_ERR_SLOT, PA_INDEX_ERR_CONTEXT_LEN, PA_INDEX_ERR_QUERY_LOC = 1, 2, 4, 8
 PA_F16, PA_BF16 = 0, 1
 
-_lib = None
+_libs = {}
+_checked = False      # calls go to libpa_check.so inside checked_indices()
 _lock = threading.Lock()
 
 
@@ -41,6 +48,10 @@ def _declare(lib):
     lib.pa_status_string.argtypes = [c_int]
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
+    lib.pa_check_indices_enabled.restype = c_int
+    lib.pa_check_indices_enabled.argtypes = []
+    lib.pa_take_index_errors.restype = c_int
+    lib.pa_take_index_errors.argtypes = [c_vp, c_vp, c_vp, c_vp]
     lib.pa_reshape_and_cache.restype = c_int
     lib.pa_reshape_and_cache.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_int, c_int, c_int,
                                          c_i64, c_int, c_vp]
@@ -126,19 +137,51 @@ def _declare(lib):
     return lib
 
 
-def load_library(build_if_missing: bool = True):
-    """Load libpa.so (building it first only if no built library exists)."""
-    global _lib
+def load_library(build_if_missing: bool = True, checked: bool | None = None):
+    """Load libpa.so, or libpa_check.so inside checked_indices() or with checked=True
+    (building both first only if the library is not built)."""
+    path = CHECK_LIB_PATH if (_checked if checked is None else checked) else LIB_PATH
     with _lock:
-        if _lib is not None:
-            return _lib
-        if not os.path.exists(LIB_PATH):
+        lib = _libs.get(path)
+        if lib is not None:
+            return lib
+        if not os.path.exists(path):
             if not build_if_missing:
-                raise ImportError(f"{LIB_PATH} is not built")
+                raise ImportError(f"{path} is not built")
             from .build import build_library
             build_library()
-        _lib = _declare(ctypes.CDLL(LIB_PATH))
-        return _lib
+        lib = _libs[path] = _declare(ctypes.CDLL(path))
+        return lib
+
+
+@contextlib.contextmanager
+def checked_indices():
+    """Within the block, every call of this module goes to libpa_check.so, whose kernels
+    record out-of-range block ids, slots and lengths (read them with pa_take_index_errors).
+    Not thread-safe: it switches the whole module."""
+    global _checked
+    prev = _checked
+    _checked = True
+    try:
+        yield load_library()
+    finally:
+        _checked = prev
+
+
+def pa_take_index_errors(stream=None):
+    """Wait for the stream and return ``(status, kinds, first_kind, first_value)`` of the index
+    errors the checking library's kernels recorded on its device since the last call
+    (status PA_OK or PA_ERR_BAD_INDEX), clearing them.  Uses libpa_check.so."""
+    lib = load_library(checked=True)
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    kinds, first_kind, first_value = ctypes.c_uint32(), ctypes.c_uint32(), ctypes.c_int64()
+    st = lib.pa_take_index_errors(s, ctypes.byref(kinds), ctypes.byref(first_kind),
+                                  ctypes.byref(first_value))
+    if st not in (PA_OK, PA_ERR_BAD_INDEX):
+        raise PAError(st, f"{lib.pa_status_string(st).decode()}: {lib.pa_last_error().decode()}")
+    return st, kinds.value, first_kind.value, first_value.value
 
 
 def _check(status: int) -> None:

@@ -1,7 +1,14 @@
-"""Build libpa.so (the C-ABI paged-attention library) for gfx950 with hipcc.
+"""Build the C-ABI paged-attention libraries for gfx950 with hipcc.
 
-Every call recompiles all sources in parallel into ``_build/`` and links
-``libpa.so`` next to this file (replaced atomically).
+Two libraries come from the same sources:
+
+* ``libpa.so``: the library;
+* ``libpa_check.so``: the same entry points compiled with ``PA_CHECK_INDICES``, whose
+  kernels record out-of-range block ids, slots and lengths on the device instead of
+  skipping them silently (``pa_take_index_errors``).
+
+Every call recompiles all sources in parallel into ``_build/`` and ``_build_check/`` and
+links both libraries next to this file (each replaced atomically).
 """
 from __future__ import annotations
 
@@ -18,7 +25,12 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpa.so")
+CHECK_LIB = os.path.join(HERE, "libpa_check.so")
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
+
+# (library, object directory, preprocessor definitions)
+VARIANTS = ((LIB, BUILD, ()),
+            (CHECK_LIB, os.path.join(HERE, "_build_check"), ("PA_CHECK_INDICES",)))
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -36,9 +48,15 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libpa.so")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, "-c", src, "-o", obj]
+def sources() -> list[str]:
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+
+
+def compile_source(src: str, out_dir: str, defines=()) -> str:
+    """Compile one source into ``out_dir`` with extra preprocessor definitions; the object."""
+    os.makedirs(out_dir, exist_ok=True)
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    cmd = [_hipcc(), *COMMON, *(f"-D{d}" for d in defines), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,20 +65,28 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build_library(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    jobs = min(len(sources), max(1, min(16, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, sources))
-    tmp = LIB + f".tmp{os.getpid()}"
+def link_library(objs, lib: str) -> str:
+    """Link objects into a shared library at ``lib`` (replaced atomically)."""
+    tmp = lib + f".tmp{os.getpid()}"
     cmd = [_hipcc(), "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"built {LIB}", file=sys.stderr)
+    os.replace(tmp, lib)
+    return lib
+
+
+def build_library(verbose: bool = False) -> str:
+    """Build both libraries; returns the path of libpa.so."""
+    srcs = sources()
+    jobs = [(lib, out_dir, defines, src) for lib, out_dir, defines in VARIANTS for src in srcs]
+    workers = min(len(jobs), max(1, min(16, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        objs = list(ex.map(lambda j: compile_source(j[3], j[1], j[2]), jobs))
+    for lib, out_dir, _ in VARIANTS:
+        link_library([o for o, j in zip(objs, jobs) if j[0] == lib], lib)
+        if verbose:
+            print(f"built {lib}", file=sys.stderr)
     return LIB
 
 

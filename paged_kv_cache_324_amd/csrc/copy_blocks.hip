@@ -21,11 +21,17 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs a) {
     const bool is_v = rem >= a.block_chunks;
     const int64_t chunk = is_v ? rem - a.block_chunks : rem;
     const int64_t src = a.src[i], dst = a.dst[i];
+    if (chunk == 0 && !is_v) {
+      report_index_error(a.index_errors, src < 0 || src >= a.num_blocks, kErrBlockId, src);
+      report_index_error(a.index_errors, dst < 0 || dst >= a.num_blocks, kErrBlockId, dst);
+    }
     if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks || src == dst) continue;
     u32x4* cache = static_cast<u32x4*>(is_v ? a.v_cache : a.k_cache);
     cache[dst * a.block_chunks + chunk] = cache[src * a.block_chunks + chunk];
   }
 }
+
+PA_LAYOUT_PROBE(copy_blocks)
 
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s) {
   const int64_t total = a.num_copies * 2 * a.block_chunks;

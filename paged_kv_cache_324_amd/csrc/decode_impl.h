@@ -82,6 +82,7 @@ constexpr float kEmptyMax = -1.0e30f;  // finite "no token yet" max: keeps 2^(m 
 
 __device__ __forceinline__ int clamp_context(const DecodeArgs& a, int seq) {
   const int L = a.context_lens[seq];
+  report_index_error(a.index_errors, L < 0 || L > a.max_context_len, kErrContextLen, L);
   return L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
 }
 
@@ -244,6 +245,7 @@ void decode_partition_kernel(const DecodeArgs a) {
     __syncthreads();  // previous chunk's table reads are done
     if ((int)threadIdx.x < nchunk_blk) {
       const int32_t blk = c0 == t0 ? tbl_first : bt[lb0 + threadIdx.x];
+      report_index_error(a.index_errors, blk < 0 || blk >= nb32, kErrBlockId, blk);
       s_tbl[threadIdx.x] = (blk >= 0 && blk < nb32) ? blk : -1;
     }
     __syncthreads();
@@ -367,6 +369,7 @@ void decode_partition_kernel(const DecodeArgs a) {
       acc[g][7] = fmaf(acc[g][7], alpha, p * hi_f32<DT>(v_new.w));
     }
     const int64_t slot = a.slot_mapping[seq];
+    if (lane == 0) report_index_error(a.index_errors, slot >= a.num_slots, kErrSlot, slot);
     if (r == 0 && slot >= 0 && slot < a.num_slots) {
       const int64_t dst = (slot * a.num_kv_heads + kvh) * D;
       reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.k_cache_w) + dst)[c] = k_new;

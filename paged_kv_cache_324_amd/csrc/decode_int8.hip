@@ -169,6 +169,7 @@ void decode_int8_kernel(const DecodeArgs a) {
       const int32_t blk = __builtin_amdgcn_readlane(ids, gr);
       const int nv = min(16, t1c - g0);
       const bool ok = nv > 0 && blk >= 0 && blk < nb32;
+      report_index_error(a.index_errors, nv > 0 && !ok, kErrBlockId, blk);
       const int off_in_blk = g0 - lb * BS;
       const uint64_t off = ok ? (uint64_t)(uint32_t)blk * block_bytes + (uint64_t)off_in_blk * row_bytes : 0ull;
       const uint32_t nrec = ok ? (uint32_t)(nv - 1) * row_bytes + D : 0u;
@@ -330,6 +331,7 @@ void decode_int8_kernel(const DecodeArgs a) {
       }
     }
     const int64_t slot = a.slot_mapping[seq];
+    if (lane == 0) report_index_error(a.index_errors, slot >= a.num_slots, kErrSlot, slot);
     if (lane < 32 && slot >= 0 && slot < a.num_slots) {
       const int64_t sblk = slot / BS;
       const int64_t srow = (sblk * a.num_kv_heads + kvh) * BS + (slot - sblk * BS);
@@ -416,6 +418,8 @@ void decode_int8_kernel(const DecodeArgs a) {
     reinterpret_cast<float2*>(a.part_ml)[prow + g] = make_float2(M, den);
   }
 }
+
+PA_LAYOUT_PROBE(decode_int8)
 
 template <int DT, int BS, int G>
 hipError_t launch_int8_t(const DecodeArgs& a, int phases, hipStream_t s) {

@@ -143,6 +143,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
   const int64_t new_row = ((int64_t)seq * a.num_kv_heads + kvh) * D;
   if (new_here && wave == 0 && lane < 32) {
     const int64_t slot = a.slot_mapping[seq];
+    if (lane == 0) report_index_error(a.index_errors, slot >= a.num_slots, kErrSlot, slot);
     if (slot >= 0 && slot < a.num_slots) {
       const void* src = lane < 16 ? a.key_new : a.value_new;
       void* dst = lane < 16 ? a.k_cache_w : a.v_cache_w;
@@ -196,6 +197,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
       const int32_t blk = __builtin_amdgcn_readlane(ids, gr);
       const int nv = min(16, t1c - g0);
       const bool ok = nv > 0 && blk >= 0 && blk < nb32;
+      report_index_error(a.index_errors, nv > 0 && !ok, kErrBlockId, blk);
       const uint64_t off = ok ? (uint64_t)(uint32_t)blk * block_bytes +
                                     (uint64_t)(g0 - lb * BS) * row_bytes
                               : 0ull;

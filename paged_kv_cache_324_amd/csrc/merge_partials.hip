@@ -87,6 +87,8 @@ __global__ __launch_bounds__(64) void merge_partials_kernel(const MergePartialsA
   if (a.out_ml && lane == 0) reinterpret_cast<float2*>(a.out_ml)[row] = make_float2(M, den);
 }
 
+PA_LAYOUT_PROBE(merge_partials)
+
 hipError_t launch_merge_partials(const MergePartialsArgs& a, int dtype, int head_dim,
                                  hipStream_t s) {
   const dim3 grid((unsigned)a.num_rows), block(64);

@@ -86,14 +86,15 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 constexpr size_t kScratchBytes = size_t(16) << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
-// Device address of `scratch` on the device that runs `stream` (the current
-// device for the null stream).  Host code never uses the array's name as an
-// address: it is looked up with hipGetSymbolAddress once per device, with that
-// device current, and kept.
-int scratch_address(hipStream_t stream, void** addr) {
-  constexpr int kMaxDevices = 64;
+// Device address of a file-scope __device__ variable on the device that runs
+// `stream` (the current device for the null stream).  Host code never uses such
+// a variable's name as an address: it is looked up with hipGetSymbolAddress
+// once per device, with that device current, and kept in `cached`.
+constexpr int kMaxDevices = 64;
+
+int device_symbol(hipStream_t stream, const void* symbol, const char* name,
+                  void* (&cached)[kMaxDevices], void** addr) {
   static std::mutex mu;
-  static void* cached[kMaxDevices] = {};
   int dev = -1;
   hipError_t e;
   if (stream) {
@@ -105,7 +106,7 @@ int scratch_address(hipStream_t stream, void** addr) {
   }
   if (e != hipSuccess) return fail(PA_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
   if (dev < 0 || dev >= kMaxDevices)
-    return fail(PA_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+    return fail(PA_ERR_UNSUPPORTED, "device %d: the library serves devices 0..%d", dev,
                 kMaxDevices - 1);
   std::lock_guard<std::mutex> lock(mu);
   if (!cached[dev]) {
@@ -115,17 +116,88 @@ int scratch_address(hipStream_t stream, void** addr) {
     if (current != dev && (e = hipSetDevice(dev)) != hipSuccess)
       return fail(PA_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
     void* p = nullptr;
-    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    e = hipGetSymbolAddress(&p, symbol);
     if (current != dev) {
       const hipError_t e2 = hipSetDevice(current);
       if (e2 != hipSuccess) return fail(PA_ERR_HIP, "hipSetDevice(%d): %s", current, hipGetErrorString(e2));
     }
     if (e != hipSuccess || !p)
-      return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+      return fail(PA_ERR_HIP, "hipGetSymbolAddress(%s) on device %d: %s", name, dev,
                   hipGetErrorString(e));
     cached[dev] = p;
   }
   *addr = cached[dev];
+  return PA_OK;
+}
+
+int scratch_address(hipStream_t stream, void** addr) {
+  static void* cached[kMaxDevices] = {};
+  return device_symbol(stream, &HIP_SYMBOL(scratch), "scratch", cached, addr);
+}
+
+#ifdef PA_CHECK_INDICES
+// The index errors the kernels of this (checking) build record, one record
+// per device (see IndexErrors); read and cleared by pa_take_index_errors.
+static __device__ pa::IndexErrors index_errors;
+#endif
+
+// Where this call's kernels record index errors: the device's record in a
+// PA_CHECK_INDICES build (after every host check: the first HIP call), null
+// otherwise (no HIP call).
+int index_errors_address(hipStream_t stream, pa::IndexErrors** addr) {
+#ifdef PA_CHECK_INDICES
+  static void* cached[kMaxDevices] = {};
+  void* p = nullptr;
+  const int st = device_symbol(stream, &HIP_SYMBOL(index_errors), "index_errors", cached, &p);
+  *addr = static_cast<pa::IndexErrors*>(p);
+  return st;
+#else
+  (void)stream;
+  *addr = nullptr;
+  return PA_OK;
+#endif
+}
+
+// Every kernel translation unit's fingerprint of the launch-argument structs
+// (pa_kernels.h), compared with this unit's once, when the library is loaded.
+const char* layout_error() {
+  static char msg[320];
+  static const bool bad = [] {
+    struct Probe {
+      const char* unit;
+      uint64_t (*fn)();
+    };
+    const Probe probes[] = {{"reshape_and_cache.hip", pa::layout_probe_reshape_and_cache},
+                            {"rope_reshape.hip", pa::layout_probe_rope_reshape},
+                            {"reshape_int8.hip", pa::layout_probe_reshape_int8},
+                            {"copy_blocks.hip", pa::layout_probe_copy_blocks},
+                            {"decode_f16.hip", pa::layout_probe_decode_f16},
+                            {"decode_bf16.hip", pa::layout_probe_decode_bf16},
+                            {"decode_int8.hip", pa::layout_probe_decode_int8},
+                            {"merge_partials.hip", pa::layout_probe_merge_partials},
+                            {"prefill.hip", pa::layout_probe_prefill}};
+    const uint64_t mine = pa::args_layout();
+    for (const Probe& pr : probes) {
+      const uint64_t theirs = pr.fn();
+      if (theirs != mine) {
+        snprintf(msg, sizeof(msg),
+                 "library build mismatch: %s was compiled with another layout of the kernel "
+                 "launch arguments (fingerprint %016llx, this unit %016llx); rebuild the whole "
+                 "library from one source tree",
+                 pr.unit, (unsigned long long)theirs, (unsigned long long)mine);
+        return true;
+      }
+    }
+    return false;
+  }();
+  return bad ? msg : nullptr;
+}
+
+[[maybe_unused]] const char* const g_layout_error_at_load = layout_error();
+
+// First check of every entry point that launches kernels.
+int check_build() {
+  if (const char* m = layout_error()) return fail(PA_ERR_HIP, "%s", m);
   return PA_OK;
 }
 
@@ -181,15 +253,58 @@ const char* pa_status_string(int status) {
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: HIP runtime error";
     case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: too few free blocks";
+    case PA_ERR_BAD_INDEX: return "PA_ERR_BAD_INDEX: kernels met out-of-range block ids, slots or lengths";
     default: return "unknown pa_status";
   }
 }
 
 const char* pa_last_error(void) { return pa::g_last_error; }
 
+int pa_check_indices_enabled(void) {
+#ifdef PA_CHECK_INDICES
+  return 1;
+#else
+  return 0;
+#endif
+}
+
+int pa_take_index_errors(void* stream, uint32_t* kinds, uint32_t* first_kind,
+                         int64_t* first_value) {
+  if (const int b = check_build()) return b;
+  if (!kinds || !first_kind || !first_value) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  *kinds = 0;
+  *first_kind = 0;
+  *first_value = 0;
+#ifdef PA_CHECK_INDICES
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  pa::IndexErrors* dev = nullptr;
+  if (const int e = index_errors_address(s, &dev)) return e;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+  pa::IndexErrors rec{};
+  e = hipMemcpy(&rec, dev, sizeof(rec), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "reading the index-error record: %s", hipGetErrorString(e));
+  const pa::IndexErrors zero{};
+  e = hipMemcpy(dev, &zero, sizeof(zero), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "clearing the index-error record: %s", hipGetErrorString(e));
+  *kinds = rec.kinds;
+  *first_kind = rec.first_kind;
+  *first_value = rec.first_value;
+  if (rec.kinds != 0)
+    return fail(PA_ERR_BAD_INDEX, "index errors 0x%x; first: kind 0x%x, value %lld", rec.kinds,
+                rec.first_kind, (long long)rec.first_value);
+  return ok();
+#else
+  (void)stream;
+  return fail(PA_ERR_UNSUPPORTED,
+              "this library is built without PA_CHECK_INDICES; index checks are in libpa_check.so");
+#endif
+}
+
 int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* src, const int64_t* dst,
                    int64_t num_copies, int num_kv_heads, int head_dim, int block_size,
                    int64_t num_blocks, int dtype, void* stream) {
+  if (const int b = check_build()) return b;
   if (num_copies < 0) return fail(PA_ERR_INVALID_ARG, "num_copies %lld < 0", (long long)num_copies);
   if (!supported_head_dim(head_dim)) return fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported", head_dim);
   if (!supported_block_size(block_size))
@@ -208,6 +323,7 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* src, const int64
   a.num_copies = num_copies;
   a.num_blocks = num_blocks;
   a.block_chunks = (int64_t)block_size * num_kv_heads * head_dim * 2 / 16;
+  if (const int e = index_errors_address(static_cast<hipStream_t>(stream), &a.index_errors)) return e;
   return hip_status(pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)), "copy_blocks launch");
 }
 
@@ -215,6 +331,7 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
                          const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,
                          int head_dim, int block_size, int64_t num_blocks, int dtype,
                          void* stream) {
+  if (const int b = check_build()) return b;
   if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens must be >= 0");
   if (num_kv_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
   if (!supported_head_dim(head_dim))
@@ -237,6 +354,7 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
   a.num_tokens = num_tokens;
   a.num_slots = num_blocks * (int64_t)block_size;
   a.row_chunks = num_kv_heads * head_dim * 2 / 16;
+  if (const int e = index_errors_address(static_cast<hipStream_t>(stream), &a.index_errors)) return e;
   return hip_status(pa::launch_reshape_and_cache(a, static_cast<hipStream_t>(stream)),
                     "reshape_and_cache launch");
 }
@@ -298,6 +416,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                 int max_blocks_per_seq, int max_context_len, float scale, int partition_size,
                 void* workspace, size_t workspace_bytes, int dtype, void* stream,
                 int phases = pa::kPhaseAll, bool use_scratch = false) {
+  if (const int b = check_build()) return b;
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0");
   int st = check_cache(num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                        max_blocks_per_seq, dtype);
@@ -380,6 +499,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   const int group = num_heads / num_kv_heads;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (const int e = index_errors_address(s, &a.index_errors)) return e;
   // PA_F16 / PA_BF16 are the kernels' dtype codes.
   hipError_t e = i8 ? pa::launch_decode_int8(a, dtype, block_size, group, phases, s)
                  : dtype == PA_BF16 ? pa::launch_decode_bf16(a, head_dim, block_size, group, phases, s)
@@ -419,6 +539,7 @@ int pa_decode_merge(void* out, const int32_t* context_lens, const int32_t* seq_o
                     int num_seqs, int num_heads, int head_dim, int max_context_len,
                     int partition_size, void* workspace, size_t workspace_bytes, int dtype,
                     void* stream) {
+  if (const int b = check_build()) return b;
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0");
   if (num_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_heads must be >= 1");
   if (!supported_head_dim(head_dim))
@@ -451,6 +572,7 @@ int pa_decode_merge(void* out, const int32_t* context_lens, const int32_t* seq_o
   a.num_parts = (int)parts;
   a.part_tokens = partition_size;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (const int e = index_errors_address(s, &a.index_errors)) return e;
   // The merge alone depends on neither the block size nor the head grouping.
   const hipError_t e = dtype == PA_BF16
                            ? pa::launch_decode_bf16(a, head_dim, 16, 1, pa::kPhaseMerge, s)
@@ -492,6 +614,7 @@ int pa_rope_reshape_and_cache(void* q, const void* key, const void* value, void*
                               int64_t num_tokens, int num_heads, int num_kv_heads, int head_dim,
                               int block_size, int64_t num_blocks, int64_t max_position, int dtype,
                               void* stream) {
+  if (const int b = check_build()) return b;
   if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens must be >= 0");
   if (num_kv_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
   if (q && num_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_heads must be >= 1 with q");
@@ -527,6 +650,7 @@ int pa_rope_reshape_and_cache(void* q, const void* key, const void* value, void*
   a.max_position = max_position;
   a.num_heads = q ? num_heads : 0;
   a.num_kv_heads = num_kv_heads;
+  if (const int e = index_errors_address(static_cast<hipStream_t>(stream), &a.index_errors)) return e;
   return hip_status(pa::launch_rope_reshape(a, dtype, head_dim, static_cast<hipStream_t>(stream)),
                     "rope_reshape_and_cache launch");
 }
@@ -547,6 +671,7 @@ int pa_decode_partial(void* out, float* out_ml, const void* q, const void* k_cac
 int pa_merge_partials(void* out, float* out_ml, const void* partial_o, const float* partial_ml,
                       int num_shards, int num_seqs, int num_heads, int head_dim, int dtype,
                       void* stream) {
+  if (const int b = check_build()) return b;
   if (num_shards < 1) return fail(PA_ERR_INVALID_ARG, "num_shards must be >= 1");
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0");
   if (num_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_heads must be >= 1");
@@ -601,6 +726,7 @@ int pa_reshape_and_cache_int8(const void* key, const void* value, void* k_codes,
                               float* k_scales, float* v_scales, const int64_t* slot_mapping,
                               int64_t num_tokens, int num_kv_heads, int head_dim, int block_size,
                               int64_t num_blocks, int dtype, void* stream) {
+  if (const int b = check_build()) return b;
   if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens must be >= 0");
   if (num_kv_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
   if (!supported_head_dim(head_dim))
@@ -626,6 +752,7 @@ int pa_reshape_and_cache_int8(const void* key, const void* value, void* k_codes,
   a.num_slots = num_blocks * (int64_t)block_size;
   a.num_kv_heads = num_kv_heads;
   a.block_size = block_size;
+  if (const int e = index_errors_address(static_cast<hipStream_t>(stream), &a.index_errors)) return e;
   return hip_status(pa::launch_reshape_int8(a, dtype, head_dim, static_cast<hipStream_t>(stream)),
                     "reshape_and_cache_int8 launch");
 }
@@ -681,6 +808,7 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
                      int num_heads, int num_kv_heads, int head_dim, int block_size,
                      int64_t num_blocks, int max_blocks_per_seq, int max_query_len, float scale,
                      int dtype, void* stream) {
+  if (const int b = check_build()) return b;
   if (num_seqs < 0 || num_tokens < 0)
     return fail(PA_ERR_INVALID_ARG, "num_seqs and num_tokens must be >= 0");
   int st = check_cache(num_heads, num_kv_heads, head_dim, block_size, num_blocks,
@@ -712,6 +840,7 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
   a.max_query_len = max_query_len;
   a.q_tiles = 0;  // chosen by the launcher
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  if (const int e = index_errors_address(static_cast<hipStream_t>(stream), &a.index_errors)) return e;
   return hip_status(pa::launch_prefill(a, dtype, head_dim, block_size, num_heads / num_kv_heads,
                                        static_cast<hipStream_t>(stream)),
                     "prefill launch");

@@ -4,7 +4,26 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa_kernels.h"
+
 namespace pa {
+
+// Records an index error in a PA_CHECK_INDICES build (see IndexErrors);
+// compiles to nothing in other builds.
+__device__ __forceinline__ void report_index_error(IndexErrors* e, bool bad, uint32_t kind,
+                                                   int64_t value) {
+#ifdef PA_CHECK_INDICES
+  if (bad && e != nullptr) {
+    atomicOr(&e->kinds, kind);
+    if (atomicCAS(&e->first_kind, 0u, kind) == 0u) e->first_value = value;
+  }
+#else
+  (void)e;
+  (void)bad;
+  (void)kind;
+  (void)value;
+#endif
+}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

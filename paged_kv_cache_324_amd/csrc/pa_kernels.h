@@ -2,9 +2,27 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace pa {
+
+// Index errors a PA_CHECK_INDICES build records on the device instead of
+// skipping the access silently: the kinds seen (an OR of the bits) and the
+// kind and offending value of the first one.  In other builds the kernels
+// never touch it and the pointer in the launch arguments is null.
+enum : uint32_t {
+  kErrBlockId = 1,      // a block id a context needs lies outside [0, num_blocks)
+  kErrSlot = 2,         // a slot at or past num_blocks * block_size (negative = padding, legal)
+  kErrContextLen = 4,   // a context length < 0, above max_context_len, or shorter than its chunk
+  kErrQueryLoc = 8,     // query_start_loc not within [0, num_tokens], or a chunk above max_query_len
+};
+
+struct IndexErrors {
+  uint32_t kinds;
+  uint32_t first_kind;
+  int64_t first_value;
+};
 
 struct ReshapeArgs {
   const void* key;
@@ -15,6 +33,7 @@ struct ReshapeArgs {
   int64_t num_tokens;
   int64_t num_slots;   // num_blocks * block_size
   int row_chunks;      // 16-byte chunks in one token's num_kv_heads * head_dim row
+  IndexErrors* index_errors;  // PA_CHECK_INDICES builds only; null otherwise
 };
 
 struct RopeReshapeArgs {
@@ -32,6 +51,7 @@ struct RopeReshapeArgs {
   int64_t max_position;
   int num_heads;
   int num_kv_heads;
+  IndexErrors* index_errors;  // PA_CHECK_INDICES builds only; null otherwise
 };
 
 struct ReshapeInt8Args {
@@ -46,6 +66,7 @@ struct ReshapeInt8Args {
   int64_t num_slots;
   int num_kv_heads;
   int block_size;
+  IndexErrors* index_errors;  // PA_CHECK_INDICES builds only; null otherwise
 };
 
 struct CopyBlocksArgs {
@@ -56,9 +77,15 @@ struct CopyBlocksArgs {
   int64_t num_copies;
   int64_t num_blocks;
   int64_t block_chunks;  // 16-byte chunks in one block of one cache
+  IndexErrors* index_errors;  // PA_CHECK_INDICES builds only; null otherwise
 };
 
 struct DecodeArgs {
+#ifdef PA_LAYOUT_SKEW_TEST
+  // Only in the layout check's test object: a translation unit compiled
+  // against an older DecodeArgs, every later field shifted.
+  const void* stale_field;
+#endif
   void* out;
   const void* q;
   const void* k_cache;
@@ -103,6 +130,7 @@ struct DecodeArgs {
   int num_parts;       // partitions per sequence in the grid
   int part_tokens;     // tokens per partition (>= every context when unsplit)
   float scale_log2;    // scale * log2(e)
+  IndexErrors* index_errors;  // PA_CHECK_INDICES builds only; null otherwise
 };
 
 struct PrefillArgs {
@@ -123,6 +151,7 @@ struct PrefillArgs {
   int max_query_len;
   int q_tiles;         // query tiles per sequence in the grid
   float scale_log2;
+  IndexErrors* index_errors;  // PA_CHECK_INDICES builds only; null otherwise
 };
 
 hipError_t launch_reshape_and_cache(const ReshapeArgs& a, hipStream_t s);
@@ -159,5 +188,54 @@ hipError_t launch_merge_partials(const MergePartialsArgs& a, int dtype, int head
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int block_size,
                           int group, hipStream_t s);
+
+// ---- layout check ----------------------------------------------------------
+// The launch-argument structs cross translation units by value, so every unit
+// must compile them alike: a kernel object built against an older version of
+// this header would read every field after a change at the wrong offset.  Each
+// kernel unit exports this fingerprint as it compiled it (PA_LAYOUT_PROBE) and
+// the C ABI compares them with its own at load; on a mismatch every entry
+// point that launches a kernel fails instead.
+constexpr uint64_t layout_mix(uint64_t h, uint64_t v) { return (h ^ v) * 1099511628211ull; }
+
+constexpr uint64_t args_layout() {
+  uint64_t h = 1469598103934665603ull;
+  const uint64_t parts[] = {
+      sizeof(ReshapeArgs), offsetof(ReshapeArgs, num_tokens), offsetof(ReshapeArgs, index_errors),
+      sizeof(RopeReshapeArgs), offsetof(RopeReshapeArgs, num_tokens),
+      offsetof(RopeReshapeArgs, index_errors),
+      sizeof(ReshapeInt8Args), offsetof(ReshapeInt8Args, num_tokens),
+      offsetof(ReshapeInt8Args, index_errors),
+      sizeof(CopyBlocksArgs), offsetof(CopyBlocksArgs, num_copies),
+      offsetof(CopyBlocksArgs, index_errors),
+      sizeof(DecodeArgs), offsetof(DecodeArgs, q), offsetof(DecodeArgs, part_out),
+      offsetof(DecodeArgs, key_new), offsetof(DecodeArgs, k_scales), offsetof(DecodeArgs, positions),
+      offsetof(DecodeArgs, num_slots), offsetof(DecodeArgs, num_seqs),
+      offsetof(DecodeArgs, scale_log2), offsetof(DecodeArgs, index_errors),
+      sizeof(MergePartialsArgs), offsetof(MergePartialsArgs, num_rows),
+      sizeof(PrefillArgs), offsetof(PrefillArgs, num_blocks), offsetof(PrefillArgs, scale_log2),
+      offsetof(PrefillArgs, index_errors), sizeof(IndexErrors),
+#ifdef PA_CHECK_INDICES
+      1,
+#else
+      0,
+#endif
+  };
+  for (uint64_t v : parts) h = layout_mix(h, v);
+  return h;
+}
+
+#define PA_LAYOUT_PROBE(unit) \
+  uint64_t layout_probe_##unit() { return args_layout(); }
+
+uint64_t layout_probe_reshape_and_cache();
+uint64_t layout_probe_rope_reshape();
+uint64_t layout_probe_reshape_int8();
+uint64_t layout_probe_copy_blocks();
+uint64_t layout_probe_decode_f16();
+uint64_t layout_probe_decode_bf16();
+uint64_t layout_probe_decode_int8();
+uint64_t layout_probe_merge_partials();
+uint64_t layout_probe_prefill();
 
 }  // namespace pa

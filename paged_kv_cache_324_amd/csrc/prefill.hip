@@ -2,6 +2,8 @@
 #include "prefill_impl.h"
 
 namespace pa {
+PA_LAYOUT_PROBE(prefill)
+
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int block_size, int group,
                           hipStream_t s) {
   if (head_dim != kPrefillD) return hipErrorInvalidValue;

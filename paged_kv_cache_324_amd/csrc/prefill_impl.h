@@ -127,11 +127,20 @@ void prefill_kernel(const PrefillArgs a) {
   if (seq < 0 || seq >= a.num_seqs) return;
 
   const int s0 = a.query_start_loc[seq];
-  const int n = min(a.query_start_loc[seq + 1] - s0, a.max_query_len);
-  int L = a.context_lens[seq];
-  L = max(0, min(L, a.max_blocks * BS));
+  const int n_raw = a.query_start_loc[seq + 1] - s0;
+  const int n = min(n_raw, a.max_query_len);
+  const int L_raw = a.context_lens[seq];
+  const int L = max(0, min(L_raw, a.max_blocks * BS));
   const int c = L - n;  // cached tokens before the chunk (negative: caller error)
   const int t0 = qt * QT;
+  if (threadIdx.x == 0 && qt == a.q_tiles - 1) {  // once per (sequence, KV head)
+    report_index_error(a.index_errors,
+                       s0 < 0 || n_raw < 0 || n_raw > a.max_query_len ||
+                           (int64_t)s0 + n_raw > a.num_tokens,
+                       kErrQueryLoc, s0);
+    report_index_error(a.index_errors, L_raw < n_raw || L_raw > a.max_blocks * BS,
+                       kErrContextLen, L_raw);
+  }
   if (n <= 0 || t0 >= n) return;
   if (s0 < 0 || (int64_t)s0 + n > a.num_tokens) return;  // malformed query_start_loc: skip
 
@@ -192,6 +201,7 @@ void prefill_kernel(const PrefillArgs a) {
     const int32_t blk = __builtin_amdgcn_readlane(ids, (kv0 / NK) & 63);
     const int nvalid = min(16, L - key0);
     const bool ok = nvalid > 0 && blk >= 0 && blk < nb32;
+    report_index_error(a.index_errors, nvalid > 0 && !ok, kErrBlockId, blk);
     const uint64_t boff = ok ? (uint64_t)(uint32_t)blk * block_bytes +
                                    (uint64_t)(key0 - lb * BS) * row_bytes
                              : 0ull;

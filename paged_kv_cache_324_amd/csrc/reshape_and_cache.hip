@@ -26,6 +26,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(ReshapeArgs a) {
     const int64_t t = tbase + lt;
     if (t >= a.num_tokens) break;
     const int64_t slot = a.slot_mapping[t];
+    report_index_error(a.index_errors, slot >= a.num_slots, kErrSlot, slot);
     if (slot < 0 || slot >= a.num_slots) continue;  // padding token / outside the pool
     const bool is_v = rem >= a.row_chunks;
     const int chunk = is_v ? rem - a.row_chunks : rem;
@@ -36,6 +37,8 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(ReshapeArgs a) {
     __builtin_nontemporal_store(__builtin_nontemporal_load(src), dst);
   }
 }
+
+PA_LAYOUT_PROBE(reshape_and_cache)
 
 hipError_t launch_reshape_and_cache(const ReshapeArgs& a, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;

@@ -32,6 +32,7 @@ __global__ __launch_bounds__(256) void reshape_int8_kernel(ReshapeInt8Args a) {
     const int64_t t = th / a.num_kv_heads;
     const int head = (int)(th - t * a.num_kv_heads);
     const int64_t slot = a.slot_mapping[t];
+    report_index_error(a.index_errors, slot >= a.num_slots, kErrSlot, slot);
     if (slot < 0 || slot >= a.num_slots) continue;  // padding token / outside the pool
     const u32x4 x = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(is_v ? a.value : a.key) +
                                                    th * D)[sub];
@@ -62,6 +63,8 @@ __global__ __launch_bounds__(256) void reshape_int8_kernel(ReshapeInt8Args a) {
     }
   }
 }
+
+PA_LAYOUT_PROBE(reshape_int8)
 
 hipError_t launch_reshape_int8(const ReshapeInt8Args& a, int dtype, int head_dim, hipStream_t s) {
   const int64_t rows = a.num_tokens * a.num_kv_heads * 2;

@@ -39,6 +39,7 @@ __global__ __launch_bounds__(1024) void rope_reshape_kernel(RopeReshapeArgs a) {
   const int hq = a.q ? a.num_heads : 0;
   const int items = (hq + 2 * a.num_kv_heads) * P;
   const int64_t slot_raw = a.slot_mapping[t];
+  if (threadIdx.x == 0) report_index_error(a.index_errors, slot_raw >= a.num_slots, kErrSlot, slot_raw);
   const bool cache_ok = slot_raw >= 0 && slot_raw < a.num_slots;  // else padding / outside the pool
   const int64_t slot = cache_ok ? slot_raw : 0;
   const float* cos_row = a.cos + pos * H2;
@@ -82,6 +83,8 @@ __global__ __launch_bounds__(1024) void rope_reshape_kernel(RopeReshapeArgs a) {
     }
   }
 }
+
+PA_LAYOUT_PROBE(rope_reshape)
 
 hipError_t launch_rope_reshape(const RopeReshapeArgs& a, int dtype, int head_dim, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;

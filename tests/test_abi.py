@@ -332,3 +332,20 @@ def test_decode_step_scratch_rejects_a_split_beyond_the_scratch(lib):
     assert lib.pa_decode_step_scratch(*a) == -1
     a[18], a[0] = 0.088, None
     assert lib.pa_decode_step_scratch(*a) == -1
+
+
+def test_checking_library_exports_the_same_entry_points():
+    chk = pa.load_library(checked=True)
+    for name in declared_functions():
+        assert hasattr(chk, name), name
+    assert chk.pa_check_indices_enabled() == 1
+    assert pa.load_library().pa_check_indices_enabled() == 0
+
+
+def test_index_errors_need_the_checking_library(lib):
+    import ctypes
+    k, f, v = ctypes.c_uint32(7), ctypes.c_uint32(7), ctypes.c_int64(7)
+    assert lib.pa_take_index_errors(None, ctypes.byref(k), ctypes.byref(f), ctypes.byref(v)) == -2
+    assert "PA_CHECK_INDICES" in lib.pa_last_error().decode()
+    assert (k.value, f.value, v.value) == (0, 0, 0)
+    assert lib.pa_take_index_errors(None, None, None, None) == -1
