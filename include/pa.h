@@ -419,7 +419,7 @@ int pa_reshape_and_cache_int8(const void* key, const void* value, void* k_codes,
  * pa_decode_int8: pa_decode over an INT8 cache: out[i][h] = softmax(scale *
  * q[i][h] . K'_j) . V'_j with K'_j, V'_j the dequantised rows; q and out are
  * 16-bit (dtype).  Arguments, partitions, workspace (pa_decode_workspace_size)
- * and seq_order as for pa_decode.  Supported: head_dim 128; num_heads /
+ * and seq_order as for pa_decode.  Supported: head_dim 64 or 128; num_heads /
  * num_kv_heads in {1, 2, 4, 8}; block_size in {16, 32, 256}.
  */
 int pa_decode_int8(void* out, const void* q, const void* k_codes, const void* v_codes,
@@ -482,7 +482,7 @@ int pa_decode_order(const int32_t* context_lens, int num_seqs, int32_t* order);
  *
  * QK^T and PV run as 32x32x16 matrix-core (MFMA) tiles with fp32 accumulation;
  * the softmax is fp32 and the probabilities are rounded to the input dtype
- * before the PV product.  Supported: head_dim 128; block_size 16, 32, 256;
+ * before the PV product.  Supported: head_dim 64 or 128; block_size 16, 32, 256;
  * num_heads / num_kv_heads in {1, 2, 4, 8}; dtype PA_F16 or PA_BF16; scale finite and
  * > 0 (PA_ERR_INVALID_ARG otherwise).
  */

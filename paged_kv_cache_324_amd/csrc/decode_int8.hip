@@ -1,4 +1,4 @@
-// Paged-attention decode over an INT8 KV cache (head_dim 128).
+// Paged-attention decode over an INT8 KV cache (head_dim 64 and 128).
 //
 // Same computation as the 16-bit decode kernels, over the dequantised cache:
 // out[i][h] = softmax(scale q K'^T) V' with K'[j] = code_K[j] * sK[j] and
@@ -9,17 +9,17 @@
 // Caches, head-major within a block: codes int8 [num_blocks][num_kv_heads]
 // [block_size][128], scales float32 [num_blocks][num_kv_heads][block_size]
 // (pa_reshape_and_cache_int8): a 16-key group of one head is one contiguous
-// 2 KB run (the token-major 16-bit layout would leave 16 runs of 128 bytes).
+// 16 D-byte run (the token-major 16-bit layout would leave 16 runs of D bytes).
 //
 // The structure is that of decode_mfma_kernel (decode_mfma_impl.h): one
 // workgroup of 2, 4 or 8 wavefronts per (sequence, KV head, partition), 32-key steps
 // taken round-robin, scores S^T = K Q^T on 16x16x32 MFMA and O^T += V^T P^T on
 // 16x16x16 MFMA from a transposed LDS tile, a merge of the wavefronts through
 // LDS.  What differs:
-//   * a key row is 128 bytes: lane (key col, quad) loads the 32 contiguous
-//     bytes of dims 32 quad .. 32 quad + 31 and MFMA step ks takes dims
-//     32 quad + 8 ks .. + 7; the query fragments follow the same dim order (a
-//     dot product does not depend on the order of its terms);
+//   * a key row is D bytes: lane (key col, quad) loads the D / 4 contiguous
+//     bytes of dims (D / 4) quad .. + D / 4 - 1 and MFMA step ks (of D / 32)
+//     takes dims (D / 4) quad + 8 ks .. + 7; the query fragments follow the
+//     same dim order (a dot product does not depend on the order of its terms);
 //   * key codes are exact in fp16 and bf16 (|code| <= 127), so each is
 //     converted in registers to the query's 16-bit type and the key scale
 //     multiplies the fp32 score;
@@ -38,12 +38,24 @@
 
 namespace pa {
 
-constexpr int kI8Row = 256;                   // bytes of one converted (16-bit) V row in LDS
 constexpr int kI8StepKeys = 32;
-constexpr int kI8Step = kI8StepKeys * kI8Row;
 constexpr float kI8LazyRescale = 8.0f;
 
-__device__ __forceinline__ int i8_vswz(int r) { return (2 * r) & 15; }
+// Swizzle of the 16-byte chunks of a converted V row in LDS (2 D bytes, D / 8
+// chunks): chunk c of row r is stored at c ^ i8_vswz<D>(r), so that the
+// transposed reads (4 consecutive rows x 2 adjacent chunks per 16 lanes) touch
+// 16 distinct bank groups: with 256-byte rows each row spans the 64 banks and
+// (2 r) & 15 gives 4 consecutive rows disjoint chunk pairs; with 128-byte rows
+// two rows span the banks and ((r >> 1) ^ (r & 2)) & 7 gives rows r0 and r0 + 2
+// (r0 % 4 = 0) disjoint pairs.
+template <int D>
+__device__ __forceinline__ int i8_vswz(int r) {
+  if constexpr (D == 128) {
+    return (2 * r) & 15;
+  } else {
+    return ((r >> 1) ^ (r & 2)) & 7;
+  }
+}
 
 // Codes b[2k], b[2k+1] of a dword (signed bytes) as a packed 16-bit pair, exactly.
 template <int DT>
@@ -74,13 +86,22 @@ __device__ __forceinline__ u32x2 i8x4_dequant(uint32_t w, float s, float nb) {
   return u32x2{pack2<DT>(f0, f1), pack2<DT>(f2, f3)};
 }
 
-template <int DT, int BS, int G, int NW>
+template <int DT, int D, int BS, int G, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_int8_kernel(const DecodeArgs a) {
-  constexpr int D = 128;
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   static_assert(G >= 1 && G <= 16, "heads of a group fill the 16 MFMA columns");
   static_assert(BS % 16 == 0, "a 16-key group lies in one block");
-  __shared__ __attribute__((aligned(16))) unsigned char s_v[NW][kI8Step];  // 8 KB per wavefront
+  constexpr int ROW = 2 * D;           // bytes of a converted (16-bit) V row in LDS
+  constexpr int KS = D / 32;           // 16x16x32 score steps per key
+  constexpr int KC = D / 64;           // 16-byte code chunks a lane loads per key
+  constexpr int LPRV = D / 16;         // lanes per V code row (16 codes each)
+  constexpr int RPLV = 64 / LPRV;      // V rows per load instruction
+  constexpr int NJ = 16 / RPLV;        // V loads per 16-key group
+  constexpr int LPRN = D / 8;          // lanes per 16-bit row of the new token
+  // One V buffer of 32 rows per wavefront; at the end the same bytes hold that
+  // wavefront's fp32 O^T (16 heads x D dims) for the merge.
+  __shared__ __attribute__((aligned(16))) unsigned char s_v[NW][kI8StepKeys * ROW];
   __shared__ float s_ml[NW * 16 * 2];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -107,13 +128,13 @@ void decode_int8_kernel(const DecodeArgs a) {
   int32_t ids_next = load_ids(wave + 2 * NW);
 
   // Q^T fragment for step ks: head col (columns past G repeat head h0), dims
-  // 32 quad + 8 ks .. + 7, the order the key codes are loaded in.
-  u32x4 qf[4];
+  // (D / 4) quad + 8 ks .. + 7, the order the key codes are loaded in.
+  u32x4 qf[KS];
   {
     const u32x4* qp = reinterpret_cast<const u32x4*>(
         static_cast<const uint16_t*>(a.q) + ((int64_t)seq * a.num_heads + h0 + (col < G ? col : 0)) * D);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = qp[4 * quad + ks];
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = qp[KS * quad + ks];
   }
 
   const int L = clamp_context(a, seq);
@@ -154,8 +175,8 @@ void decode_int8_kernel(const DecodeArgs a) {
   // keys 4 quad .. + 3 of each group (the keys whose scores this lane holds);
   // vrs: the value scale of the V row this lane stages (see store_v).
   struct Regs {
-    u32x4 kr[2][2], vr[2][2], ksc[2];
-    float vrs[2][2];
+    u32x4 kr[2][KC], vr[2][NJ], ksc[2];
+    float vrs[2][NJ];
   };
   Regs ra, rb;
 
@@ -180,36 +201,39 @@ void decode_int8_kernel(const DecodeArgs a) {
       const __amdgpu_buffer_rsrc_t rks = make_rsrc(ksbase + soff, snrec);
       const __amdgpu_buffer_rsrc_t rvs = make_rsrc(vsbase + soff, snrec);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        r.kr[gr][j] = buffer_load16<kCachePolicyNT>(rk, (uint32_t)col * row_bytes + (uint32_t)(32 * quad + 16 * j));
+      for (int j = 0; j < KC; ++j)
+        r.kr[gr][j] = buffer_load16<kCachePolicyNT>(
+            rk, (uint32_t)col * row_bytes + (uint32_t)((D / 4) * quad + 16 * j));
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NJ; ++j)
         r.vr[gr][j] = buffer_load16<kCachePolicyNT>(
-            rv, (uint32_t)(8 * j + (lane >> 3)) * row_bytes + (uint32_t)((lane & 7) * 16));
+            rv, (uint32_t)(RPLV * j + lane / LPRV) * row_bytes + (uint32_t)((lane % LPRV) * 16));
       r.ksc[gr] = buffer_load16<kCachePolicyNT>(rks, (uint32_t)(16 * quad));
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        r.vrs[gr][j] = buffer_load4f<kCachePolicyNT>(rvs, (uint32_t)(4 * (8 * j + (lane >> 3))));
+      for (int j = 0; j < NJ; ++j)
+        r.vrs[gr][j] =
+            buffer_load4f<kCachePolicyNT>(rvs, (uint32_t)(4 * (RPLV * j + lane / LPRV)));
     }
   };
 
   // V codes -> dequantised 16-bit rows of this wavefront's LDS tile (row 16 gr +
-  // 8 j + lane / 8 of the step, dims 16 (lane % 8) .. + 15 = chunks 2 (lane % 8),
-  // +1), each code times its row's scale.
+  // RPLV j + lane / LPRV of the step, dims 16 (lane % LPRV) .. + 15 = chunks
+  // 2 (lane % LPRV), +1), each code times its row's scale.
   auto store_v = [&](const Regs& r) {
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = 16 * gr + 8 * j + (lane >> 3);
-        const int c = 2 * (lane & 7);
-        unsigned char* rowp = sv + row * kI8Row;
+      for (int j = 0; j < NJ; ++j) {
+        const int row = 16 * gr + RPLV * j + lane / LPRV;
+        const int c = 2 * (lane % LPRV);
+        unsigned char* rowp = sv + row * ROW;
         const u32x4 w = r.vr[gr][j];
         const float vs = r.vrs[gr][j], nb = -128.f * vs;
         const u32x2 d0 = i8x4_dequant<DT>(w.x, vs, nb), d1 = i8x4_dequant<DT>(w.y, vs, nb);
         const u32x2 d2 = i8x4_dequant<DT>(w.z, vs, nb), d3 = i8x4_dequant<DT>(w.w, vs, nb);
-        *reinterpret_cast<u32x4*>(rowp + ((c ^ i8_vswz(row)) * 16)) = u32x4{d0.x, d0.y, d1.x, d1.y};
-        *reinterpret_cast<u32x4*>(rowp + (((c + 1) ^ i8_vswz(row)) * 16)) =
+        *reinterpret_cast<u32x4*>(rowp + ((c ^ i8_vswz<D>(row)) * 16)) =
+            u32x4{d0.x, d0.y, d1.x, d1.y};
+        *reinterpret_cast<u32x4*>(rowp + (((c + 1) ^ i8_vswz<D>(row)) * 16)) =
             u32x4{d2.x, d2.y, d3.x, d3.y};
       }
   };
@@ -219,7 +243,7 @@ void decode_int8_kernel(const DecodeArgs a) {
     for (int gr = 0; gr < 2; ++gr) {
       sc[gr] = f32x4{};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
         const u32x4 w = r.kr[gr][ks >> 1];
         const u32x4 kf = (ks & 1) ? i8_to_16<DT>(w.z, w.w) : i8_to_16<DT>(w.x, w.y);
         sc[gr] = mfma16x16x32<DT>(kf, qf[ks], sc[gr]);
@@ -258,11 +282,11 @@ void decode_int8_kernel(const DecodeArgs a) {
       const u32x2 pf = {pack2<DT>(sc[gr][0], sc[gr][1]), pack2<DT>(sc[gr][2], sc[gr][3])};
       lacc = mfma16x16x16<DT>(ones, pf, lacc);
       const int rr = 16 * gr + 4 * quad + (col >> 2);
-      const unsigned char* rowp = sv + rr * kI8Row + 8 * (col & 1);
+      const unsigned char* rowp = sv + rr * ROW + 8 * (col & 1);
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
         const int chunk = 2 * dt + ((col & 3) >> 1);
-        const u32x2 vf = lds_read_tr16(rowp + ((chunk ^ i8_vswz(rr)) * 16));
+        const u32x2 vf = lds_read_tr16(rowp + ((chunk ^ i8_vswz<D>(rr)) * 16));
         o[dt] = mfma16x16x16<DT>(vf, pf, o[dt]);
       }
     }
@@ -273,13 +297,14 @@ void decode_int8_kernel(const DecodeArgs a) {
   // use them.  Look-ahead loads are unconditional (clamped ids, size-0
   // resources past the partition), so every step waits for the same loads.
   const int nsteps = (t1c - t0 + kI8StepKeys - 1) / kI8StepKeys;
-  // The new token's 16-bit rows (lanes 0..15 key, 16..31 value, 16 bytes each)
-  // are fetched before the cached steps, on the wavefront that attends to it.
+  // The new token's 16-bit rows (lanes 0 .. LPRN - 1 key, LPRN .. 2 LPRN - 1
+  // value, 16 bytes each) are fetched before the cached steps, on the
+  // wavefront that attends to it.
   u32x4 new_x = {0u, 0u, 0u, 0u};
-  if (new_here && wave == nsteps % NW && lane < 32) {
+  if (new_here && wave == nsteps % NW && lane < 2 * LPRN) {
     const int64_t nrow = ((int64_t)seq * a.num_kv_heads + kvh) * D;
     new_x = reinterpret_cast<const u32x4*>(
-        static_cast<const uint16_t*>(lane >= 16 ? a.value_new : a.key_new) + nrow)[lane & 15];
+        static_cast<const uint16_t*>(lane >= LPRN ? a.value_new : a.key_new) + nrow)[lane % LPRN];
   }
   auto step = [&](int s, Regs& r) {
     const int32_t ids_after = load_ids(s + 3 * NW);
@@ -306,13 +331,14 @@ void decode_int8_kernel(const DecodeArgs a) {
 
   if (new_here && wave == nsteps % NW) {
     // The new token (position L-1), on the wavefront with the fewest steps.
-    // Lanes 0..15 quantise its key row and lanes 16..31 its value row, 8
-    // dimensions each, exactly as pa_reshape_and_cache_int8 does (scale = amax
-    // / 127, code = rint(x / scale), IEEE float32); the codes and scales are
-    // stored at the token's slot for later steps and attended from registers
-    // as a one-key step (every other key of the step is zeros and masked).
-    const bool is_v = lane >= 16;
-    const int qsub = lane & 15;
+    // Lanes 0 .. LPRN - 1 quantise its key row and the next LPRN its value row,
+    // 8 dimensions each, exactly as pa_reshape_and_cache_int8 does (scale =
+    // amax / 127, code = rint(x / scale), IEEE float32); the codes and scales
+    // are stored at the token's slot for later steps and attended from
+    // registers as a one-key step (every other key of the step is zeros and
+    // masked).
+    const bool is_v = lane >= LPRN;
+    const int qsub = lane % LPRN;
     const u32x4 x = new_x;
     const float f[8] = {lo_f32<DT>(x.x), hi_f32<DT>(x.x), lo_f32<DT>(x.y), hi_f32<DT>(x.y),
                         lo_f32<DT>(x.z), hi_f32<DT>(x.z), lo_f32<DT>(x.w), hi_f32<DT>(x.w)};
@@ -320,7 +346,7 @@ void decode_int8_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
 #pragma unroll
-    for (int o2 = 8; o2 >= 1; o2 >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o2));  // 16-lane row
+    for (int o2 = LPRN / 2; o2 >= 1; o2 >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o2));  // one row
     const float qscale = amax / 127.0f;
     uint32_t pk[2] = {0u, 0u};
     if (qscale > 0.f) {
@@ -332,7 +358,7 @@ void decode_int8_kernel(const DecodeArgs a) {
     }
     const int64_t slot = a.slot_mapping[seq];
     if (lane == 0) report_index_error(a.index_errors, slot >= a.num_slots, kErrSlot, slot);
-    if (lane < 32 && slot >= 0 && slot < a.num_slots) {
+    if (lane < 2 * LPRN && slot >= 0 && slot < a.num_slots) {
       const int64_t sblk = slot / BS;
       const int64_t srow = (sblk * a.num_kv_heads + kvh) * BS + (slot - sblk * BS);
       int8_t* codes = static_cast<int8_t*>(is_v ? a.v_cache_w : a.k_cache_w);
@@ -340,33 +366,34 @@ void decode_int8_kernel(const DecodeArgs a) {
       if (qsub == 0) (is_v ? a.v_scales_w : a.k_scales_w)[srow] = qscale;
     }
     // Registers of the one-key step, laid out as issue() loads a cached step:
-    // key 0 of group 0 is the new token.  Its key codes, dims 32 quad .. + 31,
-    // go to the lanes with col 0 (from quantising lanes 4 quad .. 4 quad + 3);
-    // its value codes, dims 16 (lane & 7) .. + 15, and its value scale to lanes
-    // 0..7 (from lanes 16 + 2 (lane & 7) and the next); its key scale to the
-    // quad-0 lanes.
+    // key 0 of group 0 is the new token.  Its key codes, dims (D / 4) quad ..
+    // + D / 4 - 1, go to the lanes with col 0 (from quantising lanes KS quad ..
+    // KS quad + KS - 1, 8 codes each); its value codes, dims 16 (lane % LPRV)
+    // .. + 15, and its value scale to lanes 0 .. LPRV - 1 (from lanes LPRN +
+    // 2 (lane % LPRV) and the next); its key scale to the quad-0 lanes.
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
     Regs rn;
-    uint32_t kw[8], vw[4];
+    uint32_t kw[4 * KC], vw[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) kw[k] = (uint32_t)__shfl((int)pk[k & 1], 4 * quad + (k >> 1));
+    for (int k = 0; k < 4 * KC; ++k) kw[k] = (uint32_t)__shfl((int)pk[k & 1], KS * quad + (k >> 1));
 #pragma unroll
-    for (int k = 0; k < 4; ++k) vw[k] = (uint32_t)__shfl((int)pk[k & 1], 16 + 2 * (lane & 7) + (k >> 1));
-    const float ksn = __shfl(qscale, 0), vsn = __shfl(qscale, 16);
-    rn.kr[0][0] = col == 0 ? u32x4{kw[0], kw[1], kw[2], kw[3]} : zero4;
-    rn.kr[0][1] = col == 0 ? u32x4{kw[4], kw[5], kw[6], kw[7]} : zero4;
-    rn.kr[1][0] = zero4;
-    rn.kr[1][1] = zero4;
-    rn.vr[0][0] = lane < 8 ? u32x4{vw[0], vw[1], vw[2], vw[3]} : zero4;
-    rn.vr[0][1] = zero4;
-    rn.vr[1][0] = zero4;
-    rn.vr[1][1] = zero4;
+    for (int k = 0; k < 4; ++k)
+      vw[k] = (uint32_t)__shfl((int)pk[k & 1], LPRN + 2 * (lane % LPRV) + (k >> 1));
+    const float ksn = __shfl(qscale, 0), vsn = __shfl(qscale, LPRN);
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      rn.kr[0][j] = col == 0 ? u32x4{kw[4 * j], kw[4 * j + 1], kw[4 * j + 2], kw[4 * j + 3]} : zero4;
+      rn.kr[1][j] = zero4;
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      rn.vr[0][j] = (j == 0 && lane < LPRV) ? u32x4{vw[0], vw[1], vw[2], vw[3]} : zero4;
+      rn.vr[1][j] = zero4;
+      rn.vrs[0][j] = (j == 0 && lane < LPRV) ? vsn : 0.f;
+      rn.vrs[1][j] = 0.f;
+    }
     rn.ksc[0] = quad == 0 ? u32x4{__float_as_uint(ksn), 0u, 0u, 0u} : zero4;
     rn.ksc[1] = zero4;
-    rn.vrs[0][0] = lane < 8 ? vsn : 0.f;
-    rn.vrs[0][1] = 0.f;
-    rn.vrs[1][0] = 0.f;
-    rn.vrs[1][1] = 0.f;
     store_v(rn);
     f32x4 sc[2], kscale[2];
     scores(rn, sc, kscale);
@@ -421,11 +448,11 @@ void decode_int8_kernel(const DecodeArgs a) {
 
 PA_LAYOUT_PROBE(decode_int8)
 
-template <int DT, int BS, int G>
+template <int DT, int D, int BS, int G>
 hipError_t launch_int8_t(const DecodeArgs& a, int phases, hipStream_t s) {
   const unsigned grid = (unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.num_parts);
   if (phases & kPhaseMerge && !(phases & kPhasePartitions)) {
-    launch_merge<DT, 128>(a, s);
+    launch_merge<DT, D>(a, s);
     return hipGetLastError();
   }
   // Wavefronts per workgroup: eight for spans of kMfmaLongSpan+ tokens (as for the
@@ -434,42 +461,47 @@ hipError_t launch_int8_t(const DecodeArgs& a, int phases, hipStream_t s) {
   // short partition (long split-K INT8 decode at 512: 100.3 -> 96.4 us; unsplit
   // contexts of up to 2048 tokens lose with two: 62.1 -> 67.5 us); four otherwise.
   if (a.part_tokens >= kMfmaLongSpan) {
-    hipLaunchKernelGGL((decode_int8_kernel<DT, BS, G, 8>), dim3(grid), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((decode_int8_kernel<DT, D, BS, G, 8>), dim3(grid), dim3(512), 0, s, a);
   } else if (a.num_parts > 1 && a.part_tokens <= kMfmaShortPartition) {
-    hipLaunchKernelGGL((decode_int8_kernel<DT, BS, G, 2>), dim3(grid), dim3(128), 0, s, a);
+    hipLaunchKernelGGL((decode_int8_kernel<DT, D, BS, G, 2>), dim3(grid), dim3(128), 0, s, a);
   } else {
-    hipLaunchKernelGGL((decode_int8_kernel<DT, BS, G, 4>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_int8_kernel<DT, D, BS, G, 4>), dim3(grid), dim3(256), 0, s, a);
   }
-  if (phases & kPhaseMerge) launch_merge<DT, 128>(a, s);
+  if (phases & kPhaseMerge) launch_merge<DT, D>(a, s);
   return hipGetLastError();
 }
 
-template <int DT, int BS>
+template <int DT, int D, int BS>
 hipError_t launch_int8_g(const DecodeArgs& a, int group, int phases, hipStream_t s) {
   switch (group) {
-    case 1: return launch_int8_t<DT, BS, 1>(a, phases, s);
-    case 2: return launch_int8_t<DT, BS, 2>(a, phases, s);
-    case 4: return launch_int8_t<DT, BS, 4>(a, phases, s);
-    case 8: return launch_int8_t<DT, BS, 8>(a, phases, s);
+    case 1: return launch_int8_t<DT, D, BS, 1>(a, phases, s);
+    case 2: return launch_int8_t<DT, D, BS, 2>(a, phases, s);
+    case 4: return launch_int8_t<DT, D, BS, 4>(a, phases, s);
+    case 8: return launch_int8_t<DT, D, BS, 8>(a, phases, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int DT>
-hipError_t launch_int8_dt(const DecodeArgs& a, int block_size, int group, int phases,
+template <int DT, int D>
+hipError_t launch_int8_bs(const DecodeArgs& a, int block_size, int group, int phases,
                           hipStream_t s) {
   switch (block_size) {
-    case 16: return launch_int8_g<DT, 16>(a, group, phases, s);
-    case 32: return launch_int8_g<DT, 32>(a, group, phases, s);
-    case 256: return launch_int8_g<DT, 256>(a, group, phases, s);
+    case 16: return launch_int8_g<DT, D, 16>(a, group, phases, s);
+    case 32: return launch_int8_g<DT, D, 32>(a, group, phases, s);
+    case 256: return launch_int8_g<DT, D, 256>(a, group, phases, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_decode_int8(const DecodeArgs& a, int dtype, int block_size, int group,
-                              int phases, hipStream_t s) {
-  return dtype == DT_BF16 ? launch_int8_dt<DT_BF16>(a, block_size, group, phases, s)
-                          : launch_int8_dt<DT_F16>(a, block_size, group, phases, s);
+hipError_t launch_decode_int8(const DecodeArgs& a, int dtype, int head_dim, int block_size,
+                              int group, int phases, hipStream_t s) {
+  if (head_dim == 128)
+    return dtype == DT_BF16 ? launch_int8_bs<DT_BF16, 128>(a, block_size, group, phases, s)
+                            : launch_int8_bs<DT_F16, 128>(a, block_size, group, phases, s);
+  if (head_dim == 64)
+    return dtype == DT_BF16 ? launch_int8_bs<DT_BF16, 64>(a, block_size, group, phases, s)
+                            : launch_int8_bs<DT_F16, 64>(a, block_size, group, phases, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

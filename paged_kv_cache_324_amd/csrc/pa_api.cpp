@@ -501,7 +501,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (const int e = index_errors_address(s, &a.index_errors)) return e;
   // PA_F16 / PA_BF16 are the kernels' dtype codes.
-  hipError_t e = i8 ? pa::launch_decode_int8(a, dtype, block_size, group, phases, s)
+  hipError_t e = i8 ? pa::launch_decode_int8(a, dtype, head_dim, block_size, group, phases, s)
                  : dtype == PA_BF16 ? pa::launch_decode_bf16(a, head_dim, block_size, group, phases, s)
                                     : pa::launch_decode_f16(a, head_dim, block_size, group, phases, s);
   return hip_status(e, "decode launch");
@@ -763,7 +763,6 @@ int pa_decode_int8(void* out, const void* q, const void* k_codes, const void* v_
                    int num_heads, int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
                    int max_blocks_per_seq, int max_context_len, float scale, int partition_size,
                    void* workspace, size_t workspace_bytes, int dtype, void* stream) {
-  if (head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "INT8 decode supports head_dim 128 only");
   const Int8Scales i8{k_scales, v_scales};
   return decode_impl(out, q, k_codes, v_codes, block_tables, context_lens, seq_order, nullptr, &i8, nullptr,
                      num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
@@ -778,7 +777,6 @@ int pa_decode_step_int8(void* out, const void* q, const void* key, const void* v
                         int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
                         int max_context_len, float scale, int partition_size, void* workspace,
                         size_t workspace_bytes, int dtype, void* stream) {
-  if (head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "INT8 decode supports head_dim 128 only");
   NewTokens nt{key, value, slot_mapping, k_codes, v_codes};
   nt.k_scales = k_scales;
   nt.v_scales = v_scales;
@@ -814,7 +812,6 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
   int st = check_cache(num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                        max_blocks_per_seq, dtype);
   if (st != PA_OK) return st;
-  if (head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "prefill supports head_dim 128 only");
   if (max_query_len < 0) return fail(PA_ERR_INVALID_ARG, "max_query_len must be >= 0");
   if (!valid_scale(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return ok();

@@ -164,8 +164,8 @@ enum : int { kPhasePartitions = 1, kPhaseMerge = 2, kPhaseAll = 3 };
 
 // INT8 decode: DecodeArgs with k_cache / v_cache pointing at the int8 codes and
 // the per-row scales in k_scales / v_scales.
-hipError_t launch_decode_int8(const DecodeArgs& a, int dtype, int block_size, int group,
-                              int phases, hipStream_t s);
+hipError_t launch_decode_int8(const DecodeArgs& a, int dtype, int head_dim, int block_size,
+                              int group, int phases, hipStream_t s);
 
 // dtype DT_F16 / DT_BF16; head_dim 64/128; block_size 16/32/256; group 1/2/4/8.
 hipError_t launch_decode_f16(const DecodeArgs& a, int head_dim, int block_size, int group,

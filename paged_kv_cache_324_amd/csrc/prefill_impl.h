@@ -15,7 +15,8 @@
 // serves 4 x 32 query rows.
 //
 // Both products are computed transposed so that a lane always owns one query
-// row (lane l -> row l % 32 of its wavefront):
+// row (lane l -> row l % 32 of its wavefront); with head_dim D (64 or 128) a
+// 16-key step takes D / 16 score MFMAs per 32 keys and D / 32 value tiles:
 //   S^T = K Q^T  (32x32x16 MFMA: A = 32 keys x 16 dims from LDS, B = Q^T held
 //                 in registers for the whole kernel),
 //   O^T = V^T P^T (A = 32 dims x 16 keys of V^T from LDS, B = P^T straight
@@ -42,10 +43,7 @@
 
 namespace pa {
 
-constexpr int kPrefillD = 128;
 constexpr int kPrefillKeys = 64;        // keys per KV tile
-constexpr int kPrefillRow = kPrefillD * 2;  // bytes per key row in LDS (16 chunks of 16 B)
-constexpr int kPrefillTile = kPrefillKeys * kPrefillRow;
 constexpr float kPrefillEmptyMax = -1.0e30f;
 constexpr float kLazyRescale = 8.0f;
 constexpr int kXcds = 8;  // workgroups are dispatched round-robin over the 8 XCDs of an MI355X
@@ -83,27 +81,44 @@ __device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t lds_base, uint32_
 }
 
 // Swizzle of the 16-byte chunks of a tile row: chunk c of row r is stored at
-// position c ^ swz(r), with swz(r) the two 2-bit fields of r & 15 swapped.
-// Both read patterns then hit 16 distinct 16-byte bank groups: 16 consecutive
-// rows at one chunk (the K operand), and 4 consecutive rows (4 r0 .. 4 r0 + 3)
-// at 4 adjacent chunks (4 a .. 4 a + 3, the transposed V operand), since
-// (4 a + i) ^ ((j << 2) | k) = 4 (a ^ j) + (i ^ k).
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-
-__device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
-  return (uint32_t)row * kPrefillRow + (uint32_t)((chunk ^ swz(row)) * 16);
+// position c ^ swz<D>(r).
+// * D = 128 (256-byte rows, 16 chunks): swz(r) is the two 2-bit fields of r & 15
+//   swapped.  Both read patterns then hit 16 distinct 16-byte bank groups: 16
+//   consecutive rows at one chunk (the K operand), and 4 consecutive rows
+//   (4 r0 .. 4 r0 + 3) at 4 adjacent chunks (4 a .. 4 a + 3, the transposed V
+//   operand), since (4 a + i) ^ ((j << 2) | k) = 4 (a ^ j) + (i ^ k).
+// * D = 64 (128-byte rows, 8 chunks; two rows span the 64 banks): swz(r) =
+//   ((r >> 1) ^ (r & 2)) & 7 runs through all 8 positions over the even rows
+//   of 16 consecutive ones and over the odd rows (the K operand), and gives rows
+//   r0 and r0 + 2 (r0 % 4 = 0) disjoint pairs of adjacent positions (the
+//   transposed V operand reads 4 rows x 2 adjacent chunks per 16 lanes).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  } else {
+    return ((row >> 1) ^ (row & 2)) & 7;
+  }
 }
 
-template <int DT, int BS, int G>
+template <int D>
+__device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
+  return (uint32_t)row * (2 * D) + (uint32_t)((chunk ^ swz<D>(row)) * 16);
+}
+
+template <int DT, int D, int BS, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(const PrefillArgs a) {
-  constexpr int D = kPrefillD;
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   constexpr int NK = kPrefillKeys;
   constexpr int QT = 128 / G;
+  constexpr int ROW = 2 * D;           // bytes of a key row in LDS
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int RPL = 64 / CPR;        // rows a 1 KB load of 64 lanes covers
   static_assert(BS % 16 == 0, "a wavefront stages 16 keys of one block");
-  // [buffer][K or V][64 key rows x 256 B]: double-buffered tiles filled straight
+  // [buffer][K or V][64 key rows x 2D bytes]: double-buffered tiles filled straight
   // from the cache by buffer loads into LDS.
-  __shared__ __attribute__((aligned(16))) unsigned char s_kv[2][2][kPrefillTile];
+  __shared__ __attribute__((aligned(16))) unsigned char s_kv[2][2][NK * ROW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -179,8 +194,8 @@ void prefill_kernel(const PrefillArgs a) {
   const u32x4 ones = {one2, one2, one2, one2};
 
   // ---- staging: wavefront w moves keys kv0 + 16 w .. + 15 (one block) of K
-  // and of V with four 1 KB buffer loads each; lane l of load i brings key row
-  // 4 i + l / 16, chunk (l % 16) ^ swz(row), so the tile lands already swizzled.
+  // and of V with 16 / RPL 1 KB buffer loads each; lane l of load i brings key row
+  // RPL i + l / CPR, chunk (l % CPR) ^ swz(row), so the tile lands already swizzled.
   const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks;
   const int32_t nb32 = a.num_blocks > INT32_MAX ? INT32_MAX : (int32_t)a.num_blocks;
   const uint32_t row_bytes = (uint32_t)a.num_kv_heads * D * 2;
@@ -188,7 +203,7 @@ void prefill_kernel(const PrefillArgs a) {
   const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)kvh * D * 2;
   const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)kvh * D * 2;
   const int nblk_last = max(0, (L + BS - 1) / BS - 1);
-  const int srow = lane >> 4;  // row within a 1 KB load (4 rows of 256 B)
+  const int srow = lane / CPR;  // row within a 1 KB load
   // Block ids, lane-parallel: for window w, lane j holds the id of the block
   // this wavefront stages in tile 64 w + j (reads clamped to the context).
   auto load_ids = [&](int w) -> int32_t {
@@ -209,11 +224,11 @@ void prefill_kernel(const PrefillArgs a) {
     const u32x4 rk = rsrc_words(kbase + boff, nrec);
     const u32x4 rv = rsrc_words(vbase + boff, nrec);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * i + srow;  // 0..15, also the tile row modulo 16
-      const uint32_t voff = (uint32_t)r * row_bytes + (uint32_t)(((lane & 15) ^ swz(r)) * 16);
-      lds_dma16(rk, lds_offset(s_kv[buf][0] + (16 * wave + 4 * i) * kPrefillRow), voff);
-      lds_dma16(rv, lds_offset(s_kv[buf][1] + (16 * wave + 4 * i) * kPrefillRow), voff);
+    for (int i = 0; i < 16 / RPL; ++i) {
+      const int r = RPL * i + srow;  // 0..15, also the tile row modulo 16
+      const uint32_t voff = (uint32_t)r * row_bytes + (uint32_t)(((lane % CPR) ^ swz<D>(r)) * 16);
+      lds_dma16(rk, lds_offset(s_kv[buf][0] + (16 * wave + RPL * i) * ROW), voff);
+      lds_dma16(rv, lds_offset(s_kv[buf][1] + (16 * wave + RPL * i) * ROW), voff);
     }
   };
 
@@ -248,7 +263,7 @@ void prefill_kernel(const PrefillArgs a) {
       const int kr = sub * 32 + (lane & 31);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(sk + tile_off(kr, 2 * ks + half));
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(sk + tile_off<D>(kr, 2 * ks + half));
         s[sub] = mfma32x32x16<DT>(kf, qf[ks], s[sub]);
       }
     }
@@ -304,8 +319,8 @@ void prefill_kernel(const PrefillArgs a) {
       for (int dt = 0; dt < D / 32; ++dt) {
         const int chunk = 4 * dt + 2 * dh + ((p16 & 3) >> 1);
         const int sub8 = 8 * (p16 & 1);
-        const u32x2 lo = lds_read_tr16(sv + tile_off(r1, chunk) + sub8);
-        const u32x2 hi = lds_read_tr16(sv + tile_off(r2, chunk) + sub8);
+        const u32x2 lo = lds_read_tr16(sv + tile_off<D>(r1, chunk) + sub8);
+        const u32x2 hi = lds_read_tr16(sv + tile_off<D>(r2, chunk) + sub8);
         o[dt] = mfma32x32x16<DT>(u32x4{lo.x, lo.y, hi.x, hi.y}, pf, o[dt]);
       }
     }
@@ -355,7 +370,7 @@ void prefill_kernel(const PrefillArgs a) {
   }
 }
 
-template <int DT, int BS, int G>
+template <int DT, int D, int BS, int G>
 hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t s) {
   PrefillArgs a = a0;
   constexpr int QT = 128 / G;
@@ -364,27 +379,27 @@ hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t s) {
   const int64_t grid = (groups + kXcds - 1) / kXcds * kXcds * a.q_tiles;
   if (grid == 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<DT, BS, G>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((prefill_kernel<DT, D, BS, G>), dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <int DT, int BS>
+template <int DT, int D, int BS>
 hipError_t launch_prefill_g(const PrefillArgs& a, int group, hipStream_t s) {
   switch (group) {
-    case 1: return launch_prefill_t<DT, BS, 1>(a, s);
-    case 2: return launch_prefill_t<DT, BS, 2>(a, s);
-    case 4: return launch_prefill_t<DT, BS, 4>(a, s);
-    case 8: return launch_prefill_t<DT, BS, 8>(a, s);
+    case 1: return launch_prefill_t<DT, D, BS, 1>(a, s);
+    case 2: return launch_prefill_t<DT, D, BS, 2>(a, s);
+    case 4: return launch_prefill_t<DT, D, BS, 4>(a, s);
+    case 8: return launch_prefill_t<DT, D, BS, 8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int DT>
+template <int DT, int D>
 hipError_t launch_prefill_dt(const PrefillArgs& a, int block_size, int group, hipStream_t s) {
   switch (block_size) {
-    case 16: return launch_prefill_g<DT, 16>(a, group, s);
-    case 32: return launch_prefill_g<DT, 32>(a, group, s);
-    case 256: return launch_prefill_g<DT, 256>(a, group, s);
+    case 16: return launch_prefill_g<DT, D, 16>(a, group, s);
+    case 32: return launch_prefill_g<DT, D, 32>(a, group, s);
+    case 256: return launch_prefill_g<DT, D, 256>(a, group, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -139,7 +139,7 @@ def test_prefill_rejects_bad_arguments(lib):
     bad[16] = -1
     assert f(*bad) == -1
     bad = list(args)
-    bad[12] = 64    # head_dim 64 has no prefill kernel
+    bad[12] = 96    # head_dim 96 has no prefill kernel (64 and 128 do)
     assert f(*bad) == -2
 
 
@@ -178,7 +178,7 @@ def test_decode_step_int8_rejects_bad_arguments(lib):
     bad[4] = None                          # slot_mapping
     assert f(*bad) == -1 and "null" in lib.pa_last_error().decode()
     bad = list(base)
-    bad[15] = 64                           # head_dim: INT8 decode takes 128 only
+    bad[15] = 96                           # head_dim: INT8 decode takes 64 and 128
     assert f(*bad) == -2
     bad = list(base)
     bad[21] = 32                           # needs a workspace

@@ -140,27 +140,29 @@ def test_reshape_int8_special_rows_and_skipped_slots():
 
 
 # ------------------------------------------------------------------ decode over INT8
-SWEEP = [(dt, BS, G, p) for dt in ("bf16", "f16") for BS in (16, 32, 256) for G in (1, 2, 4, 8)
-         for p in (0, 256)]
+SWEEP = [(dt, D, BS, G, p) for dt in ("bf16", "f16") for D in (128, 64) for BS in (16, 32, 256)
+         for G in (1, 2, 4, 8) for p in (0, 256)]
 
 
-@pytest.mark.parametrize("dt,BS,G,partition", SWEEP)
-def test_decode_int8_shape_sweep(dt, BS, G, partition):
+@pytest.mark.parametrize("dt,D,BS,G,partition", SWEEP)
+def test_decode_int8_shape_sweep(dt, D, BS, G, partition):
     Hkv = 2
-    b = make_batch(B=4, Hq=Hkv * G, Hkv=Hkv, D=128, BS=BS, dtype=dt, scale=128 ** -0.5,
-                   seed=9100 + SWEEP.index((dt, BS, G, partition)), lens_range=(1, 700))
+    b = make_batch(B=4, Hq=Hkv * G, Hkv=Hkv, D=D, BS=BS, dtype=dt, scale=D ** -0.5,
+                   seed=9100 + SWEEP.index((dt, D, BS, G, partition)), lens_range=(1, 700))
     ib = Int8Batch(b)
-    check_close(to_f64(ib.decode(partition)), ib.oracle(), f"int8 {dt} BS{BS} G{G} p{partition}")
+    check_close(to_f64(ib.decode(partition)), ib.oracle(),
+                f"int8 {dt} D{D} BS{BS} G{G} p{partition}")
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("partition", [0, 256, 16])
-def test_decode_int8_length_edges(partition):
+def test_decode_int8_length_edges(partition, D):
     lens = [1, 15, 16, 17, 31, 32, 33, 255, 256, 257, 511, 0]
-    b = make_batch(B=len(lens), Hq=16, Hkv=4, D=128, BS=16, dtype="bf16", scale=128 ** -0.5,
-                   seed=9200 + partition, lens=lens)
+    b = make_batch(B=len(lens), Hq=16, Hkv=4, D=D, BS=16, dtype="bf16", scale=D ** -0.5,
+                   seed=9200 + partition + D, lens=lens)
     ib = Int8Batch(b)
     got = to_f64(ib.decode(partition))
-    check_close(got, ib.oracle(), f"int8 edges p{partition}")
+    check_close(got, ib.oracle(), f"int8 edges D{D} p{partition}")
     assert np.all(got[lens.index(0)] == 0)
 
 
@@ -214,31 +216,32 @@ def _step_int8(ib, partition):
     return out
 
 
-STEP = [(dt, BS, G, p) for dt in ("bf16", "f16") for BS in (16, 256) for G in (1, 2, 4, 8)
-        for p in (0, 256)]
+STEP = [(dt, D, BS, G, p) for dt in ("bf16", "f16") for D in (128, 64) for BS in (16, 256)
+        for G in (1, 2, 4, 8) for p in (0, 256)]
 
 
-@pytest.mark.parametrize("dt,BS,G,partition", STEP)
-def test_decode_step_int8_matches_oracle(dt, BS, G, partition):
+@pytest.mark.parametrize("dt,D,BS,G,partition", STEP)
+def test_decode_step_int8_matches_oracle(dt, D, BS, G, partition):
     Hkv = 2
-    b = make_batch(B=6, Hq=Hkv * G, Hkv=Hkv, D=128, BS=BS, dtype=dt, scale=128 ** -0.5,
-                   seed=9600 + STEP.index((dt, BS, G, partition)), lens_range=(1, 700))
+    b = make_batch(B=6, Hq=Hkv * G, Hkv=Hkv, D=D, BS=BS, dtype=dt, scale=D ** -0.5,
+                   seed=9600 + STEP.index((dt, D, BS, G, partition)), lens_range=(1, 700))
     ib = Int8Batch(b, write_new=False)
     got = to_f64(_step_int8(ib, partition))
     check_close(got, ib.oracle(), f"int8 step {dt} BS{BS} G{G} p{partition}")
     ib.check_caches()
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("partition", [0, 512, 32])
-def test_decode_step_int8_length_edges(partition):
+def test_decode_step_int8_length_edges(partition, D):
     """Lengths 1 (only the new token), block and partition edges, and 4096+ tokens (the
     eight-wavefront kernel when unsplit, two wavefronts at partitions up to 512)."""
     lens = [1, 2, 16, 17, 33, 512, 513, 4097, 5000]
-    b = make_batch(B=len(lens), Hq=8, Hkv=2, D=128, BS=16, dtype="bf16", scale=128 ** -0.5,
-                   seed=9650 + partition, lens=lens)
+    b = make_batch(B=len(lens), Hq=8, Hkv=2, D=D, BS=16, dtype="bf16", scale=D ** -0.5,
+                   seed=9650 + partition + D, lens=lens)
     ib = Int8Batch(b, write_new=False)
     got = to_f64(_step_int8(ib, partition))
-    check_close(got, ib.oracle(), f"int8 step edges p{partition}")
+    check_close(got, ib.oracle(), f"int8 step edges D{D} p{partition}")
     ib.check_caches()
 
 

@@ -42,16 +42,44 @@ def test_prefill_chunked_config_full_size():
     check_full(got, _oracle(b), "chunked_prefill", b.dtype)
 
 
-SWEEP = [(dt, BS, G) for dt in ("bf16", "f16") for BS in (16, 32, 256) for G in (1, 2, 4, 8)]
+SWEEP = [(dt, D, BS, G) for dt in ("bf16", "f16") for D in (128, 64) for BS in (16, 32, 256)
+         for G in (1, 2, 4, 8)]
 
 
-@pytest.mark.parametrize("dt,BS,G", SWEEP)
-def test_prefill_shape_sweep(dt, BS, G):
+@pytest.mark.parametrize("dt,D,BS,G", SWEEP)
+def test_prefill_shape_sweep(dt, D, BS, G):
     Hkv = 2
-    b = make_batch(B=3, Hq=Hkv * G, Hkv=Hkv, D=128, BS=BS, dtype=dt, scale=128 ** -0.5,
-                   seed=2000 + SWEEP.index((dt, BS, G)), n_new=150, ctx_range=(0, 400))
+    b = make_batch(B=3, Hq=Hkv * G, Hkv=Hkv, D=D, BS=BS, dtype=dt, scale=D ** -0.5,
+                   seed=2000 + SWEEP.index((dt, D, BS, G)), n_new=150, ctx_range=(0, 400))
     got = to_f64(_prefill(b, upload(b)))
-    check_close(got, _oracle(b), f"prefill {dt} BS{BS} G{G}")
+    check_close(got, _oracle(b), f"prefill {dt} D{D} BS{BS} G{G}")
+
+
+@pytest.mark.parametrize("n_new,ctx", [(1, (0, 0)), (17, (0, 0)), (64, (63, 65)), (300, (1000, 1400))])
+def test_prefill_head_dim_64_chunk_lengths(n_new, ctx):
+    b = make_batch(B=4, Hq=32, Hkv=8, D=64, BS=16, dtype="bf16", scale=0.125,
+                   seed=3050 + n_new, n_new=n_new, ctx_range=ctx)
+    got = to_f64(_prefill(b, upload(b), ordered=True))
+    check_close(got, _oracle(b), f"prefill D64 n={n_new} ctx={ctx}")
+
+
+def test_prefill_head_dim_64_rows_equal_decodes():
+    """Row t of a head_dim-64 chunk equals a GPU decode of the same query with context c + t + 1."""
+    b = make_batch(B=2, Hq=16, Hkv=4, D=64, BS=32, dtype="f16", scale=0.125, seed=3210,
+                   n_new=40, ctx_range=(100, 300))
+    d = upload(b)
+    got = to_f64(_prefill(b, d))
+    for i in range(b.B):
+        s0, n = int(b.query_start_loc[i]), int(b.n_new[i])
+        c = int(b.context_lens[i]) - n
+        ts = [0, 1, 31, 32, 39]
+        q = d.q[s0 + torch.tensor(ts, device="cuda")].contiguous()
+        lens = torch.tensor([c + t + 1 for t in ts], dtype=torch.int32, device="cuda")
+        tables = d.block_tables[i:i + 1].repeat(len(ts), 1).contiguous()
+        out = torch.empty_like(q)
+        pa_decode(out, q, d.k_cache, d.v_cache, tables, lens, b.scale, c + n, 0)
+        torch.cuda.synchronize()
+        check_close(got[[s0 + t for t in ts]], to_f64(out), "D64 chunk vs decodes")
 
 
 @pytest.mark.parametrize("n_new,ctx", [(1, (0, 0)), (1, (700, 900)), (17, (0, 0)),
