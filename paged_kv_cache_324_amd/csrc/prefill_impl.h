@@ -32,9 +32,9 @@
 //
 // Softmax statistics are fp32 (page "vLLM-Ascend ...", section 3.1, problem
 // 2); the probabilities are rounded to the input dtype for the PV product.  The
-// row sum is one more MFMA per 16-key step, ones^T P^T accumulated in fp32: it
-// sums exactly the rounded probabilities the numerator uses and takes the
-// additions off the vector ALU (the matrix cores have the spare cycles).
+// row sum adds exactly those rounded probabilities in fp32, two per
+// v_dot2_f32 with a pair of ones (16 per tile; lane l and l ^ 32 each sum their
+// half of the keys and are added once at the end).
 #pragma once
 
 #include "mfma.h"
@@ -189,9 +189,9 @@ void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
   float m = kPrefillEmptyMax;
-  f32x16 lacc = f32x16{};  // row sums of the rounded P, every row of the lane's column
+  // This lane's keys of its row's sum of the rounded P (lane l ^ 32 holds the others).
+  float lpart = 0.f;
   const uint32_t one2 = pack2<DT>(1.f, 1.f);
-  const u32x4 ones = {one2, one2, one2, one2};
 
   // ---- staging: wavefront w moves keys kv0 + 16 w .. + 15 (one block) of K
   // and of V with 16 / RPL 1 KB buffer loads each; lane l of load i brings key row
@@ -241,6 +241,24 @@ void prefill_kernel(const PrefillArgs a) {
   //   dim 32 dt + l % 32.
   const int p16 = lane & 15;
   const int dh = (lane >> 4) & 1;
+  // Those addresses for tile buffer 0, per lane, computed once.  Key rows 32 sub
+  // + r and 16 kk + r share r's swizzle (it depends on r % 16 only), so the other
+  // halves and steps add immediates (32 sub, 16 kk rows); the buffer flip of each
+  // tile adds +-kBuf to all of them.
+  constexpr int kBuf = 2 * NK * ROW;   // bytes from tile buffer 0 to buffer 1
+  uint32_t koff[D / 16], vlo[D / 32], vhi[D / 32];
+  {
+    const int r1 = 4 * half + (p16 >> 2);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) koff[ks] = tile_off<D>(lane & 31, 2 * ks + half);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int chunk = 4 * dt + 2 * dh + ((p16 & 3) >> 1);
+      vlo[dt] = NK * ROW + tile_off<D>(r1, chunk) + 8 * (p16 & 1);
+      vhi[dt] = NK * ROW + tile_off<D>(r1 + 8, chunk) + 8 * (p16 & 1);
+    }
+  }
+  const unsigned char* const lds = &s_kv[0][0][0];
 
   // Smallest causal limit over the wavefront's rows: tiles below it need no mask.
   int wave_min_vis = vis;
@@ -248,9 +266,7 @@ void prefill_kernel(const PrefillArgs a) {
   for (int o2 = 32; o2 >= 1; o2 >>= 1) wave_min_vis = min(wave_min_vis, __shfl_xor(wave_min_vis, o2));
   wave_min_vis = __builtin_amdgcn_readfirstlane(wave_min_vis);
 
-  auto compute = [&](int kv0, int buf) {
-    const unsigned char* sk = s_kv[buf][0];
-    const unsigned char* sv = s_kv[buf][1];
+  auto compute = [&](int kv0) {
     // ---- S^T for the tile's two 32-key halves
     // Matrix phases run at raised wave priority: of the two wavefronts sharing
     // a SIMD, the one with MFMAs ready issues first and the other's softmax
@@ -260,10 +276,9 @@ void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       s[sub] = f32x16{};
-      const int kr = sub * 32 + (lane & 31);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(sk + tile_off<D>(kr, 2 * ks + half));
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(lds + koff[ks] + sub * 32 * ROW);
         s[sub] = mfma32x32x16<DT>(kf, qf[ks], s[sub]);
       }
     }
@@ -275,12 +290,14 @@ void prefill_kernel(const PrefillArgs a) {
     // more than kLazyRescale (log2 units); until then p <= 2^kLazyRescale,
     // harmless in fp32 and in the 16-bit P.
     if (kv0 + NK > wave_min_vis) {
+      // key kv0 + 4 half + c (c = 32 sub + 8 (j / 4) + j % 4) is visible iff c < lim
+      const int lim = vis - kv0 - 4 * half;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int key = kv0 + sub * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-          s[sub][j] = key < vis ? s[sub][j] : -__builtin_inff();
+          const int c = sub * 32 + 8 * (j >> 2) + (j & 3);
+          s[sub][j] = c < lim ? s[sub][j] : -__builtin_inff();
         }
       }
     }
@@ -295,7 +312,7 @@ void prefill_kernel(const PrefillArgs a) {
       const float m_new = fmaxf(m, mx);
       const float alpha = fast_exp2(m - m_new);
       m = m_new;
-      lacc *= alpha;
+      lpart *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
     }
@@ -312,15 +329,11 @@ void prefill_kernel(const PrefillArgs a) {
       const int jb = 8 * (kk & 1);
       const u32x4 pf = {pack2<DT>(ps[jb + 0], ps[jb + 1]), pack2<DT>(ps[jb + 2], ps[jb + 3]),
                         pack2<DT>(ps[jb + 4], ps[jb + 5]), pack2<DT>(ps[jb + 6], ps[jb + 7])};
-      lacc = mfma32x32x16<DT>(ones, pf, lacc);
-      const int r1 = 16 * kk + 4 * half + (p16 >> 2);
-      const int r2 = r1 + 8;
+      lpart = dot2<DT>(pf.w, one2, dot2<DT>(pf.z, one2, dot2<DT>(pf.y, one2, dot2<DT>(pf.x, one2, lpart))));
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const int chunk = 4 * dt + 2 * dh + ((p16 & 3) >> 1);
-        const int sub8 = 8 * (p16 & 1);
-        const u32x2 lo = lds_read_tr16(sv + tile_off<D>(r1, chunk) + sub8);
-        const u32x2 hi = lds_read_tr16(sv + tile_off<D>(r2, chunk) + sub8);
+        const u32x2 lo = lds_read_tr16(lds + vlo[dt] + kk * 16 * ROW);
+        const u32x2 hi = lds_read_tr16(lds + vhi[dt] + kk * 16 * ROW);
         o[dt] = mfma32x32x16<DT>(u32x4{lo.x, lo.y, hi.x, hi.y}, pf, o[dt]);
       }
     }
@@ -348,14 +361,22 @@ void prefill_kernel(const PrefillArgs a) {
       }
       stage(kv0 + NK, (it + 1) & 1, ids_cur);
     }
-    if (kv0 < wave_end) compute(kv0, it & 1);
+    if (kv0 < wave_end) compute(kv0);
+    const int32_t flip = (it & 1) ? -kBuf : kBuf;   // next tile is in the other buffer
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) koff[ks] += flip;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      vlo[dt] += flip;
+      vhi[dt] += flip;
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
   // ---- normalise and store: lane holds dims 32 dt + 8 (j/4) + 4 half + (j%4)
+  const float lsum = sum_xor32(lpart);
   if (!row_valid) return;
-  const float lsum = lacc[0];
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;  // no visible key: zero row
   uint16_t* op = static_cast<uint16_t*>(a.out) + ((int64_t)(s0 + t) * a.num_heads + h) * D;
 #pragma unroll
