@@ -25,16 +25,21 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(ReshapeArgs a) {
     const int rem = local - lt * per_token;
     const int64_t t = tbase + lt;
     if (t >= a.num_tokens) break;
-    const int64_t slot = a.slot_mapping[t];
-    report_index_error(a.index_errors, slot >= a.num_slots, kErrSlot, slot);
-    if (slot < 0 || slot >= a.num_slots) continue;  // padding token / outside the pool
     const bool is_v = rem >= a.row_chunks;
     const int chunk = is_v ? rem - a.row_chunks : rem;
     const u32x4* src = reinterpret_cast<const u32x4*>(is_v ? a.value : a.key) +
                        t * a.row_chunks + chunk;
+    // The slot and the row are independent: both loads are issued before either
+    // is used (the row is read even for a skipped token; it lies in the input),
+    // so the copy costs one memory round trip before its store, not two.
+    const int64_t slot = a.slot_mapping[t];
+    u32x4 row = __builtin_nontemporal_load(src);
+    asm volatile("" : "+v"(row));  // keeps the row load ahead of the slot test (no sinking)
+    report_index_error(a.index_errors, slot >= a.num_slots, kErrSlot, slot);
+    if (slot < 0 || slot >= a.num_slots) continue;  // padding token / outside the pool
     u32x4* dst = reinterpret_cast<u32x4*>(is_v ? a.v_cache : a.k_cache) +
                  slot * a.row_chunks + chunk;
-    __builtin_nontemporal_store(__builtin_nontemporal_load(src), dst);
+    __builtin_nontemporal_store(row, dst);
   }
 }
 

@@ -31,11 +31,15 @@ __global__ __launch_bounds__(256) void reshape_int8_kernel(ReshapeInt8Args a) {
     const bool is_v = r & 1;
     const int64_t t = th / a.num_kv_heads;
     const int head = (int)(th - t * a.num_kv_heads);
+    // The slot and the row are independent loads, both issued before either is
+    // used (one memory round trip, not two); the row lies in the input even for
+    // a skipped token.
     const int64_t slot = a.slot_mapping[t];
+    u32x4 x = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(is_v ? a.value : a.key) +
+                                             th * D)[sub];
+    asm volatile("" : "+v"(x));  // keeps the row load ahead of the slot test (no sinking)
     report_index_error(a.index_errors, slot >= a.num_slots, kErrSlot, slot);
     if (slot < 0 || slot >= a.num_slots) continue;  // padding token / outside the pool
-    const u32x4 x = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(is_v ? a.value : a.key) +
-                                                   th * D)[sub];
     float f[8] = {lo_f32<DT>(x.x), hi_f32<DT>(x.x), lo_f32<DT>(x.y), hi_f32<DT>(x.y),
                   lo_f32<DT>(x.z), hi_f32<DT>(x.z), lo_f32<DT>(x.w), hi_f32<DT>(x.w)};
     float amax = 0.f;
