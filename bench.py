@@ -183,44 +183,60 @@ def upload(torch, b, dev):
 
 
 class Timer:
-    """The timing protocol.  A timed call is preceded by a flush: a read of a buffer of
-    `flush_mb` MiB (default 1 GiB, four times the 256 MB Infinity Cache), so no operand
-    is served from the MALL or an L2, and, being a read, it leaves no dirty line to be
-    written back during the call.  HIP events recorded on the stream the call is enqueued
-    on bracket the call alone."""
+    """The timing protocol.  A timed call is preceded by a flush: the library's read of a
+    buffer of `flush_mb` MiB (default 1 GiB, four times the 256 MB Infinity Cache), so no
+    operand is served from the MALL or an L2, and, being a read, it leaves no dirty line
+    to be written back during the call.  The call's duration is the interval between two
+    HIP events on its stream that the library's kernels record from their own dispatch
+    end timestamps (pa_set_kernel_events): the end of the flush and the end of the call's
+    last kernel.  No other packet sits between them, so the interval is the call's
+    device time plus the dispatch gap to its first kernel, the gap a stream of calls
+    also has."""
 
-    def __init__(self, torch, dev, flush_mb: int):
+    def __init__(self, torch, pa, dev, flush_mb: int):
         self.torch = torch
+        self.pa = pa
         self.stream = torch.cuda.current_stream(dev)
         self.flush_bytes = max(1, int(flush_mb)) << 20
-        # float32 rows of 64 KiB: torch's row sums over them are its fastest streaming read
-        self.flush_buf = torch.zeros((self.flush_bytes >> 16, 1 << 14), dtype=torch.float32,
-                                     device=dev)
+        self.flush_buf = torch.zeros(self.flush_bytes, dtype=torch.uint8, device=dev)
 
     def flush(self):
-        self.flush_buf.sum(dim=1)
+        self.pa.pa_cache_flush(self.flush_buf, stream=self.stream)
 
-    def _bracket(self, fn, n, flush):
+    def _events(self, n):
         torch = self.torch
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n)]
-        torch.cuda.synchronize()
-        for s, e in ev:
-            if flush:
-                self.flush()
-            s.record(self.stream)
-            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in ev:              # a torch event holds no HIP event before its first record
             e.record(self.stream)
         torch.cuda.synchronize()
-        return np.array([s.elapsed_time(e) for s, e in ev])
+        return ev
 
     def cold(self, fn, n):
-        """Durations (ms) of n calls, each after a flush."""
-        return self._bracket(fn, n, True)
+        """Device times (ms) of n calls, each after a flush: flush end to call end."""
+        marks, ends = self._events(n), self._events(n)
+        try:
+            for a, b in zip(marks, ends):
+                self.pa.pa_set_kernel_events(None, a)
+                self.flush()
+                self.pa.pa_set_kernel_events(None, b)
+                fn()
+        finally:
+            self.pa.pa_set_kernel_events()
+        self.torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in zip(marks, ends)])
 
     def warm(self, fn, n):
-        """Durations (ms) of n event-bracketed calls issued back to back."""
-        return self._bracket(fn, n, False)
+        """Device times (ms) of n calls issued back to back: the end of each call to the end
+        of the next (n + 1 calls)."""
+        ends = self._events(n + 1)
+        try:
+            for b in ends:
+                self.pa.pa_set_kernel_events(None, b)
+                fn()
+        finally:
+            self.pa.pa_set_kernel_events()
+        self.torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in zip(ends[:-1], ends[1:])])
 
     def back_to_back(self, fn, n):
         """Wall time per call (ms) of n calls issued back to back, nothing else on the stream."""
@@ -244,16 +260,14 @@ class Timer:
             torch.cuda.synchronize()
 
     def stream_read_ceiling(self):
-        """A streaming read of the flush buffer (torch's row sums over float32, its fastest
-        read-only kernel here), as a reference rate for what a read-only kernel reaches on
-        this device; never used as a denominator."""
+        """The flush itself timed back to back: a plain streaming read, as a reference rate
+        for what a read-only kernel reaches on this device; never used as a denominator."""
         for _ in range(3):
             self.flush()
-        ms = self.warm(self.flush, 10)
-        return {"kernel": f"torch row sums over {self.flush_bytes >> 20} MiB of float32 "
-                          "(a streaming read)",
-                "GBps": round(self.flush_bytes / (float(np.median(ms)) * 1e-3) / 1e9, 1),
-                "us_p50": round(float(np.median(ms)) * 1e3, 2)}
+        ms = float(np.median(self.warm(self.flush, 10)))
+        return {"kernel": f"pa_cache_flush over {self.flush_bytes >> 20} MiB (a streaming read)",
+                "GBps": round(self.flush_bytes / (ms * 1e-3) / 1e9, 1),
+                "us_p50": round(ms * 1e3, 2)}
 
 
 # Secondary workloads run a fixed number of cold steps after a time-based warm-up,
@@ -300,6 +314,7 @@ def run_decode(pa, torch, b, partition, steps, warmup, unfused, dev, timer, warm
     step_ms = timer.cold(step, steps)                     # the timed region
     out_bits = out.view(torch.int16).cpu().numpy().view(np.uint16)
     warm_ms = timer.back_to_back(step, steps)
+    warm_dev_ms = timer.warm(step, steps)
     split = bool(partition) and b.max_context_len > partition
     phases = None
     if split:
@@ -324,8 +339,8 @@ def run_decode(pa, torch, b, partition, steps, warmup, unfused, dev, timer, warm
     kern = "decode_mfma_kernel" if (b.G >= 4 and b.D == 128) else "decode_partition_kernel"
     name = ("pa_decode" if unfused else "pa_decode_step") + (
         f" ({kern} + merge kernel)" if split else f" (one {kern} launch)")
-    return {"step_ms": step_ms, "warm_ms": warm_ms, "kernel_name": name, "phases": phases,
-            "out_bits": out_bits}
+    return {"step_ms": step_ms, "warm_ms": warm_ms, "warm_dev_ms": warm_dev_ms,
+            "kernel_name": name, "phases": phases, "out_bits": out_bits}
 
 
 def int8_kv_bytes(b) -> int:
@@ -749,7 +764,7 @@ def main(argv=None) -> int:
         print("bench.py: the headline workload is a decode batch", file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
-    timer = Timer(torch, dev, args.flush_mb)
+    timer = Timer(torch, pa, dev, args.flush_mb)
 
     t_gen = time.perf_counter()
     seed = cfg["seed"] if args.seed is None else args.seed
@@ -784,16 +799,20 @@ def main(argv=None) -> int:
                    "seq_order": "longest context first (pa_decode_order on the host)",
                    "kv_bytes_per_step": kv},
         "protocol": (f"{args.warmup} warm-up steps, then {args.steps} timed steps, each after a "
-                     f"{args.flush_mb} MiB flush read and bracketed by HIP events on its stream; "
-                     "value and ms_per_step from the median, roofline.achieved from the mean of "
-                     "the same durations"),
+                     f"{args.flush_mb} MiB flush read (pa_cache_flush); a step's time runs from "
+                     "the flush kernel's end to the step's last kernel's end, both HIP events on "
+                     "the stream recorded from the kernels' dispatch timestamps "
+                     "(pa_set_kernel_events); value and ms_per_step from the median, "
+                     "roofline.achieved from the mean of the same durations"),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "seqs_per_s": round(b.B / t, 1),
         "step_us": _stats_us(r["step_ms"]),
         "warm_back_to_back": {"us_per_step": round(r["warm_ms"] * 1e3, 2),
                               "GBps": round(kv / (r["warm_ms"] * 1e-3) / 1e9, 2),
+                              "device_us": _stats_us(r["warm_dev_ms"]),
                               "note": "labelled extra: the same step issued back to back "
-                                      "without flushes, wall time per step"},
+                                      "without flushes; us_per_step is wall time per step, "
+                                      "device_us the interval between consecutive steps' ends"},
         "kernels": r["phases"] or {"k2": r["kernel_name"], "k3": "none (no context split)"},
         "stream_read_ceiling": timer.stream_read_ceiling(),
         "roofline": _hbm_roofline(r["kernel_name"], kv, r["step_ms"],

@@ -117,6 +117,33 @@ int pa_take_index_errors(void* stream, uint32_t* kinds, uint32_t* first_kind,
                          int64_t* first_value);
 
 /*
+ * Measuring aids.
+ *
+ * pa_set_kernel_events arms HIP events (hipEvent_t handles the caller created
+ * with timing enabled) on the calling thread.  While armed, every kernel a
+ * library call on this thread launches records stop_event as it ends, from
+ * the dispatch's own end timestamp (hipExtLaunchKernel); start_event, if not
+ * NULL, is recorded by the first kernel launched after arming, as it begins
+ * (the runtime may place it in a packet of its own just before that kernel).
+ * Arming again replaces both; (NULL, NULL) disarms.  A start event without a
+ * stop event is PA_ERR_INVALID_ARG.  A call that launches no kernel leaves the
+ * events as they were.  The events stay the caller's and must outlive the
+ * launches that record them.  Stop events armed around two calls in turn give,
+ * by hipEventElapsedTime, the device time from the end of the first call's
+ * last kernel to the end of the second's.
+ *
+ * pa_cache_flush reads `bytes` bytes of the device buffer `buf` (address and
+ * size multiples of 16) on `stream` and writes nothing: read through a buffer
+ * larger than the caches, it leaves the L2s and the Infinity Cache holding
+ * clean lines of its own, so that a kernel after it finds none of its
+ * operands cached.  bytes == 0 is a no-op; a NULL buffer or misaligned
+ * address or size is PA_ERR_INVALID_ARG.
+ */
+int pa_set_kernel_events(void* start_event, void* stop_event);
+
+int pa_cache_flush(const void* buf, size_t bytes, void* stream);
+
+/*
  * reshape_and_cache: write this step's new keys and values into their cache
  * slots (the fill of fixed-size blocks, page "vLLM-Ascend ...", section 2.2,
  * preprocessing stage; block layout of page "Nano-vLLM-Ascend", section 2.1).

@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     checked_indices,
     decode_workspace,
     load_library,
+    pa_cache_flush,
     pa_copy_blocks,
     pa_decode,
     pa_decode_int8,
@@ -30,6 +31,7 @@ from ._binding import (  # noqa: F401
     pa_prefill_chunk,
     pa_reshape_and_cache,
     pa_reshape_and_cache_int8,
+    pa_set_kernel_events,
     pa_rope_reshape_and_cache,
     pa_take_index_errors,
     pa_version,

@@ -52,6 +52,10 @@ def _declare(lib):
     lib.pa_check_indices_enabled.argtypes = []
     lib.pa_take_index_errors.restype = c_int
     lib.pa_take_index_errors.argtypes = [c_vp, c_vp, c_vp, c_vp]
+    lib.pa_set_kernel_events.restype = c_int
+    lib.pa_set_kernel_events.argtypes = [c_vp, c_vp]
+    lib.pa_cache_flush.restype = c_int
+    lib.pa_cache_flush.argtypes = [c_vp, c_sz, c_vp]
     lib.pa_reshape_and_cache.restype = c_int
     lib.pa_reshape_and_cache.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_int, c_int, c_int,
                                          c_i64, c_int, c_vp]
@@ -182,6 +186,34 @@ def pa_take_index_errors(stream=None):
     if st not in (PA_OK, PA_ERR_BAD_INDEX):
         raise PAError(st, f"{lib.pa_status_string(st).decode()}: {lib.pa_last_error().decode()}")
     return st, kinds.value, first_kind.value, first_value.value
+
+
+def _event_handle(ev) -> int | None:
+    if ev is None:
+        return None
+    if isinstance(ev, int):
+        return ev
+    handle = ev.cuda_event
+    if not handle:
+        raise ValueError("a torch.cuda.Event has no HIP event until it is first recorded")
+    return handle
+
+
+def pa_set_kernel_events(start=None, stop=None) -> None:
+    """Arm timing events on this thread (no arguments: disarm).  While armed, every kernel the
+    library launches records ``stop`` as it ends; ``start``, if given, is recorded by the first
+    one as it begins.  Takes torch.cuda.Event objects (enable_timing=True, recorded once so that
+    their HIP event exists) or raw hipEvent_t handles."""
+    _check(load_library().pa_set_kernel_events(_event_handle(start), _event_handle(stop)))
+
+
+def pa_cache_flush(buf: torch.Tensor, stream=None) -> None:
+    """Read all of the device tensor ``buf`` and write nothing (evicts the caches' contents
+    when ``buf`` is larger than them)."""
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    _check(load_library().pa_cache_flush(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                         _stream(buf, stream)))
 
 
 def _check(status: int) -> None:

@@ -38,7 +38,7 @@ hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s) {
   if (total == 0) return hipSuccess;
   int64_t blocks = (total + 255) / 256;
   if (blocks > (1 << 20)) blocks = 1 << 20;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  launch(copy_blocks_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

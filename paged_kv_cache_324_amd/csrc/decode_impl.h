@@ -548,16 +548,16 @@ void launch_partitions(const DecodeArgs& a, unsigned grid, hipStream_t s) {
   using Shape = DecodeShape<G>;
   if constexpr (decode_uses_mfma<D, G>()) {
     if (a.part_tokens >= kMfmaLongSpan) {
-      hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, G, 8, ROPE>), dim3(grid), dim3(512), 0, s, a);
+      launch((decode_mfma_kernel<DT, BS, G, 8, ROPE>), dim3(grid), dim3(512), 0, s, a);
     } else if (a.num_parts > 1 && a.part_tokens <= kMfmaShortPartition) {
-      hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, G, 2, ROPE>), dim3(grid), dim3(128), 0, s, a);
+      launch((decode_mfma_kernel<DT, BS, G, 2, ROPE>), dim3(grid), dim3(128), 0, s, a);
     } else {
-      hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, G, 4, ROPE>), dim3(grid), dim3(256), 0, s, a);
+      launch((decode_mfma_kernel<DT, BS, G, 4, ROPE>), dim3(grid), dim3(256), 0, s, a);
     }
   } else {
-    hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, Shape::waves, Shape::pf,
-                                                Shape::waves_per_eu, PA_DECODE_AUX, ROPE>),
-                       dim3(grid), dim3(64 * Shape::waves), 0, s, a);
+    launch((decode_partition_kernel<DT, D, BS, G, Shape::waves, Shape::pf, Shape::waves_per_eu,
+                                    PA_DECODE_AUX, ROPE>),
+           dim3(grid), dim3(64 * Shape::waves), 0, s, a);
   }
 }
 
@@ -566,8 +566,8 @@ void launch_partitions(const DecodeArgs& a, unsigned grid, hipStream_t s) {
 template <int DT, int D>
 void launch_merge(const DecodeArgs& a, hipStream_t s) {
   if (a.num_parts > 1) {
-    hipLaunchKernelGGL((decode_merge_kernel<DT, D>), dim3((unsigned)(a.num_seqs * a.num_heads)),
-                       dim3(64), 0, s, a);
+    launch((decode_merge_kernel<DT, D>), dim3((unsigned)(a.num_seqs * a.num_heads)), dim3(64),
+           0, s, a);
   }
 }
 

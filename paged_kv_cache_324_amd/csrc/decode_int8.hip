@@ -461,11 +461,11 @@ hipError_t launch_int8_t(const DecodeArgs& a, int phases, hipStream_t s) {
   // short partition (long split-K INT8 decode at 512: 100.3 -> 96.4 us; unsplit
   // contexts of up to 2048 tokens lose with two: 62.1 -> 67.5 us); four otherwise.
   if (a.part_tokens >= kMfmaLongSpan) {
-    hipLaunchKernelGGL((decode_int8_kernel<DT, D, BS, G, 8>), dim3(grid), dim3(512), 0, s, a);
+    launch((decode_int8_kernel<DT, D, BS, G, 8>), dim3(grid), dim3(512), 0, s, a);
   } else if (a.num_parts > 1 && a.part_tokens <= kMfmaShortPartition) {
-    hipLaunchKernelGGL((decode_int8_kernel<DT, D, BS, G, 2>), dim3(grid), dim3(128), 0, s, a);
+    launch((decode_int8_kernel<DT, D, BS, G, 2>), dim3(grid), dim3(128), 0, s, a);
   } else {
-    hipLaunchKernelGGL((decode_int8_kernel<DT, D, BS, G, 4>), dim3(grid), dim3(256), 0, s, a);
+    launch((decode_int8_kernel<DT, D, BS, G, 4>), dim3(grid), dim3(256), 0, s, a);
   }
   if (phases & kPhaseMerge) launch_merge<DT, D>(a, s);
   return hipGetLastError();

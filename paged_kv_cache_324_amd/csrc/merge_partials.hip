@@ -93,12 +93,12 @@ hipError_t launch_merge_partials(const MergePartialsArgs& a, int dtype, int head
                                  hipStream_t s) {
   const dim3 grid((unsigned)a.num_rows), block(64);
   if (dtype == DT_BF16) {
-    if (head_dim == 128) hipLaunchKernelGGL((merge_partials_kernel<DT_BF16, 128>), grid, block, 0, s, a);
-    else if (head_dim == 64) hipLaunchKernelGGL((merge_partials_kernel<DT_BF16, 64>), grid, block, 0, s, a);
+    if (head_dim == 128) launch((merge_partials_kernel<DT_BF16, 128>), grid, block, 0, s, a);
+    else if (head_dim == 64) launch((merge_partials_kernel<DT_BF16, 64>), grid, block, 0, s, a);
     else return hipErrorInvalidValue;
   } else {
-    if (head_dim == 128) hipLaunchKernelGGL((merge_partials_kernel<DT_F16, 128>), grid, block, 0, s, a);
-    else if (head_dim == 64) hipLaunchKernelGGL((merge_partials_kernel<DT_F16, 64>), grid, block, 0, s, a);
+    if (head_dim == 128) launch((merge_partials_kernel<DT_F16, 128>), grid, block, 0, s, a);
+    else if (head_dim == 64) launch((merge_partials_kernel<DT_F16, 64>), grid, block, 0, s, a);
     else return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -36,6 +36,11 @@ int ok() {
   return PA_OK;
 }
 
+KernelEvents& kernel_events() {
+  static thread_local KernelEvents ev{};
+  return ev;
+}
+
 }  // namespace pa
 
 namespace {
@@ -299,6 +304,26 @@ int pa_take_index_errors(void* stream, uint32_t* kinds, uint32_t* first_kind,
   return fail(PA_ERR_UNSUPPORTED,
               "this library is built without PA_CHECK_INDICES; index checks are in libpa_check.so");
 #endif
+}
+
+int pa_set_kernel_events(void* start_event, void* stop_event) {
+  if (start_event != nullptr && stop_event == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "a start event needs a stop event");
+  pa::KernelEvents& ev = pa::kernel_events();
+  ev.start = static_cast<hipEvent_t>(start_event);
+  ev.stop = static_cast<hipEvent_t>(stop_event);
+  ev.start_pending = start_event != nullptr;
+  return ok();
+}
+
+int pa_cache_flush(const void* buf, size_t bytes, void* stream) {
+  if (bytes == 0) return ok();
+  if (buf == nullptr) return fail(PA_ERR_INVALID_ARG, "null buffer");
+  if ((reinterpret_cast<uintptr_t>(buf) & 15) != 0 || (bytes & 15) != 0)
+    return fail(PA_ERR_INVALID_ARG, "buffer address and size must be multiples of 16 bytes");
+  if (const int b = check_build()) return b;
+  return hip_status(pa::launch_cache_flush(buf, (int64_t)(bytes / 16), static_cast<hipStream_t>(stream)),
+                    "cache_flush launch");
 }
 
 int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* src, const int64_t* dst,

@@ -1,6 +1,7 @@
 // Internal launch interface between the C ABI (pa_api.cpp) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -186,8 +187,36 @@ struct MergePartialsArgs {
 hipError_t launch_merge_partials(const MergePartialsArgs& a, int dtype, int head_dim,
                                  hipStream_t s);
 
+hipError_t launch_cache_flush(const void* buf, int64_t chunks, hipStream_t s);
+
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int block_size,
                           int group, hipStream_t s);
+
+// ---- kernel timing events --------------------------------------------------
+// Events armed on the calling thread by pa_set_kernel_events: the first kernel
+// launched after arming records `start` (if any) and every kernel launched
+// while armed records `stop` as it ends, from the dispatch's own timestamps.
+struct KernelEvents {
+  hipEvent_t start;
+  hipEvent_t stop;
+  bool start_pending;
+};
+KernelEvents& kernel_events();
+
+// Every kernel of the library is launched through this: hipLaunchKernelGGL,
+// or the extended launch that records the armed events.
+template <typename... KArgs, typename... Args>
+inline void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds_bytes,
+                   hipStream_t s, Args... args) {
+  KernelEvents& ev = kernel_events();
+  if (ev.stop == nullptr) {
+    hipLaunchKernelGGL(kernel, grid, block, lds_bytes, s, args...);
+    return;
+  }
+  hipEvent_t start = ev.start_pending ? ev.start : nullptr;
+  ev.start_pending = false;
+  hipExtLaunchKernelGGL(kernel, grid, block, lds_bytes, s, start, ev.stop, 0u, args...);
+}
 
 // ---- layout check ----------------------------------------------------------
 // The launch-argument structs cross translation units by value, so every unit

@@ -400,7 +400,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t s) {
   const int64_t grid = (groups + kXcds - 1) / kXcds * kXcds * a.q_tiles;
   if (grid == 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<DT, D, BS, G>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  launch((prefill_kernel<DT, D, BS, G>), dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

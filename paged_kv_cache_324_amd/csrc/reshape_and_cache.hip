@@ -51,7 +51,7 @@ hipError_t launch_reshape_and_cache(const ReshapeArgs& a, hipStream_t s) {
   const int64_t tpb = per_token >= 256 ? 1 : 256 / per_token;
   const int64_t blocks = (a.num_tokens + tpb - 1) / tpb;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  launch(reshape_and_cache_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -78,11 +78,11 @@ hipError_t launch_reshape_int8(const ReshapeInt8Args& a, int dtype, int head_dim
   if (blocks > (1 << 20)) blocks = 1 << 20;
   const dim3 grid((unsigned)blocks), block(256);
   if (dtype == DT_BF16) {
-    if (head_dim == 128) hipLaunchKernelGGL((reshape_int8_kernel<DT_BF16, 128>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((reshape_int8_kernel<DT_BF16, 64>), grid, block, 0, s, a);
+    if (head_dim == 128) launch((reshape_int8_kernel<DT_BF16, 128>), grid, block, 0, s, a);
+    else launch((reshape_int8_kernel<DT_BF16, 64>), grid, block, 0, s, a);
   } else {
-    if (head_dim == 128) hipLaunchKernelGGL((reshape_int8_kernel<DT_F16, 128>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((reshape_int8_kernel<DT_F16, 64>), grid, block, 0, s, a);
+    if (head_dim == 128) launch((reshape_int8_kernel<DT_F16, 128>), grid, block, 0, s, a);
+    else launch((reshape_int8_kernel<DT_F16, 64>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

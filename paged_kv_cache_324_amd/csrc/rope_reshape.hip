@@ -94,12 +94,12 @@ hipError_t launch_rope_reshape(const RopeReshapeArgs& a, int dtype, int head_dim
   const int threads = (int)(items >= 1024 ? 1024 : (items + 63) / 64 * 64);
   const dim3 grid((unsigned)a.num_tokens), block(threads);
   if (dtype == DT_BF16) {
-    if (head_dim == 128) hipLaunchKernelGGL((rope_reshape_kernel<DT_BF16, 128>), grid, block, 0, s, a);
-    else if (head_dim == 64) hipLaunchKernelGGL((rope_reshape_kernel<DT_BF16, 64>), grid, block, 0, s, a);
+    if (head_dim == 128) launch((rope_reshape_kernel<DT_BF16, 128>), grid, block, 0, s, a);
+    else if (head_dim == 64) launch((rope_reshape_kernel<DT_BF16, 64>), grid, block, 0, s, a);
     else return hipErrorInvalidValue;
   } else {
-    if (head_dim == 128) hipLaunchKernelGGL((rope_reshape_kernel<DT_F16, 128>), grid, block, 0, s, a);
-    else if (head_dim == 64) hipLaunchKernelGGL((rope_reshape_kernel<DT_F16, 64>), grid, block, 0, s, a);
+    if (head_dim == 128) launch((rope_reshape_kernel<DT_F16, 128>), grid, block, 0, s, a);
+    else if (head_dim == 64) launch((rope_reshape_kernel<DT_F16, 64>), grid, block, 0, s, a);
     else return hipErrorInvalidValue;
   }
   return hipGetLastError();

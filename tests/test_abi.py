@@ -349,3 +349,18 @@ def test_index_errors_need_the_checking_library(lib):
     assert "PA_CHECK_INDICES" in lib.pa_last_error().decode()
     assert (k.value, f.value, v.value) == (0, 0, 0)
     assert lib.pa_take_index_errors(None, None, None, None) == -1
+
+
+def test_kernel_events_and_cache_flush_reject_bad_arguments(lib):
+    assert lib.pa_set_kernel_events(P, None) == -1
+    assert "stop event" in lib.pa_last_error().decode()
+    assert lib.pa_set_kernel_events(None, P) == 0       # arming makes no HIP call
+    assert lib.pa_set_kernel_events(P, P) == 0
+    assert lib.pa_set_kernel_events(None, None) == 0
+    pa.pa_set_kernel_events()
+    with pytest.raises(ValueError):
+        pa.pa_set_kernel_events(__import__("torch").cuda.Event(enable_timing=True), 1)
+    assert lib.pa_cache_flush(None, 0, None) == 0       # nothing to read
+    assert lib.pa_cache_flush(None, 16, None) == -1
+    assert lib.pa_cache_flush(ctypes.c_void_p(0x1008), 16, None) == -1
+    assert lib.pa_cache_flush(P, 24, None) == -1
