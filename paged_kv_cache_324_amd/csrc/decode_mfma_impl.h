@@ -13,23 +13,29 @@
 // The partition is cut into 32-key steps taken round-robin by the NW
 // wavefronts:
 //   S^T = K Q^T   16x16x32 MFMA, two 16-key groups per step.  A = K rows
-//                 (16 keys x 32 dims), loaded straight from the cache into
-//                 registers: lane l takes key l % 16, dims 32 ks + 8 (l/16) ..,
-//                 through a buffer resource based at the group's block (16
-//                 keys never straddle a block) whose size ends at the last
-//                 valid key.  B = Q^T, the G heads in columns 0..G-1.
+//                 (16 keys x 32 dims).  K and V rows are loaded whole, four
+//                 256-byte rows per load instruction, through buffer
+//                 resources based at the group's block (16 keys never
+//                 straddle a block) whose size ends at the last valid key;
+//                 K goes through this wavefront's LDS K buffer, from which
+//                 lane l reads key l % 16, dims 32 ks + 8 (l/16) ...  (Loading
+//                 the A fragments straight from the cache made each load
+//                 instruction span 16 rows 2 KB apart, eight 4 KB pages, and
+//                 stalled the L1 address translation: 10% slower on Llama-2-
+//                 shaped batches, 11% on split long contexts.)  B = Q^T, the G
+//                 heads in columns 0..G-1.
 //   softmax       lane l owns head l % 16 and 4 keys of each group; the max
 //                 adds two lane exchanges (l ^ 16, l ^ 32).  Rescaling of O is
 //                 lazy (only when a maximum grows by more than 2^8).
 //   O^T += V^T P^T  16x16x16 MFMA over each group's 16 keys.  V rows are
 //                 loaded into registers with K, stored to this wavefront's LDS
-//                 buffer and read back transposed (ds_read_b64_tr_b16); P^T is
+//                 V buffer and read back transposed (ds_read_b64_tr_b16); P^T is
 //                 the softmax registers rounded to the input dtype.
 //   row sum       one more 16x16x16 MFMA per group, ones P^T: the sum, in
 //                 fp32, of exactly the rounded p the value product consumes,
 //                 so numerator and denominator weigh every key alike.
-// As soon as a step's K and V have left their registers (scores issued, V in
-// LDS) the same registers take the loads of the wavefront's next step, whose
+// As soon as a step's K and V have left their registers (both in LDS) the
+// same registers take the loads of the wavefront's next step, whose
 // block ids were loaded a step earlier still; so one step per wavefront is
 // always in flight.
 // At the end the NW wavefronts' (m, l, O) are merged through LDS and the
@@ -51,6 +57,10 @@ constexpr float kMdLazyRescale = 8.0f;
 // the transposed reads (8 rows x chunks {2 dt, 2 dt + 1} per half wavefront)
 // then touch 16 distinct bank groups.
 __device__ __forceinline__ int md_vswz(int r) { return (2 * r) & 15; }
+// K rows likewise with chunk c of row r at c ^ (r & 7): the score operands (16
+// rows, one 16-byte chunk each per quarter wavefront) then read 8 distinct bank
+// groups per 8 lanes.
+__device__ __forceinline__ int md_kswz(int r) { return r & 7; }
 
 template <int DT, int BS, int G, int NW, bool ROPE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -61,6 +71,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
   // One V buffer per wavefront; at the end the same bytes hold that
   // wavefront's fp32 O^T (16 heads x 128 dims) for the merge.
   __shared__ __attribute__((aligned(16))) unsigned char s_v[NW][kMdStep];  // 8 KB per wavefront
+  __shared__ __attribute__((aligned(16))) unsigned char s_k[NW][kMdStep];
   __shared__ float s_ml[NW * 16 * 2];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -106,23 +117,23 @@ void decode_mfma_kernel(const DecodeArgs a) {
   // Fused rotary step: fragment ks holds 16-byte chunk 4 ks + quad, so chunks
   // j and j + 8 (dims 8 j .. + 7 of the two halves) are fragments ks and ks + 2
   // of the same lane; table entries of pair index 8 (4 ks + quad), ks = 0, 1.
-  float rcs[2][8], rsn[2][8];
+  // The table rows are read where they are used (for q, then for the new key),
+  // so they hold no registers across the context loop.
+  int64_t rope_pos = 0;
   bool rope_ok = false;
   if constexpr (ROPE) {
-    const int64_t pos = a.positions[seq];
-    rope_ok = pos >= 0 && pos < a.max_position;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      rope_row8(a.rope_cos, rope_ok ? pos : 0, D / 2, 8 * (4 * ks + quad), rcs[ks]);
-      rope_row8(a.rope_sin, rope_ok ? pos : 0, D / 2, 8 * (4 * ks + quad), rsn[ks]);
-    }
+    rope_pos = a.positions[seq];
+    rope_ok = rope_pos >= 0 && rope_pos < a.max_position;
   }
   auto rotate_frags = [&](u32x4 (&f)[4]) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      float rcs[8], rsn[8];
+      rope_row8(a.rope_cos, rope_pos, D / 2, 8 * (4 * ks + quad), rcs);
+      rope_row8(a.rope_sin, rope_pos, D / 2, 8 * (4 * ks + quad), rsn);
       const u32x4 x1 = f[ks], x2 = f[ks + 2];
-      f[ks] = rope_half8<DT>(x1, x2, rcs[ks], rsn[ks], true);
-      f[ks + 2] = rope_half8<DT>(x2, x1, rcs[ks], rsn[ks], false);
+      f[ks] = rope_half8<DT>(x1, x2, rcs, rsn, true);
+      f[ks + 2] = rope_half8<DT>(x2, x1, rcs, rsn, false);
     }
   };
 
@@ -152,9 +163,8 @@ void decode_mfma_kernel(const DecodeArgs a) {
       if constexpr (ROPE) {
         if (lane < 16 && rope_ok) {  // the stored key is the rotated one
           float cs[8], sn[8];
-          const int64_t pos = a.positions[seq];
-          rope_row8(a.rope_cos, pos, D / 2, 8 * (col & 7), cs);
-          rope_row8(a.rope_sin, pos, D / 2, 8 * (col & 7), sn);
+          rope_row8(a.rope_cos, rope_pos, D / 2, 8 * (col & 7), cs);
+          rope_row8(a.rope_sin, rope_pos, D / 2, 8 * (col & 7), sn);
           chunk = rope_half8<DT>(chunk, srow[col ^ 8], cs, sn, col < 8);
         }
       }
@@ -182,11 +192,11 @@ void decode_mfma_kernel(const DecodeArgs a) {
   const uint32_t one2 = pack2<DT>(1.f, 1.f);
   const u32x2 ones = {one2, one2};
   unsigned char* const sv = s_v[wave];
-  u32x4 kf[2][4], vr[2][4];
+  unsigned char* const sk = s_k[wave];
+  u32x4 kf[2][4], kr[2][4], vr[2][4];
 
-  // K fragments to registers (lane: key col, dims 32 ks + 8 quad ..) and the
-  // V rows this lane will store (row 4 i + quad of each group, chunk col ^
-  // swizzle), for step s; `ids` holds the step's block ids.  Past
+  // The K and V rows this lane will store (row 4 i + quad of each group,
+  // chunk col ^ swizzle), for step s; `ids` holds the step's block ids.  Past
   // the cached range the resources have size 0: loads return zeros without
   // touching memory.
   auto issue = [&](int s, int32_t ids) {
@@ -205,12 +215,10 @@ void decode_mfma_kernel(const DecodeArgs a) {
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + off, nrec);
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + off, nrec);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        kf[gr][ks] = buffer_load16<kCachePolicyNT>(
-            rk, (uint32_t)col * row_bytes + (uint32_t)(4 * ks + quad) * 16);
-#pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = 4 * i + quad;
+        kr[gr][i] = buffer_load16<kCachePolicyNT>(
+            rk, (uint32_t)rr * row_bytes + (uint32_t)((col ^ md_kswz(16 * gr + rr)) * 16));
         vr[gr][i] = buffer_load16<kCachePolicyNT>(
             rv, (uint32_t)rr * row_bytes + (uint32_t)((col ^ md_vswz(16 * gr + rr)) * 16));
       }
@@ -223,6 +231,25 @@ void decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<u32x4*>(sv + (16 * gr + 4 * i + quad) * kMdRow + col * 16) = vr[gr][i];
+  };
+  auto store_k = [&]() {
+#pragma unroll
+    for (int gr = 0; gr < 2; ++gr)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4*>(sk + (16 * gr + 4 * i + quad) * kMdRow + col * 16) = kr[gr][i];
+  };
+  // Score operands from the K rows in LDS: lane (key col, quad) takes chunk
+  // 4 ks + quad of key 16 gr + col.
+  auto load_kf = [&]() {
+#pragma unroll
+    for (int gr = 0; gr < 2; ++gr) {
+      const int r = 16 * gr + col;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kf[gr][ks] = *reinterpret_cast<const u32x4*>(
+            sk + r * kMdRow + (((4 * ks + quad) ^ md_kswz(r)) * 16));
+    }
   };
 
   auto scores = [&](f32x4 (&sc)[2]) {
@@ -334,7 +361,9 @@ void decode_mfma_kernel(const DecodeArgs a) {
       // (clamped ids, size-0 resources), so every step sees the same loads in
       // flight.
       const int32_t ids_after = load_ids(s + 2 * NW);
+      store_k();
       store_v();
+      load_kf();
       f32x4 sc[2];
       scores(sc);
       issue(s + NW, ids_next);
