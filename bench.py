@@ -334,9 +334,9 @@ def run_decode(pa, torch, b, partition, steps, warmup, unfused, dev, timer, warm
                   "note": "k2: pa_decode_partitions alone, cold (no new-token store); k3: "
                           "pa_decode_merge alone over the partials k2 left, back to back "
                           "(the partials resident, as after k2 in a step)"}
-    # The library runs the matrix-core kernel for 4+ query heads per KV head at
+    # The library runs the matrix-core kernel for 2+ query heads per KV head at
     # head_dim 128, the vector kernel otherwise.
-    kern = "decode_mfma_kernel" if (b.G >= 4 and b.D == 128) else "decode_partition_kernel"
+    kern = "decode_mfma_kernel" if (b.G >= 2 and b.D == 128) else "decode_partition_kernel"
     name = ("pa_decode" if unfused else "pa_decode_step") + (
         f" ({kern} + merge kernel)" if split else f" (one {kern} launch)")
     return {"step_ms": step_ms, "warm_ms": warm_ms, "warm_dev_ms": warm_dev_ms,
@@ -607,7 +607,7 @@ def secondary_entry(pa, torch, entry, dev, timer):
         ns = int(variant[2:])
         r2 = run_decode_cp(pa, torch, b2, ns, n, dev, timer)
         kb = r2["shard_kv_bytes"]
-        kern = "decode_mfma_kernel" if (b2.G >= 4 and b2.D == 128) else "decode_partition_kernel"
+        kern = "decode_mfma_kernel" if (b2.G >= 2 and b2.D == 128) else "decode_partition_kernel"
         return {
             "step": f"pa_decode_partial (shard 0 of {ns}) + pa_merge_partials ({ns} shards)",
             "partition_size": r2["partition_size"], "steps": n,

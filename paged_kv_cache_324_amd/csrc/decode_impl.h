@@ -49,11 +49,13 @@ namespace pa {
 #endif
 
 // Launch shape of decode_partition_kernel for G query heads per KV head.
-// G <= 2: eight wavefronts per workgroup and four steps of K and V in flight
+// G <= 2 (G = 2 only at head_dim 64: at head_dim 128 the matrix-core kernel
+// runs): eight wavefronts per workgroup and four steps of K and V in flight
 // per lane, within 128 VGPRs, so that a SIMD holds four wavefronts and a
-// compute unit two workgroups (on the Qwen3-shaped batch this measured 3.5%
-// faster than four wavefronts with eight steps each: the same bytes in flight
-// per workgroup, and the same two-round longest-first dispatch).
+// compute unit two workgroups (on the Qwen3-shaped batch, when it ran here,
+// this measured 3.5% faster than four wavefronts with eight steps each: the
+// same bytes in flight per workgroup, and the same two-round longest-first
+// dispatch).
 // G = 4 or 8 (head_dim 64; at head_dim 128 the matrix-core kernel runs):
 // four wavefronts, four steps, two wavefronts per SIMD.
 // Wavefronts per decode_mfma_kernel workgroup: eight when a workgroup streams
@@ -536,11 +538,14 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
 template <int DT, int BS, int G, int NW, bool ROPE>
 __global__ void decode_mfma_kernel(const DecodeArgs a);
 
-// Matrix cores take the score/value products once a KV head serves 4 or more
-// query heads (head_dim 128); below that the fp32 vector path is faster.
+// Matrix cores take the score/value products once a KV head serves 2 or more
+// query heads (head_dim 128): the matrix-core kernel's whole-row loads then
+// stream faster than the vector kernel even with 14 of its 16 MFMA columns
+// idle (Qwen3-shaped batch, G = 2: 98.6 -> 95.5 us per step).  With one query
+// head per KV head the vector kernel keeps it (6.4 TB/s on uniform contexts).
 template <int D, int G>
 constexpr bool decode_uses_mfma() {
-  return D == 128 && G >= 4;
+  return D == 128 && G >= 2;
 }
 
 template <int DT, int D, int BS, int G, bool ROPE>

@@ -1,4 +1,4 @@
-// Paged-attention decode on matrix cores, for 4..16 query heads per KV head.
+// Paged-attention decode on matrix cores, for 2..16 query heads per KV head.
 //
 // Same computation, inputs, outputs and partition scheme as
 // decode_partition_kernel (decode_impl.h): out[i][h] = softmax(scale q K^T) V
