@@ -16,10 +16,15 @@
 // taken round-robin, scores S^T = K Q^T on 16x16x32 MFMA and O^T += V^T P^T on
 // 16x16x16 MFMA from a transposed LDS tile, a merge of the wavefronts through
 // LDS.  What differs:
-//   * a key row is D bytes: lane (key col, quad) loads the D / 4 contiguous
-//     bytes of dims (D / 4) quad .. + D / 4 - 1 and MFMA step ks (of D / 32)
-//     takes dims (D / 4) quad + 8 ks .. + 7; the query fragments follow the
-//     same dim order (a dot product does not depend on the order of its terms);
+//   * a key row is D bytes.  Key rows are loaded whole, like value rows
+//     (1024 / D rows per load instruction), and staged in the wavefront's LDS
+//     K tile as codes; lane (key col, quad) reads back the D / 4 codes of dims
+//     (D / 4) quad .. + D / 4 - 1 and MFMA step ks (of D / 32) takes dims
+//     (D / 4) quad + 8 ks .. + 7; the query fragments follow the same dim
+//     order (a dot product does not depend on the order of its terms).
+//     (Loading those operand slices straight from the cache, 16 rows a quarter
+//     of a line each per instruction, streamed 14% slower: 4.9 TB/s with no
+//     arithmetic at all on the Qwen3-shaped batch);
 //   * key codes are exact in fp16 and bf16 (|code| <= 127), so each is
 //     converted in registers to the query's 16-bit type and the key scale
 //     multiplies the fp32 score;
@@ -54,6 +59,20 @@ __device__ __forceinline__ int i8_vswz(int r) {
     return (2 * r) & 15;
   } else {
     return ((r >> 1) ^ (r & 2)) & 7;
+  }
+}
+
+// Swizzle of the 16-byte chunks of a K code row in LDS (D bytes, D / 16
+// chunks): chunk c of row r is stored at c ^ i8_kswz<D>(r), so that the score
+// operand reads (16 rows, one chunk each per 16 lanes) touch 16 distinct bank
+// groups: a 128-byte row puts rows r and r + 2 in the same half of the banks,
+// a 64-byte row rows r and r + 4 in the same quarter.
+template <int D>
+__device__ __forceinline__ int i8_kswz(int r) {
+  if constexpr (D == 128) {
+    return (r ^ (r >> 3)) & 7;
+  } else {
+    return (r >> 2) & 3;
   }
 }
 
@@ -102,6 +121,7 @@ void decode_int8_kernel(const DecodeArgs a) {
   // One V buffer of 32 rows per wavefront; at the end the same bytes hold that
   // wavefront's fp32 O^T (16 heads x D dims) for the merge.
   __shared__ __attribute__((aligned(16))) unsigned char s_v[NW][kI8StepKeys * ROW];
+  __shared__ __attribute__((aligned(16))) unsigned char s_k[NW][kI8StepKeys * D];  // raw K codes
   __shared__ float s_ml[NW * 16 * 2];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -170,12 +190,13 @@ void decode_int8_kernel(const DecodeArgs a) {
   const uint32_t one2 = pack2<DT>(1.f, 1.f);
   const u32x2 ones = {one2, one2};
   unsigned char* const sv = s_v[wave];
+  unsigned char* const sk = s_k[wave];
   // Two register sets of codes and scales: the steps s + 4 and s + 8 of a
   // wavefront are in flight while step s computes.  ksc: the key scales of
   // keys 4 quad .. + 3 of each group (the keys whose scores this lane holds);
   // vrs: the value scale of the V row this lane stages (see store_v).
   struct Regs {
-    u32x4 kr[2][KC], vr[2][NJ], ksc[2];
+    u32x4 kr[2][NJ], vr[2][NJ], ksc[2];
     float vrs[2][NJ];
   };
   Regs ra, rb;
@@ -201,9 +222,12 @@ void decode_int8_kernel(const DecodeArgs a) {
       const __amdgpu_buffer_rsrc_t rks = make_rsrc(ksbase + soff, snrec);
       const __amdgpu_buffer_rsrc_t rvs = make_rsrc(vsbase + soff, snrec);
 #pragma unroll
-      for (int j = 0; j < KC; ++j)
+      for (int j = 0; j < NJ; ++j) {
+        const int kr_row = RPLV * j + lane / LPRV;
         r.kr[gr][j] = buffer_load16<kCachePolicyNT>(
-            rk, (uint32_t)col * row_bytes + (uint32_t)((D / 4) * quad + 16 * j));
+            rk, (uint32_t)kr_row * row_bytes +
+                    (uint32_t)(((lane % LPRV) ^ i8_kswz<D>(16 * gr + kr_row)) * 16));
+      }
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
         r.vr[gr][j] = buffer_load16<kCachePolicyNT>(
@@ -238,13 +262,35 @@ void decode_int8_kernel(const DecodeArgs a) {
       }
   };
 
-  auto scores = [&](const Regs& r, f32x4 (&sc)[2], f32x4 (&kscale)[2]) {
+  // K code rows to this wavefront's LDS tile as loaded (row 16 gr + RPLV j +
+  // lane / LPRV, chunk position lane % LPRV), and back as score operands: lane
+  // (key col, quad) takes chunks KC quad .. + KC - 1 of key 16 gr + col, dims
+  // (D / 4) quad .. + D / 4 - 1.
+  auto store_k = [&](const Regs& r) {
+#pragma unroll
+    for (int gr = 0; gr < 2; ++gr)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        *reinterpret_cast<u32x4*>(sk + (16 * gr + RPLV * j + lane / LPRV) * D + (lane % LPRV) * 16) =
+            r.kr[gr][j];
+  };
+  auto load_kq = [&](u32x4 (&kq)[2][KC]) {
+#pragma unroll
+    for (int gr = 0; gr < 2; ++gr) {
+      const int row = 16 * gr + col;
+#pragma unroll
+      for (int j = 0; j < KC; ++j)
+        kq[gr][j] = *reinterpret_cast<const u32x4*>(sk + row * D + ((KC * quad + j) ^ i8_kswz<D>(row)) * 16);
+    }
+  };
+
+  auto scores = [&](const u32x4 (&kq)[2][KC], const Regs& r, f32x4 (&sc)[2], f32x4 (&kscale)[2]) {
 #pragma unroll
     for (int gr = 0; gr < 2; ++gr) {
       sc[gr] = f32x4{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 w = r.kr[gr][ks >> 1];
+        const u32x4 w = kq[gr][ks >> 1];
         const u32x4 kf = (ks & 1) ? i8_to_16<DT>(w.z, w.w) : i8_to_16<DT>(w.x, w.y);
         sc[gr] = mfma16x16x32<DT>(kf, qf[ks], sc[gr]);
       }
@@ -308,9 +354,12 @@ void decode_int8_kernel(const DecodeArgs a) {
   }
   auto step = [&](int s, Regs& r) {
     const int32_t ids_after = load_ids(s + 3 * NW);
+    store_k(r);
     store_v(r);
+    u32x4 kq[2][KC];
+    load_kq(kq);
     f32x4 sc[2], kscale[2];
-    scores(r, sc, kscale);
+    scores(kq, r, sc, kscale);
     issue(s + 2 * NW, ids_next, r);
     ids_next = ids_after;
     accumulate(sc, kscale, t0 + kI8StepKeys * s, t1c);
@@ -365,14 +414,16 @@ void decode_int8_kernel(const DecodeArgs a) {
       *reinterpret_cast<uint2*>(codes + srow * D + 8 * qsub) = make_uint2(pk[0], pk[1]);
       if (qsub == 0) (is_v ? a.v_scales_w : a.k_scales_w)[srow] = qscale;
     }
-    // Registers of the one-key step, laid out as issue() loads a cached step:
-    // key 0 of group 0 is the new token.  Its key codes, dims (D / 4) quad ..
-    // + D / 4 - 1, go to the lanes with col 0 (from quantising lanes KS quad ..
-    // KS quad + KS - 1, 8 codes each); its value codes, dims 16 (lane % LPRV)
-    // .. + 15, and its value scale to lanes 0 .. LPRV - 1 (from lanes LPRN +
-    // 2 (lane % LPRV) and the next); its key scale to the quad-0 lanes.
+    // Registers of the one-key step, key 0 of group 0 being the new token: its
+    // key codes in the score-operand layout load_kq returns (dims (D / 4) quad
+    // .. + D / 4 - 1 on the lanes with col 0, from quantising lanes KS quad ..
+    // KS quad + KS - 1, 8 codes each); as issue() loads a cached step, its
+    // value codes, dims 16 (lane % LPRV) .. + 15, and its value scale to lanes
+    // 0 .. LPRV - 1 (from lanes LPRN + 2 (lane % LPRV) and the next); its key
+    // scale to the quad-0 lanes.
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
     Regs rn;
+    u32x4 kqn[2][KC];
     uint32_t kw[4 * KC], vw[4];
 #pragma unroll
     for (int k = 0; k < 4 * KC; ++k) kw[k] = (uint32_t)__shfl((int)pk[k & 1], KS * quad + (k >> 1));
@@ -382,8 +433,8 @@ void decode_int8_kernel(const DecodeArgs a) {
     const float ksn = __shfl(qscale, 0), vsn = __shfl(qscale, LPRN);
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
-      rn.kr[0][j] = col == 0 ? u32x4{kw[4 * j], kw[4 * j + 1], kw[4 * j + 2], kw[4 * j + 3]} : zero4;
-      rn.kr[1][j] = zero4;
+      kqn[0][j] = col == 0 ? u32x4{kw[4 * j], kw[4 * j + 1], kw[4 * j + 2], kw[4 * j + 3]} : zero4;
+      kqn[1][j] = zero4;
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -396,7 +447,7 @@ void decode_int8_kernel(const DecodeArgs a) {
     rn.ksc[1] = zero4;
     store_v(rn);
     f32x4 sc[2], kscale[2];
-    scores(rn, sc, kscale);
+    scores(kqn, rn, sc, kscale);
     accumulate(sc, kscale, L - 1, L);
   }
 
