@@ -271,17 +271,33 @@ void prefill_kernel(const PrefillArgs a) {
     // Matrix phases run at raised wave priority: of the two wavefronts sharing
     // a SIMD, the one with MFMAs ready issues first and the other's softmax
     // (vector ALU) fills in behind it.
+    // The first half's operands are all read before its first product, and the
+    // second half's are read behind the first half's products, so only the
+    // first read's latency is exposed.
     f32x16 s[2];
     __builtin_amdgcn_s_setprio(1);
+    u32x4 kf[2][D / 16];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      s[sub] = f32x16{};
+    for (int ks = 0; ks < D / 16; ++ks) kf[0][ks] = *reinterpret_cast<const u32x4*>(lds + koff[ks]);
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(lds + koff[ks] + sub * 32 * ROW);
-        s[sub] = mfma32x32x16<DT>(kf, qf[ks], s[sub]);
-      }
+    for (int ks = 0; ks < D / 16; ++ks) {
+      kf[1][ks] = *reinterpret_cast<const u32x4*>(lds + koff[ks] + 32 * ROW);
+      s[0] = mfma32x32x16<DT>(kf[0][ks], qf[ks], s[0]);
     }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) s[1] = mfma32x32x16<DT>(kf[1][ks], qf[ks], s[1]);
+    // That order, pinned (the scheduler would otherwise read each operand just
+    // before its product): D / 16 LDS reads, then D / 16 (product, read) pairs,
+    // then the second half's D / 16 products.
+    __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
     __builtin_amdgcn_s_setprio(0);
     // ---- mask, online softmax (this lane's query; partner lane l ^ 32).  Only
     // tiles that cross some row's causal limit need the mask.  The scale is
