@@ -37,6 +37,8 @@
 // half of the keys and are added once at the end).
 #pragma once
 
+#include <type_traits>
+
 #include "mfma.h"
 #include "pa_device.h"
 #include "pa_kernels.h"
@@ -210,27 +212,29 @@ void prefill_kernel(const PrefillArgs a) {
     const int key0 = (64 * w + lane) * NK + 16 * wave;
     return bt[min(key0 / BS, nblk_last)];
   };
-  auto stage = [&](int kv0, int buf, int32_t ids) {
+  // KIND 0: the K rows, 1: the V rows of the tile at key kv0, into buffer buf.
+  auto stage = [&](auto kind, int kv0, int buf, int32_t ids) {
+    constexpr int KIND = decltype(kind)::value;
     const int key0 = kv0 + 16 * wave;
     const int lb = key0 / BS;
     const int32_t blk = __builtin_amdgcn_readlane(ids, (kv0 / NK) & 63);
     const int nvalid = min(16, L - key0);
     const bool ok = nvalid > 0 && blk >= 0 && blk < nb32;
-    report_index_error(a.index_errors, nvalid > 0 && !ok, kErrBlockId, blk);
+    if (KIND == 0) report_index_error(a.index_errors, nvalid > 0 && !ok, kErrBlockId, blk);
     const uint64_t boff = ok ? (uint64_t)(uint32_t)blk * block_bytes +
                                    (uint64_t)(key0 - lb * BS) * row_bytes
                              : 0ull;
     const uint32_t nrec = ok ? (uint32_t)(nvalid - 1) * row_bytes + D * 2 : 0u;
-    const u32x4 rk = rsrc_words(kbase + boff, nrec);
-    const u32x4 rv = rsrc_words(vbase + boff, nrec);
+    const u32x4 rs = rsrc_words((KIND == 0 ? kbase : vbase) + boff, nrec);
 #pragma unroll
     for (int i = 0; i < 16 / RPL; ++i) {
       const int r = RPL * i + srow;  // 0..15, also the tile row modulo 16
       const uint32_t voff = (uint32_t)r * row_bytes + (uint32_t)(((lane % CPR) ^ swz<D>(r)) * 16);
-      lds_dma16(rk, lds_offset(s_kv[buf][0] + (16 * wave + RPL * i) * ROW), voff);
-      lds_dma16(rv, lds_offset(s_kv[buf][1] + (16 * wave + RPL * i) * ROW), voff);
+      lds_dma16(rs, lds_offset(s_kv[buf][KIND] + (16 * wave + RPL * i) * ROW), voff);
     }
   };
+  using KRows = std::integral_constant<int, 0>;
+  using VRows = std::integral_constant<int, 1>;
 
   // Operand addressing inside a tile.
   //   S^T = K Q^T, A operand: key row 32 sub + l % 32, dims 16 ks + 8 half .. + 7.
@@ -266,45 +270,44 @@ void prefill_kernel(const PrefillArgs a) {
   for (int o2 = 32; o2 >= 1; o2 >>= 1) wave_min_vis = min(wave_min_vis, __shfl_xor(wave_min_vis, o2));
   wave_min_vis = __builtin_amdgcn_readfirstlane(wave_min_vis);
 
-  auto compute = [&](int kv0) {
-    // ---- S^T for the tile's two 32-key halves
-    // Matrix phases run at raised wave priority: of the two wavefronts sharing
-    // a SIMD, the one with MFMAs ready issues first and the other's softmax
-    // (vector ALU) fills in behind it.
-    // The first half's operands are all read before its first product, and the
-    // second half's are read behind the first half's products, so only the
-    // first read's latency is exposed.
-    f32x16 s[2];
-    __builtin_amdgcn_s_setprio(1);
+  // ---- S^T of the tile whose K rows koff addresses, both 32-key halves,
+  // their products alternating so that no product waits for the one before
+  // it; the operands of D / 32 dim steps are read ahead of the first product
+  // (with the order pinned by the caller, see pin_scores).
+  auto scores = [&](f32x16 (&sc)[2]) {
+    constexpr int AHEAD = D / 32;
     u32x4 kf[2][D / 16];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) kf[0][ks] = *reinterpret_cast<const u32x4*>(lds + koff[ks]);
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+    for (int ks = 0; ks < AHEAD; ++ks) {
+      kf[0][ks] = *reinterpret_cast<const u32x4*>(lds + koff[ks]);
+      kf[1][ks] = *reinterpret_cast<const u32x4*>(lds + koff[ks] + 32 * ROW);
+    }
+    sc[0] = f32x16{};
+    sc[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      kf[1][ks] = *reinterpret_cast<const u32x4*>(lds + koff[ks] + 32 * ROW);
-      s[0] = mfma32x32x16<DT>(kf[0][ks], qf[ks], s[0]);
+      if (ks + AHEAD < D / 16) {
+        kf[0][ks + AHEAD] = *reinterpret_cast<const u32x4*>(lds + koff[ks + AHEAD]);
+        kf[1][ks + AHEAD] = *reinterpret_cast<const u32x4*>(lds + koff[ks + AHEAD] + 32 * ROW);
+      }
+      sc[0] = mfma32x32x16<DT>(kf[0][ks], qf[ks], sc[0]);
+      sc[1] = mfma32x32x16<DT>(kf[1][ks], qf[ks], sc[1]);
     }
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) s[1] = mfma32x32x16<DT>(kf[1][ks], qf[ks], s[1]);
-    // That order, pinned (the scheduler would otherwise read each operand just
-    // before its product): D / 16 LDS reads, then D / 16 (product, read) pairs,
-    // then the second half's D / 16 products.
+  };
+  // scores() alone: D / 16 LDS reads, then (2 products, 2 reads) while reads
+  // remain, then the last products.
+  auto pin_scores = [&]() {
     __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (ks + D / 32 < D / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
-    __builtin_amdgcn_s_setprio(0);
-    // ---- mask, online softmax (this lane's query; partner lane l ^ 32).  Only
-    // tiles that cross some row's causal limit need the mask.  The scale is
-    // positive, so the maximum is taken over raw scores and folded into the
-    // exponent.  O and l are rescaled only when some row's maximum grows by
-    // more than kLazyRescale (log2 units); until then p <= 2^kLazyRescale,
-    // harmless in fp32 and in the 16-bit P.
+  };
+
+  // ---- causal mask of the tile at key kv0 (this lane's query).  Only tiles
+  // that cross some row's limit need it.
+  auto mask = [&](f32x16 (&sc)[2], int kv0) {
     if (kv0 + NK > wave_min_vis) {
       // key kv0 + 4 half + c (c = 32 sub + 8 (j / 4) + j % 4) is visible iff c < lim
       const int lim = vis - kv0 - 4 * half;
@@ -313,35 +316,47 @@ void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int c = sub * 32 + 8 * (j >> 2) + (j & 3);
-          s[sub][j] = c < lim ? s[sub][j] : -__builtin_inff();
+          sc[sub][j] = c < lim ? sc[sub][j] : -__builtin_inff();
         }
       }
     }
+  };
+
+  // ---- online softmax of a masked tile, in place, without a branch: the
+  // row maximum (this lane and its partner l ^ 32), the lazy update of m
+  // (only when some row's maximum grows by more than kLazyRescale, in log2
+  // units; until then p <= 2^kLazyRescale, harmless in fp32 and in the 16-bit
+  // P), and p = 2^(s scale_log2 - m).  The scale is positive, so the maximum is
+  // taken over raw scores and folded into the exponent.  Returns the factor
+  // O and l must be rescaled by (1 when m did not move) and whether it moved.
+  auto softmax = [&](f32x16 (&sc)[2], bool& moved) -> float {
     float mx = -__builtin_inff();
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[sub][j]);
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[sub][j]);
     }
     mx = max_xor32(mx) * a.scale_log2;  // partner lane l ^ 32, by a lane swap
-    if (__builtin_amdgcn_read_exec() & __builtin_amdgcn_ballot_w64(mx > m + kLazyRescale)) {
-      const float m_new = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - m_new);
-      m = m_new;
-      lpart *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-    }
+    moved = (__builtin_amdgcn_read_exec() & __builtin_amdgcn_ballot_w64(mx > m + kLazyRescale)) != 0;
+    const float m_new = moved ? fmaxf(m, mx) : m;
+    const float alpha = fast_exp2(m - m_new);
+    m = m_new;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) s[sub][j] = fast_exp2(fmaf(s[sub][j], a.scale_log2, -m));
+      for (int j = 0; j < 16; ++j) sc[sub][j] = fast_exp2(fmaf(sc[sub][j], a.scale_log2, -m));
     }
+    return alpha;
+  };
+
+  // ---- O^T += V^T P^T over the tile's four 16-key steps (V rows at vlo/vhi),
+  // and the row sum of the same rounded P.  Raised wave priority: of the two
+  // wavefronts sharing a SIMD, the one with products ready issues first.
+  auto pv = [&](const f32x16 (&sc)[2]) {
     __builtin_amdgcn_s_setprio(1);
-    // ---- O^T += V^T P^T over the tile's four 16-key steps
 #pragma unroll
     for (int kk = 0; kk < NK / 16; ++kk) {
-      const f32x16& ps = s[kk >> 1];
+      const f32x16& ps = sc[kk >> 1];
       const int jb = 8 * (kk & 1);
       const u32x4 pf = {pack2<DT>(ps[jb + 0], ps[jb + 1]), pack2<DT>(ps[jb + 2], ps[jb + 3]),
                         pack2<DT>(ps[jb + 4], ps[jb + 5]), pack2<DT>(ps[jb + 6], ps[jb + 7])};
@@ -356,38 +371,94 @@ void prefill_kernel(const PrefillArgs a) {
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // ---- pipeline: tile i+1 streams into the other buffer while tile i
-  // computes; the copies are waited for only at the end of the iteration.
-  // Block ids of the next window of 64 tiles are loaded a window ahead.
+  // ---- pipeline.  Tile i's K and V rows live in buffer i & 1, but in
+  // different iterations: iteration i computes S^T of tile i + 1 (its K) while
+  // the vector ALU runs tile i's softmax, then tile i's value product (its V).
+  // So at the top of iteration i, after one barrier, K of tile i + 2 streams
+  // into the buffer tile i's K leaves and V of tile i + 1 into the one tile
+  // i - 1's V leaves, each with a whole iteration to arrive.  Block ids come
+  // lane-parallel in windows of 64 tiles, loaded a window ahead (one set for
+  // the K stream, one for the V stream).
   const int ntiles = (kv_end + NK - 1) / NK;
-  int32_t ids_cur = 0, ids_nxt = 0;
+  const int nw = min(ntiles, (wave_end + NK - 1) / NK);  // tiles this wavefront computes
+  int32_t idk = 0, idk_n = 0, idv = 0, idv_n = 0;
   if (ntiles > 0) {
-    ids_cur = load_ids(0);
-    ids_nxt = load_ids(1);
-    stage(0, 0, ids_cur);
+    idk = load_ids(0);
+    idk_n = load_ids(1);
+    idv = idk;
+    idv_n = idk_n;
+    stage(KRows{}, 0, 0, idk);
+    if (ntiles > 1) stage(KRows{}, NK, 1, idk);
+    stage(VRows{}, 0, 0, idv);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int kv0 = it * NK;
-    if (it + 1 < ntiles) {
-      if (((it + 1) & 63) == 0) {
-        ids_cur = ids_nxt;
-        ids_nxt = load_ids(((it + 1) >> 6) + 1);
-      }
-      stage(kv0 + NK, (it + 1) & 1, ids_cur);
-    }
-    if (kv0 < wave_end) compute(kv0);
-    const int32_t flip = (it & 1) ? -kBuf : kBuf;   // next tile is in the other buffer
+  f32x16 sa[2], sb[2];
+  if (nw > 0) {
+    scores(sa);
+    pin_scores();
+  }
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) koff[ks] += flip;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      vlo[dt] += flip;
-      vhi[dt] += flip;
-    }
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] += kBuf;  // K of tile 1
+
+  // One iteration: sc holds tile it's raw scores, sn receives tile it + 1's.
+  auto iteration = [&](int it, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (it + 2 < ntiles) {
+      if (((it + 2) & 63) == 0) {
+        idk = idk_n;
+        idk_n = load_ids(((it + 2) >> 6) + 1);
+      }
+      stage(KRows{}, (it + 2) * NK, it & 1, idk);
+    }
+    if (it + 1 < ntiles) {
+      if (((it + 1) & 63) == 0) {
+        idv = idv_n;
+        idv_n = load_ids(((it + 1) >> 6) + 1);
+      }
+      stage(VRows{}, (it + 1) * NK, (it + 1) & 1, idv);
+    }
+    if (it < nw) {
+      mask(sc, it * NK);
+      bool moved;
+      float alpha;
+      if (it + 1 < nw) {
+        scores(sn);
+        alpha = softmax(sc, moved);
+        // Interleave: the next tile's D / 8 products run on the matrix cores
+        // while this tile's softmax issues on the vector ALU between them.
+        __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 1);
+        __builtin_amdgcn_sched_group_barrier(0x402, 10, 1);
+#pragma unroll
+        for (int k = 0; k < D / 8; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x402, 6, 1);
+          if ((k & 1) && k / 2 + D / 32 < D / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+      } else {
+        alpha = softmax(sc, moved);
+      }
+      if (moved) {
+        lpart *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+      }
+      pv(sc);
+    }
+    // next iteration: K of tile it + 2 (buffer it & 1), V of tile it + 1
+    const int32_t kflip = (it & 1) ? kBuf : -kBuf;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) koff[ks] += kflip;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      vlo[dt] -= kflip;
+      vhi[dt] -= kflip;
+    }
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    iteration(it, sa, sb);
+    if (it + 1 < ntiles) iteration(it + 1, sb, sa);
   }
 
   // ---- normalise and store: lane holds dims 32 dt + 8 (j/4) + 4 half + (j%4)
