@@ -85,13 +85,15 @@ def test_stop_event_follows_the_last_kernel_across_calls():
 
 def test_flush_end_to_call_end_brackets_the_call():
     """Stop events at the end of a flush and of the call after it: their interval holds the
-    call's kernels (no shorter than start-to-stop events of the same call) and little else."""
+    call's kernels (no shorter than start-to-stop events of the same call) and little else.
+    The flush reads 1 GiB (about 180 us), so the host has enqueued the call before it ends;
+    the first round, which pays first-use costs on the host, is not checked."""
     d, call = _decode_case(0)
     out = torch.empty_like(d.q)
-    buf = torch.zeros(256 << 20, dtype=torch.uint8, device="cuda")
+    buf = torch.zeros(1 << 30, dtype=torch.uint8, device="cuda")
     fe, ks, ke = _events(3)
     spans, kern = [], []
-    for _ in range(6):
+    for _ in range(7):
         pa_set_kernel_events(None, fe)
         try:
             pa_cache_flush(buf)
@@ -104,7 +106,7 @@ def test_flush_end_to_call_end_brackets_the_call():
         kern.append(ks.elapsed_time(ke))
     log("flush end to call end " + ", ".join(f"{x * 1e3:.1f}" for x in spans) +
         " us; call start to end " + ", ".join(f"{x * 1e3:.1f}" for x in kern) + " us")
-    for s, k in zip(spans, kern):
+    for s, k in zip(spans[1:], kern[1:]):
         assert s >= k - 1e-3 and s < k + 0.05
 
 
