@@ -507,14 +507,15 @@ hipError_t launch_int8_t(const DecodeArgs& a, int phases, hipStream_t s) {
     return hipGetLastError();
   }
   // Wavefronts per workgroup: eight for spans of kMfmaLongSpan+ tokens (as for the
-  // 16-bit matrix-core kernel); two for contexts cut into partitions of at most
-  // kMfmaShortPartition tokens, so that each wavefront takes more steps of its
-  // short partition (long split-K INT8 decode at 512: 100.3 -> 96.4 us; unsplit
-  // contexts of up to 2048 tokens lose with two: 62.1 -> 67.5 us); four otherwise.
+  // 16-bit matrix-core kernel); one for contexts cut into partitions of at most
+  // kMfmaShortPartition tokens, so that a wavefront takes all steps of its short
+  // partition and no merge of wavefronts follows (long split-K INT8 decode at
+  // 512: four 100.3, two 96.4 then 98.9, one 96.0 us; unsplit contexts of up to
+  // 2048 tokens lose with two: 62.1 -> 67.5 us); four otherwise.
   if (a.part_tokens >= kMfmaLongSpan) {
     launch((decode_int8_kernel<DT, D, BS, G, 8>), dim3(grid), dim3(512), 0, s, a);
   } else if (a.num_parts > 1 && a.part_tokens <= kMfmaShortPartition) {
-    launch((decode_int8_kernel<DT, D, BS, G, 2>), dim3(grid), dim3(128), 0, s, a);
+    launch((decode_int8_kernel<DT, D, BS, G, 1>), dim3(grid), dim3(64), 0, s, a);
   } else {
     launch((decode_int8_kernel<DT, D, BS, G, 4>), dim3(grid), dim3(256), 0, s, a);
   }
