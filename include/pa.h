@@ -130,7 +130,8 @@ int pa_take_index_errors(void* stream, uint32_t* kinds, uint32_t* first_kind,
  * events as they were.  The events stay the caller's and must outlive the
  * launches that record them.  Stop events armed around two calls in turn give,
  * by hipEventElapsedTime, the device time from the end of the first call's
- * last kernel to the end of the second's.
+ * last kernel to the end of the second's.  Launches into a stream that is
+ * being captured into a HIP graph record no events.
  *
  * pa_cache_flush reads `bytes` bytes of the device buffer `buf` (address and
  * size multiples of 16) on `stream` and writes nothing: read through a buffer

@@ -209,7 +209,9 @@ template <typename... KArgs, typename... Args>
 inline void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds_bytes,
                    hipStream_t s, Args... args) {
   KernelEvents& ev = kernel_events();
-  if (ev.stop == nullptr) {
+  hipStreamCaptureStatus capturing = hipStreamCaptureStatusNone;
+  if (ev.stop != nullptr) (void)hipStreamIsCapturing(s, &capturing);
+  if (ev.stop == nullptr || capturing != hipStreamCaptureStatusNone) {  // no events in a graph
     hipLaunchKernelGGL(kernel, grid, block, lds_bytes, s, args...);
     return;
   }

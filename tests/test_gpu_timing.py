@@ -125,3 +125,29 @@ def test_arming_a_start_event_alone_is_rejected():
     with pytest.raises(PAError):
         pa_set_kernel_events(ks, None)
     pa_set_kernel_events()
+
+
+def test_armed_events_stay_out_of_a_graph_capture():
+    """A call captured into a HIP graph while events are armed launches normally: the
+    capture succeeds, the events are not recorded by the replays, and the replays give the
+    eager result."""
+    d, call = _decode_case(0)
+    ref = torch.empty_like(d.q)
+    call(ref)
+    out = torch.zeros_like(d.q)
+    ks, ke = _events(2)
+    torch.cuda.synchronize()
+    before = ks.elapsed_time(ke)
+    graph = torch.cuda.CUDAGraph()
+    pa_set_kernel_events(ks, ke)
+    try:
+        with torch.cuda.graph(graph):
+            call(out)
+    finally:
+        pa_set_kernel_events()
+    for _ in range(3):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(out), to_bits(ref))
+    assert ks.elapsed_time(ke) == before
