@@ -67,6 +67,23 @@ def test_bit_exact_against_oracle(dt, D, BS, with_q):
     assert np.array_equal(got[2], ref[2])
 
 
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("f16", 64)])
+def test_long_chunk_odd_count_with_skipped_rows(dt, D):
+    """A chunk of 2048+ tokens, where workgroups take two tokens each: an odd count leaves the
+    last workgroup one token short, and rows to skip fall on both tokens of a pair."""
+    rng = np.random.default_rng(9950 + D)
+    T, Hq, Hkv, NB, BS, P = 2051, 8, 2, 160, 16, 8192
+    q, k, v = _rows(rng, (T, Hq, D), dt), _rows(rng, (T, Hkv, D), dt), _rows(rng, (T, Hkv, D), dt)
+    cos, sin = rope_tables(P, D)
+    pos = rng.integers(0, P, T)
+    pos[[0, 7, 1000, 1001, T - 1]] = [P, -1, -7, P + 5, P]        # outside the table
+    slots = rng.permutation(NB * BS)[:T].astype(np.int64)
+    slots[[1, 6, 1001, 2048, T - 2]] = [-1, NB * BS, -1, NB * BS + 9, -1]
+    got, ref = run_both(q, k, v, pos, slots, cos, sin, NB, BS, dt)
+    for g, r in zip(got, ref):
+        assert np.array_equal(g, r)
+
+
 def test_quarter_turns_and_special_values():
     """Exact angles give exact results; infinities and NaNs travel as the arithmetic says."""
     dt, D, T, Hkv, NB, BS = "bf16", 128, 8, 2, 4, 16
