@@ -617,8 +617,8 @@ def secondary_entry(pa, torch, entry, dev, timer):
             "merge_us": _stats_us(r2["merge_ms"]),
             "merge_GBps": round(r2["merge_bytes"] / (float(np.mean(r2["merge_ms"])) * 1e-3) / 1e9, 2),
             "roofline": _hbm_roofline(f"pa_decode_partial ({kern})", kb, r2["partial_ms"],
-                                      traffic_from(f"decode_{name}_cp{ns}_counters.md",
-                                                   KERNEL_SOURCES))}
+                                      traffic_from(f"decode_{name}_cp{ns}_p{r2['partition_size']}"
+                                                   "_counters.md", KERNEL_SOURCES))}
     if variant == "graph":
         r2 = run_graph(pa, torch, b2, n, 10, dev, timer)
         kv2 = b2.kv_bytes()

@@ -211,7 +211,7 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int m
  * A partition_size for pa_decode / pa_decode_step suited to the current
  * device: 0 (no split) when the num_seqs * num_kv_heads (sequence, KV head)
  * pairs already give every compute unit two workgroups; otherwise a multiple
- * of block_size (at least 256) that cuts max_context_len into enough
+ * of block_size (at least 512) that cuts max_context_len into enough
  * partitions for about eight workgroups per compute unit.  Every split gives
  * the same attention up to rounding; this one trades the partitions'
  * parallelism against the partial results they write (page "vLLM-Ascend ...",

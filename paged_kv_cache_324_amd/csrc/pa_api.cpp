@@ -395,7 +395,7 @@ int pa_decode_partition_hint(int num_seqs, int num_kv_heads, int max_context_len
   const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
   if (pairs >= slots || max_context_len == 0) return 0;
   const int64_t parts = (4 * slots + pairs - 1) / pairs;  // partitions per longest context
-  int64_t p = std::max<int64_t>(256, (max_context_len + parts - 1) / parts);
+  int64_t p = std::max<int64_t>(512, (max_context_len + parts - 1) / parts);
   p = (p + block_size - 1) / block_size * block_size;
   return p >= max_context_len ? 0 : (int)p;
 }
