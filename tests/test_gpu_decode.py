@@ -70,6 +70,37 @@ def test_reshape_skips_padding_and_out_of_pool_slots():
     assert np.array_equal(to_bits(d.v_cache[d.idx]), vc)
 
 
+@pytest.mark.parametrize("Hkv,D,T", [(8, 128, 4099), (4, 128, 5001), (2, 64, 20001), (1, 64, 3333)])
+def test_reshape_ragged_multi_token_workgroups(Hkv, D, T):
+    """Token counts that leave the last workgroup partly empty when a workgroup takes
+    several tokens per thread, with padding and out-of-pool slots among them: the whole
+    pool is compared, so a stray or missing row shows."""
+    rng = np.random.default_rng(4400 + T)
+    BS = 16
+    NB = -(-(T * 13 // 10) // BS)
+    key = to_u16(rng.standard_normal((T, Hkv, D)).astype(np.float32), "bf16")
+    value = to_u16(rng.standard_normal((T, Hkv, D)).astype(np.float32), "bf16")
+    slots = rng.permutation(NB * BS)[:T].astype(np.int64)
+    bad = rng.choice(T, 12, replace=False)
+    slots[bad[:4]] = -1
+    slots[bad[4:8]] = NB * BS + np.arange(4)          # past the pool: skipped
+    slots[bad[8:]] = -(1 << 40)
+    slots[T - 1] = -1                                  # the very last token is padding
+    log(f"reshape ragged: T={T} Hkv={Hkv} D={D} NB={NB}")
+    sentinel = np.full((NB, BS, Hkv, D), 0x1234, np.uint16)
+    kc = torch.from_numpy(sentinel.view(np.int16)).cuda().view(torch.bfloat16)
+    vc = kc.clone()
+    pa_reshape_and_cache(torch.from_numpy(key.view(np.int16)).cuda().view(torch.bfloat16),
+                         torch.from_numpy(value.view(np.int16)).cuda().view(torch.bfloat16),
+                         kc, vc, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    hk, hv = sentinel.copy(), sentinel.copy()
+    sl = np.where((slots >= 0) & (slots < NB * BS), slots, -1)
+    oracle.reshape_and_cache(key, value, hk, hv, sl)
+    assert np.array_equal(to_bits(kc), hk)
+    assert np.array_equal(to_bits(vc), hv)
+
+
 def test_reshape_empty_is_noop():
     b = make_config("tiny_decode")
     d = upload(b)
