@@ -260,14 +260,29 @@ class Timer:
             torch.cuda.synchronize()
 
     def stream_read_ceiling(self):
-        """The flush itself timed back to back: a plain streaming read, as a reference rate
-        for what a read-only kernel reaches on this device; never used as a denominator."""
+        """Streaming read rates of this device, as references (never a denominator):
+        non-temporal loads over 4 GiB (pa_stream_read), the HBM read rate a kernel that
+        streams its operands once can reach; and the flush itself (plain loads, which
+        allocate cache lines) timed back to back over its buffer."""
+        big = self.torch.empty(4 << 30, dtype=self.torch.uint8, device=self.flush_buf.device)
+
+        def read():
+            self.pa.pa_stream_read(big, stream=self.stream)
+
+        for _ in range(3):
+            read()
+        ms_nt = float(np.median(self.warm(read, 10)))
+        del big
         for _ in range(3):
             self.flush()
         ms = float(np.median(self.warm(self.flush, 10)))
-        return {"kernel": f"pa_cache_flush over {self.flush_bytes >> 20} MiB (a streaming read)",
-                "GBps": round(self.flush_bytes / (ms * 1e-3) / 1e9, 1),
-                "us_p50": round(ms * 1e3, 2)}
+        return {"kernel": "pa_stream_read over 4096 MiB (non-temporal loads)",
+                "GBps": round((4 << 30) / (ms_nt * 1e-3) / 1e9, 1),
+                "us_p50": round(ms_nt * 1e3, 2),
+                "flush_read": {"kernel": f"pa_cache_flush over {self.flush_bytes >> 20} MiB "
+                                         "(plain loads)",
+                               "GBps": round(self.flush_bytes / (ms * 1e-3) / 1e9, 1),
+                               "us_p50": round(ms * 1e3, 2)}}
 
 
 # Secondary workloads run a fixed number of cold steps after a time-based warm-up,

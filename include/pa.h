@@ -139,10 +139,18 @@ int pa_take_index_errors(void* stream, uint32_t* kinds, uint32_t* first_kind,
  * clean lines of its own, so that a kernel after it finds none of its
  * operands cached.  bytes == 0 is a no-op; a NULL buffer or misaligned
  * address or size is PA_ERR_INVALID_ARG.
+ *
+ * pa_stream_read is the same read with non-temporal loads, which leave the
+ * caches' contents alone (so it is no flush): timed over a buffer several
+ * times the Infinity Cache, it gives the device's streaming read rate from
+ * HBM, the practical ceiling for kernels that stream their operands once.
+ * Same arguments and errors as pa_cache_flush.
  */
 int pa_set_kernel_events(void* start_event, void* stop_event);
 
 int pa_cache_flush(const void* buf, size_t bytes, void* stream);
+
+int pa_stream_read(const void* buf, size_t bytes, void* stream);
 
 /*
  * reshape_and_cache: write this step's new keys and values into their cache

@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     decode_workspace,
     load_library,
     pa_cache_flush,
+    pa_stream_read,
     pa_copy_blocks,
     pa_decode,
     pa_decode_int8,

@@ -56,6 +56,8 @@ def _declare(lib):
     lib.pa_set_kernel_events.argtypes = [c_vp, c_vp]
     lib.pa_cache_flush.restype = c_int
     lib.pa_cache_flush.argtypes = [c_vp, c_sz, c_vp]
+    lib.pa_stream_read.restype = c_int
+    lib.pa_stream_read.argtypes = [c_vp, c_sz, c_vp]
     lib.pa_reshape_and_cache.restype = c_int
     lib.pa_reshape_and_cache.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_int, c_int, c_int,
                                          c_i64, c_int, c_vp]
@@ -213,6 +215,15 @@ def pa_cache_flush(buf: torch.Tensor, stream=None) -> None:
     if not buf.is_contiguous():
         raise ValueError("buf must be contiguous")
     _check(load_library().pa_cache_flush(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                         _stream(buf, stream)))
+
+
+def pa_stream_read(buf: torch.Tensor, stream=None) -> None:
+    """Read all of the device tensor ``buf`` with non-temporal loads and write nothing (a
+    streaming-read rate reference; the caches' contents are left alone)."""
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    _check(load_library().pa_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(),
                                          _stream(buf, stream)))
 
 

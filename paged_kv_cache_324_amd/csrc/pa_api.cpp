@@ -316,14 +316,25 @@ int pa_set_kernel_events(void* start_event, void* stop_event) {
   return ok();
 }
 
-int pa_cache_flush(const void* buf, size_t bytes, void* stream) {
+namespace {
+int read_buffer(const void* buf, size_t bytes, bool non_temporal, void* stream) {
   if (bytes == 0) return ok();
   if (buf == nullptr) return fail(PA_ERR_INVALID_ARG, "null buffer");
   if ((reinterpret_cast<uintptr_t>(buf) & 15) != 0 || (bytes & 15) != 0)
     return fail(PA_ERR_INVALID_ARG, "buffer address and size must be multiples of 16 bytes");
   if (const int b = check_build()) return b;
-  return hip_status(pa::launch_cache_flush(buf, (int64_t)(bytes / 16), static_cast<hipStream_t>(stream)),
-                    "cache_flush launch");
+  return hip_status(pa::launch_cache_flush(buf, (int64_t)(bytes / 16), non_temporal,
+                                           static_cast<hipStream_t>(stream)),
+                    non_temporal ? "stream_read launch" : "cache_flush launch");
+}
+}  // namespace
+
+int pa_cache_flush(const void* buf, size_t bytes, void* stream) {
+  return read_buffer(buf, bytes, false, stream);
+}
+
+int pa_stream_read(const void* buf, size_t bytes, void* stream) {
+  return read_buffer(buf, bytes, true, stream);
 }
 
 int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* src, const int64_t* dst,

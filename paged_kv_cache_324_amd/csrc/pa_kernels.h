@@ -187,7 +187,7 @@ struct MergePartialsArgs {
 hipError_t launch_merge_partials(const MergePartialsArgs& a, int dtype, int head_dim,
                                  hipStream_t s);
 
-hipError_t launch_cache_flush(const void* buf, int64_t chunks, hipStream_t s);
+hipError_t launch_cache_flush(const void* buf, int64_t chunks, bool non_temporal, hipStream_t s);
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int block_size,
                           int group, hipStream_t s);

@@ -364,3 +364,7 @@ def test_kernel_events_and_cache_flush_reject_bad_arguments(lib):
     assert lib.pa_cache_flush(None, 16, None) == -1
     assert lib.pa_cache_flush(ctypes.c_void_p(0x1008), 16, None) == -1
     assert lib.pa_cache_flush(P, 24, None) == -1
+    assert lib.pa_stream_read(None, 0, None) == 0
+    assert lib.pa_stream_read(None, 16, None) == -1
+    assert lib.pa_stream_read(ctypes.c_void_p(0x1008), 16, None) == -1
+    assert lib.pa_stream_read(P, 24, None) == -1

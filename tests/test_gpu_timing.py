@@ -2,13 +2,13 @@
 their own dispatch timestamps.  A stop event armed before a call takes the end of its last
 kernel, across calls; the start event lies no later than the first kernel's start; both lie
 inside event records queued on the stream around the call; arming changes no output bit.
-pa_cache_flush: reads its buffer and writes nothing."""
+pa_cache_flush and pa_stream_read: read their buffer and write nothing."""
 import numpy as np
 import pytest
 import torch
 
 from paged_kv_cache_324_amd import (PAError, decode_workspace, pa_cache_flush, pa_decode,
-                                    pa_decode_order, pa_set_kernel_events)
+                                    pa_decode_order, pa_set_kernel_events, pa_stream_read)
 from workloads import make_batch
 
 from _gpu import log, to_bits, upload
@@ -116,6 +116,17 @@ def test_cache_flush_writes_nothing():
     pa_cache_flush(buf)
     with pytest.raises(PAError):
         pa_cache_flush(buf[:5])             # 20 bytes: not a multiple of 16
+    torch.cuda.synchronize()
+    assert torch.equal(buf, before)
+
+
+def test_stream_read_writes_nothing():
+    buf = torch.arange(1 << 22, dtype=torch.int32, device="cuda")
+    before = buf.clone()
+    pa_stream_read(buf)
+    pa_stream_read(buf[4:8])                # 16 bytes at a 16-byte offset
+    with pytest.raises(PAError):
+        pa_stream_read(buf[:5])             # 20 bytes: not a multiple of 16
     torch.cuda.synchronize()
     assert torch.equal(buf, before)
 
