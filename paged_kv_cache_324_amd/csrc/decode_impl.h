@@ -72,6 +72,14 @@ constexpr int kMfmaLongSpan = 4096;
 // (context-parallel shard at partition 256: 31.5 -> 30.8 us; long split-K at
 // 512: 165.6 -> 164.3 us).
 constexpr int kMfmaShortPartition = 512;
+// Persistent workgroups (decode_mfma_kernel's PERSIST): with eight wavefronts,
+// when the work items outnumber the compute units; with two, when they number
+// at least twice the resident workgroups.  Each workgroup then pairs long items
+// with short ones and skips a launch per item (Llama-2-shaped batches 266 ->
+// 260 / 265 -> 258 us, long split-K 150 -> 148 us).  With four wavefronts (the
+// Qwen3-shaped batch) it measured 1% slower, and a grid that is not larger than
+// the resident workgroups gains nothing from it: both keep one item per
+// workgroup.
 
 template <int G>
 struct DecodeShape {
@@ -535,7 +543,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
     reinterpret_cast<float2*>(a.out_ml)[(int64_t)seq * a.num_heads + h] = make_float2(M, den);
 }
 
-template <int DT, int BS, int G, int NW, bool ROPE>
+template <int DT, int BS, int G, int NW, bool ROPE, bool PERSIST>
 __global__ void decode_mfma_kernel(const DecodeArgs a);
 
 // Matrix cores take the score/value products once a KV head serves 2 or more
@@ -552,12 +560,20 @@ template <int DT, int D, int BS, int G, bool ROPE>
 void launch_partitions(const DecodeArgs& a, unsigned grid, hipStream_t s) {
   using Shape = DecodeShape<G>;
   if constexpr (decode_uses_mfma<D, G>()) {
+    // Workgroups resident at once: two wavefronts per SIMD, four SIMDs per unit.
+    const unsigned cus = a.num_cus > 0 ? (unsigned)a.num_cus : 256u;
     if (a.part_tokens >= kMfmaLongSpan) {
-      launch((decode_mfma_kernel<DT, BS, G, 8, ROPE>), dim3(grid), dim3(512), 0, s, a);
+      if (grid > cus)
+        launch((decode_mfma_kernel<DT, BS, G, 8, ROPE, true>), dim3(cus), dim3(512), 0, s, a);
+      else
+        launch((decode_mfma_kernel<DT, BS, G, 8, ROPE, false>), dim3(grid), dim3(512), 0, s, a);
     } else if (a.num_parts > 1 && a.part_tokens <= kMfmaShortPartition) {
-      launch((decode_mfma_kernel<DT, BS, G, 2, ROPE>), dim3(grid), dim3(128), 0, s, a);
+      if (grid >= 8 * cus)
+        launch((decode_mfma_kernel<DT, BS, G, 2, ROPE, true>), dim3(4 * cus), dim3(128), 0, s, a);
+      else
+        launch((decode_mfma_kernel<DT, BS, G, 2, ROPE, false>), dim3(grid), dim3(128), 0, s, a);
     } else {
-      launch((decode_mfma_kernel<DT, BS, G, 4, ROPE>), dim3(grid), dim3(256), 0, s, a);
+      launch((decode_mfma_kernel<DT, BS, G, 4, ROPE, false>), dim3(grid), dim3(256), 0, s, a);
     }
   } else {
     launch((decode_partition_kernel<DT, D, BS, G, Shape::waves, Shape::pf, Shape::waves_per_eu,

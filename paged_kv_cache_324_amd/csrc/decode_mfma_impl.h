@@ -62,9 +62,10 @@ __device__ __forceinline__ int md_vswz(int r) { return (2 * r) & 15; }
 // groups per 8 lanes.
 __device__ __forceinline__ int md_kswz(int r) { return r & 7; }
 
+// One work item: (partition, sequence rank, KV head) number `item` of the grid's
+// order.
 template <int DT, int BS, int G, int NW, bool ROPE>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void decode_mfma_kernel(const DecodeArgs a) {
+__device__ __forceinline__ void decode_mfma_item(const DecodeArgs& a, const int item) {
   constexpr int D = 128;
   static_assert(G >= 1 && G <= 16, "heads of a group fill the 16 MFMA columns");
   static_assert(BS % 16 == 0, "a 16-key group lies in one block");
@@ -82,8 +83,8 @@ void decode_mfma_kernel(const DecodeArgs a) {
   // second one); within a partition index, sequences in `seq_order` when one
   // is given.
   const int per_part = a.num_seqs * a.num_kv_heads;
-  const int part = blockIdx.x / per_part;
-  const int rest = blockIdx.x - part * per_part;
+  const int part = item / per_part;
+  const int rest = item - part * per_part;
   const int rank = rest / a.num_kv_heads;
   const int kvh = rest - rank * a.num_kv_heads;
   const int seq = a.seq_order ? a.seq_order[rank] : rank;
@@ -399,6 +400,26 @@ void decode_mfma_kernel(const DecodeArgs a) {
     accumulate(sc, L - 1, L);
   }
   merge();
+}
+
+// One work item per workgroup, or (PERSIST) a grid of W workgroups each taking
+// items b, 2W - 1 - b, 2W + b, 4W - 1 - b, ...: in the longest-first order that
+// pairs long items with short ones, and saves a workgroup launch per item.
+template <int DT, int BS, int G, int NW, bool ROPE, bool PERSIST>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_mfma_kernel(const DecodeArgs a) {
+  if constexpr (!PERSIST) {
+    decode_mfma_item<DT, BS, G, NW, ROPE>(a, (int)blockIdx.x);
+  } else {
+    const int n = a.num_seqs * a.num_kv_heads * a.num_parts;
+    const int W = (int)gridDim.x;
+    for (int k = 0;; ++k) {
+      const int item = (k & 1) ? (k + 1) * W - 1 - (int)blockIdx.x : k * W + (int)blockIdx.x;
+      if (item >= n) break;
+      decode_mfma_item<DT, BS, G, NW, ROPE>(a, item);
+      __syncthreads();  // the next item reuses the LDS buffers
+    }
+  }
 }
 
 }  // namespace pa

@@ -532,6 +532,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.max_context_len = max_context_len;
   a.num_parts = (int)parts;
   a.part_tokens = parts > 1 ? partition_size : (max_context_len > 0 ? max_context_len : 1);
+  a.num_cus = device_cus();
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   const int group = num_heads / num_kv_heads;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -130,6 +130,7 @@ struct DecodeArgs {
   int max_context_len;
   int num_parts;       // partitions per sequence in the grid
   int part_tokens;     // tokens per partition (>= every context when unsplit)
+  int num_cus;         // compute units of the device: how many workgroups fit at once
   float scale_log2;    // scale * log2(e)
   IndexErrors* index_errors;  // PA_CHECK_INDICES builds only; null otherwise
 };
@@ -241,7 +242,7 @@ constexpr uint64_t args_layout() {
       offsetof(CopyBlocksArgs, index_errors),
       sizeof(DecodeArgs), offsetof(DecodeArgs, q), offsetof(DecodeArgs, part_out),
       offsetof(DecodeArgs, key_new), offsetof(DecodeArgs, k_scales), offsetof(DecodeArgs, positions),
-      offsetof(DecodeArgs, num_slots), offsetof(DecodeArgs, num_seqs),
+      offsetof(DecodeArgs, num_slots), offsetof(DecodeArgs, num_seqs), offsetof(DecodeArgs, num_cus),
       offsetof(DecodeArgs, scale_log2), offsetof(DecodeArgs, index_errors),
       sizeof(MergePartialsArgs), offsetof(MergePartialsArgs, num_rows),
       sizeof(PrefillArgs), offsetof(PrefillArgs, num_blocks), offsetof(PrefillArgs, scale_log2),
