@@ -467,3 +467,35 @@ def test_seq_order_subset_leaves_other_rows_unwritten(G, partition):
     assert np.all(got[unlisted] == 0x1234)
     ref, _ = _oracle_rows(b, listed)
     check_close(to_f64(out)[listed], ref, f"subset G{G} p{partition}")
+
+
+@pytest.mark.parametrize("partition", [0, 256])
+def test_persistent_workgroups_with_skipped_and_empty_items(partition):
+    """Grids large enough for persistent workgroups (eight wavefronts over 4k+-token spans
+    unsplit; two wavefronts over 256-token partitions), where some items are skipped by
+    seq_order and some sequences are empty: every listed row matches the oracle, empty
+    sequences give zero rows, unlisted rows keep their contents."""
+    rng = np.random.default_rng(77 + partition)
+    B = 40 if partition == 0 else 16
+    lens = rng.integers(4096, 5000, size=B)
+    lens[[3, 11]] = 0
+    b = make_batch(B=B, Hq=32, Hkv=8, D=128, BS=16, dtype="bf16", scale=0.088, seed=81 + partition,
+                   lens=lens, NB=None)
+    d = upload(b)
+    pa_reshape_and_cache(d.key_new, d.value_new, d.k_cache, d.v_cache, d.slot_mapping)
+    from paged_kv_cache_324_amd import pa_decode_order
+    order = pa_decode_order(b.context_lens).copy()
+    skipped = order[[1, 6]].copy()
+    order[[1, 6]] = [-1, B + 5]
+    listed = np.setdiff1d(np.arange(B), skipped)
+    log(f"persistent p{partition}: B={B} items={B * 8 * (1 if partition == 0 else -(-int(lens.max()) // partition))}")
+    out = torch.full(tuple(d.q.shape), 0x1234, dtype=torch.int16, device="cuda").view(d.q.dtype)
+    pa_decode(out, d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, b.scale,
+              b.max_context_len, partition, seq_order=torch.from_numpy(order).cuda())
+    torch.cuda.synchronize()
+    got = to_bits(out)
+    assert np.all(got[skipped] == 0x1234)
+    empty = np.intersect1d(listed, np.flatnonzero(b.context_lens == 0))
+    assert len(empty) and np.all(got[empty] == 0)
+    ref, _ = _oracle_rows(b, listed)
+    check_close(to_f64(out)[listed], ref, f"persistent p{partition}")
