@@ -9,9 +9,10 @@
 // instead of fp32 vector ALUs, which keeps GQA-8 decode bound by HBM rather
 // than by VALU issue.
 //
-// One workgroup (NW wavefronts) per (sequence, KV head, context partition).
-// The partition is cut into 32-key steps taken round-robin by the NW
-// wavefronts:
+// One workgroup (NW wavefronts) per (sequence, KV head, context partition),
+// or, for grids larger than the resident workgroups (PERSIST), a resident
+// grid whose workgroups take several such items in turn.  The partition is
+// cut into 32-key steps taken round-robin by the NW wavefronts:
 //   S^T = K Q^T   16x16x32 MFMA, two 16-key groups per step.  A = K rows
 //                 (16 keys x 32 dims).  K and V rows are loaded whole, four
 //                 256-byte rows per load instruction, through buffer
