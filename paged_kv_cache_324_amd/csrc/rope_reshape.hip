@@ -28,9 +28,9 @@ namespace pa {
 
 // One workgroup per U consecutive tokens (blockDim = a token's item count
 // rounded up to whole wavefronts, at most 1024; a token with more items loops).
-// A thread takes the same item of each of the U tokens and issues all their
-// loads (position, slot, the rows, then the table entries) before computing
-// and storing any, so it keeps U rows in flight.
+// A thread takes the same item of each of the U tokens and loads all their
+// positions, slots and rows before computing and storing any, so it keeps U
+// rows in flight; each token's table entries are read as it is rotated.
 template <int DT, int D, int U>
 __global__ __launch_bounds__(1024) void rope_reshape_kernel(RopeReshapeArgs a) {
   constexpr int P = D / 16;          // items per row
