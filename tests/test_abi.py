@@ -104,6 +104,7 @@ def test_partition_hint(lib):
     assert h(128, 8, 2048, 16) == 0            # 1024 pairs: enough workgroups unsplit
     assert h(64, 8, 8192, 32) == 0             # 512 pairs: two per compute unit
     assert h(8, 8, 32768, 256) == 1024         # 64 pairs: 32 partitions of the longest context
+    assert h(8, 8, 4096, 256) == 512           # the 512-token floor (32 partitions would be 128)
     assert h(8, 8, 30000, 16) == 944           # rounded up to a whole block
     assert h(1, 1, 100, 16) == 0               # shorter than the minimum partition
     assert h(4, 8, 0, 16) == 0
